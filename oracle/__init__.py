@@ -1,0 +1,19 @@
+"""Plain CPU oracle of the predictive sparse-KV decode path (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import
+this package; the product path never does.
+"""
+from .dd_oracle import (  # noqa: F401
+    BF16,
+    F32,
+    attend_rows,
+    attention_weights,
+    bookkeeping,
+    default_scale,
+    gather_rows,
+    layer_step,
+    masked_attention,
+    scaled_logits,
+    select_topk,
+    upcast,
+)
