@@ -1,0 +1,251 @@
+"""Benchmark of the predictive sparse-KV decode hot path on one MI355X.
+
+One step = one dd_layer_step over one batch of the Llama-2-7B-shape
+single-layer workload (batch 1, 32 heads x 128, 32768 cached keys, bf16 K/V,
+top-128, current + speculated query): scoring of every key for both queries,
+both top-k selections with the prediction bookkeeping, the prefetch of the
+predicted rows on the side stream, the miss fetch and the sparse attention.
+The prediction is the speculated set of an untimed first step, as in decode.
+
+Inputs are resident before the clock starts: keys in HBM, the full K/V in
+pinned host memory.  The key copy rotates over several identical HBM copies
+so that repeated steps cannot be served from the 256 MB Infinity Cache.
+
+Prints one JSON line (see the fields at the end of main()).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "keys scored/s (% HBM peak) + gather GB/s + layer decode step µs, 7B-shape 32K"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "sparse_kv_retrieval_dual_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def _counter_traffic(kernel_file: str, workload: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(PROFILES, f"{os.path.splitext(kernel_file)[0]}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    if fields.get("source_sha256_16") != _source_hash(kernel_file):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, lay, budget_s: float):
+    """The oracle as it stands, single-threaded, on the same workload; it
+    repeats the whole layer until about budget_s seconds have passed."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    q = lay["q"].cpu().numpy()
+    k16 = lay["k"].cpu().view(__import__("torch").int16).numpy()
+    v16 = lay["v"].cpu().view(__import__("torch").int16).numpy()
+    lens = lay["lens"].cpu().numpy()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.layer_step(q, k16, k16, v16, lens, w.k, w.dtype)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    if limiter is not None:
+        limiter.unregister()
+    keys = int(np.sum(lens)) * w.H * reps
+    return {"value": keys / el, "unit": "keys/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full oracle layer steps of {w.name} (B={w.B} H={w.H} n={w.n_max} "
+                      f"k={w.k}; fp64 scoring, full sort, dense-masked attention) in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_32k_layer")
+    ap.add_argument("--copies", type=int, default=4, help="HBM copies of the keys to rotate over")
+    ap.add_argument("--ring", type=int, default=2)
+    ap.add_argument("--gather-cus", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each GPU would run its own share of requests or heads independently).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gen
+    import sparse_kv_retrieval_dual_amd as dd
+    from sparse_kv_retrieval_dual_amd.hipevents import EventSet
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dd.load()
+    dev = torch.device("cuda:0")
+    w = gen.workload(args.workload)
+    assert w.L == 1, "the timed workload is a single layer step"
+    lay = gen.make_layer(w, 0, dev)
+    lens = lay["lens"]
+    kh = dd.host_empty(lay["k"].shape, lay["k"].dtype)
+    vh = dd.host_empty(lay["v"].shape, lay["v"].dtype)
+    kh.copy_(lay["k"].cpu())
+    vh.copy_(lay["v"].cpu())
+    k_copies = [lay["k"]] + [lay["k"].clone() for _ in range(args.copies - 1)]
+    q = lay["q"]
+    B, H, D, k = w.B, w.H, w.D, w.k
+    n_keys = int(lens.sum().item()) * H
+    eb = w.elem_bytes
+    torch.cuda.synchronize()
+
+    ctx = dd.Context(ring_slots=args.ring, gather_cus=args.gather_cus)
+    cur = [torch.empty(B, H, k, dtype=torch.int32, device=dev)]
+    spec = [torch.empty(B, H, k, dtype=torch.int32, device=dev)]
+    out = [torch.empty(B, H, D, dtype=torch.float32, device=dev)]
+    lse = [torch.empty(B, H, dtype=torch.float32, device=dev)]
+    stats = torch.zeros(1, 3, dtype=torch.int64, device=dev)
+    ring = torch.empty(dd.ring_bytes(args.ring, B, H, D, k, dd.kv_dtype(lay["k"])), dtype=torch.uint8, device=dev)
+    ws = torch.empty(dd.layer_step_workspace_bytes(B, H, D, w.n_max, k), dtype=torch.uint8, device=dev)
+
+    def step(i, pred, timing=None):
+        ctx.layer_step([q], [k_copies[i % len(k_copies)]], [kh], [vh], lens, k, pred=pred,
+                       cur=cur, spec=spec, out=out, lse=lse, stats=stats, ring=ring, ws=ws,
+                       timing=timing)
+
+    # Untimed first step without a prediction; its speculated set predicts the next.
+    step(0, None)
+    pred = [spec[0].clone()]
+    for i in range(args.warmup):
+        step(i, pred)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    stage = EventSet(K * dd.DD_STAGE_EVENTS)
+    bounds = EventSet(2)
+    torch.cuda.synchronize()
+    bounds.record(0)
+    for i in range(K):
+        step(i, pred, timing=stage.handles[i * dd.DD_STAGE_EVENTS:(i + 1) * dd.DD_STAGE_EVENTS])
+    bounds.record(1)
+    torch.cuda.synchronize()
+    total_ms = bounds.elapsed_ms(0, 1)
+    ms_per_step = total_ms / K
+
+    def avg(a, b):
+        return float(np.mean([stage.elapsed_ms(i * 7 + a, i * 7 + b) for i in range(K)]))
+
+    t_score = avg(0, 1)
+    t_topk = avg(1, 2)
+    t_miss = avg(2, 3)
+    t_attn = avg(3, 4)
+    t_prefetch = avg(5, 6)
+    st = stats[0].cpu().tolist()
+    misses, hits, fetched = st
+    valid = int(torch.clamp(lens, max=k).sum().item()) * H
+
+    # Algorithmic bytes of the scorer per launch: every valid key row once
+    # (both queries), plus the two fp32 logits written per key.
+    score_bytes = n_keys * D * eb + n_keys * 2 * 4
+    score_gbps = score_bytes / (t_score * 1e-3) / 1e9
+    prefetch_bytes = valid * 2 * D * eb              # k rows of K and V per (b, h)
+    prefetch_gbps = prefetch_bytes / (t_prefetch * 1e-3) / 1e9
+    miss_bytes = misses * 2 * D * eb
+
+    # Reference rates measured in the same process.
+    big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    big2 = torch.empty_like(big)
+    ev = EventSet(2)
+    dd.stream_copy(big, big2)
+    copies = []
+    for _ in range(5):
+        ev.record(0)
+        dd.stream_copy(big, big2)
+        ev.record(1)
+        torch.cuda.synchronize()
+        copies.append(2 * big.numel() / (ev.elapsed_ms(0, 1) * 1e-3) / 1e9)
+    hbm_copy = float(np.median(copies))
+    hpin = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    h2d = []
+    for _ in range(5):
+        ev.record(0)
+        big.copy_(hpin, non_blocking=True)
+        ev.record(1)
+        torch.cuda.synchronize()
+        h2d.append(big.numel() / (ev.elapsed_ms(0, 1) * 1e-3) / 1e9)
+    h2d_gbps = float(np.median(h2d))
+    del big, big2, hpin
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, lay, args.cpu_seconds)
+
+    traffic = _counter_traffic("score.hip", w.name)
+    result = {
+        "metric": METRIC,
+        "value": n_keys / (ms_per_step * 1e-3),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": D, "context": w.n_max,
+                   "top_k": k, "queries": 2, "kv_dtype": w.dtype, "accumulate": "f32",
+                   "ring_slots": args.ring, "hbm_key_copies": len(k_copies)},
+        "roofline": {"bound": "hbm", "achieved": score_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": score_gbps / HBM_PEAK_GBPS,
+                     "traffic": None if traffic is None else traffic,
+                     "kernel": "score", "algorithmic_bytes": score_bytes,
+                     "avg_launch_us": t_score * 1e3},
+        "cpu_baseline": cpu,
+        "layer_step_us": ms_per_step * 1e3,
+        "stages_us": {"score": t_score * 1e3, "topk_bookkeeping": t_topk * 1e3,
+                      "miss_fetch": t_miss * 1e3, "attention": t_attn * 1e3,
+                      "prefetch_side_stream": t_prefetch * 1e3},
+        "score_keys_per_s": n_keys / (t_score * 1e-3),
+        "score_frac_of_measured_hbm_copy": score_gbps / hbm_copy,
+        "gather_GBps": prefetch_gbps,
+        "gather_frac_of_h2d": prefetch_gbps / h2d_gbps,
+        "h2d_memcpy_GBps": h2d_gbps,
+        "hbm_stream_copy_GBps": hbm_copy,
+        "prediction": {"misses": misses, "hits": hits, "rows_fetched": fetched,
+                       "recall": hits / max(valid, 1), "miss_bytes": miss_bytes},
+    }
+    ctx.close()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

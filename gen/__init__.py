@@ -13,4 +13,6 @@ from .workloads import (  # noqa: F401
     tie_scores,
     random_sorted_indices,
     bf16_bits,
+    random_tensor,
+    random_positions,
 )

@@ -212,3 +212,28 @@ def bf16_bits(t: torch.Tensor) -> torch.Tensor:
     """The raw 16-bit patterns of a bfloat16 tensor, as int16 (a view)."""
     assert t.dtype == torch.bfloat16
     return t.view(torch.int16)
+
+
+def random_tensor(shape, seed: int, dtype=torch.float32, scale: float = 1.0,
+                  device="cpu") -> torch.Tensor:
+    """Seeded N(0, scale^2) tensor, rounded to `dtype` (RNE for bf16)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    t = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    if scale != 1.0:
+        t = t * scale
+    return t.to(dtype)
+
+
+def random_positions(rows: int, k: int, m: int, seed: int, invalid_frac: float = 0.0) -> torch.Tensor:
+    """int32 [rows][k]: distinct row numbers in [0, m) per row, in random order;
+    a fraction of entries is replaced by -1 or by m + something (out of range)."""
+    g = torch.Generator().manual_seed(seed)
+    out = torch.empty(rows, k, dtype=torch.int32)
+    for r in range(rows):
+        out[r] = torch.randperm(m, generator=g)[:k].to(torch.int32)
+    if invalid_frac > 0:
+        bad = torch.rand(rows, k, generator=g) < invalid_frac
+        alt = torch.where(torch.rand(rows, k, generator=g) < 0.5, torch.tensor(-1),
+                          torch.tensor(m) + torch.randint(0, 50, (rows, k), generator=g))
+        out = torch.where(bad, alt.to(torch.int32), out)
+    return out

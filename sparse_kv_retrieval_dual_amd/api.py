@@ -1,0 +1,292 @@
+"""Torch-facing binding of libdd: same operations and names as include/dd.h.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory, streams and the host-side tensors.  Shapes
+and dtypes are checked here so that a mistake raises a Python error before
+anything is enqueued; the library checks its own contract again.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import weakref
+
+import torch
+
+from . import _lib as L
+
+_DTYPE = {torch.float32: L.DD_F32, torch.bfloat16: L.DD_BF16}
+
+
+def _lib():
+    return L.load()
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(t, name):
+    _need(t.is_cuda, f"{name} must be a GPU tensor")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def kv_dtype(t: torch.Tensor) -> int:
+    _need(t.dtype in _DTYPE, f"K/V dtype must be float32 or bfloat16, got {t.dtype}")
+    return _DTYPE[t.dtype]
+
+
+# --------------------------------------------------------------------------- host memory
+def host_empty(shape, dtype: torch.dtype) -> torch.Tensor:
+    """A CPU tensor over pinned, device-mapped memory from dd_host_alloc.
+
+    Its address is also valid in kernels; the memory is freed with
+    dd_host_free once the last tensor viewing it is gone.
+    """
+    shape = tuple(int(s) for s in shape)
+    nbytes = math.prod(shape) * torch.empty((), dtype=dtype).element_size()
+    if nbytes == 0:
+        return torch.empty(shape, dtype=dtype)
+    lib = _lib()
+    ptr = ctypes.c_void_p()
+    L.check(lib.dd_host_alloc(nbytes, ctypes.byref(ptr)))
+    addr = ptr.value
+    buf = (ctypes.c_uint8 * nbytes).from_address(addr)
+    weakref.finalize(buf, lib.dd_host_free, ctypes.c_void_p(addr))
+    return torch.frombuffer(buf, dtype=torch.uint8).view(dtype).reshape(shape)
+
+
+# --------------------------------------------------------------------------- stages
+def score(q, keys, lens, kind: str = "logits", scale: float = 0.0, out=None, stream=None):
+    """dd_score.  q fp32 [B][H][Q][D]; keys [B][H][n_max][D]; lens int32 [B]."""
+    _dev(q, "q"), _dev(keys, "keys"), _dev(lens, "lens")
+    _need(q.dtype == torch.float32 and q.dim() == 4, "q must be fp32 [B][H][Q][D]")
+    B, H, Q, D = q.shape
+    _need(keys.dim() == 4 and keys.shape[0] == B and keys.shape[1] == H and keys.shape[3] == D,
+          "keys must be [B][H][n_max][D]")
+    _need(lens.dtype == torch.int32 and lens.numel() == B, "lens must be int32 [B]")
+    n_max = keys.shape[2]
+    if out is None:
+        out = torch.empty(B, H, Q, n_max, dtype=torch.float32, device=q.device)
+    _dev(out, "out")
+    _need(out.shape == (B, H, Q, n_max) and out.dtype == torch.float32, "out must be fp32 [B][H][Q][n_max]")
+    k_code = {"logits": L.DD_LOGITS, "alpha": L.DD_ALPHA}[kind]
+    L.check(_lib().dd_score(_p(q), _p(keys), _p(lens), B, H, Q, D, n_max, kv_dtype(keys),
+                            float(scale), k_code, _p(out), _stream(stream)))
+    return out
+
+
+def topk(scores, lens, k: int, out=None, stream=None):
+    """dd_topk.  scores fp32 [B][H][Q][n_max] -> int32 [B][H][Q][k], ascending, -1 padded."""
+    _dev(scores, "scores"), _dev(lens, "lens")
+    _need(scores.dtype == torch.float32 and scores.dim() == 4, "scores must be fp32 [B][H][Q][n_max]")
+    B, H, Q, n_max = scores.shape
+    _need(lens.dtype == torch.int32 and lens.numel() == B, "lens must be int32 [B]")
+    if out is None:
+        out = torch.empty(B, H, Q, k, dtype=torch.int32, device=scores.device)
+    _dev(out, "out")
+    _need(out.shape == (B, H, Q, k) and out.dtype == torch.int32, "out must be int32 [B][H][Q][k]")
+    L.check(_lib().dd_topk(_p(scores), _p(lens), B, H, Q, n_max, int(k), _p(out), _stream(stream)))
+    return out
+
+
+def gather(k_host, v_host, idx, cnt=None, k_out=None, v_out=None, stream=None):
+    """dd_gather.  k_host/v_host pinned [B][H][n_max][D] (host_empty); idx int32 [B][H][m]."""
+    ref = k_host if k_host is not None else v_host
+    _need(ref is not None, "need at least one host plane")
+    _dev(idx, "idx")
+    _need(idx.dtype == torch.int32 and idx.dim() == 3, "idx must be int32 [B][H][m]")
+    B, H, m = idx.shape
+    _need(ref.dim() == 4 and ref.shape[0] == B and ref.shape[1] == H, "host planes must be [B][H][n_max][D]")
+    n_max, D = ref.shape[2], ref.shape[3]
+    dt = kv_dtype(ref)
+    for t, name in ((k_host, "k_host"), (v_host, "v_host")):
+        if t is not None:
+            _need(not t.is_cuda and t.is_contiguous() and t.shape == ref.shape and t.dtype == ref.dtype,
+                  f"{name} must be a contiguous host tensor like the other plane")
+    if cnt is not None:
+        _dev(cnt, "cnt")
+        _need(cnt.dtype == torch.int32 and cnt.numel() == B * H, "cnt must be int32 [B][H]")
+    if k_host is not None and k_out is None:
+        k_out = torch.empty(B, H, m, D, dtype=ref.dtype, device=idx.device)
+    if v_host is not None and v_out is None:
+        v_out = torch.empty(B, H, m, D, dtype=ref.dtype, device=idx.device)
+    for t, name in ((k_out, "k_out"), (v_out, "v_out")):
+        if t is not None:
+            _dev(t, name)
+            _need(t.shape == (B, H, m, D) and t.dtype == ref.dtype, f"{name} must be [B][H][m][D]")
+    L.check(_lib().dd_gather(_p(k_host), _p(v_host), _p(idx), _p(cnt), B, H, m, D, n_max, dt,
+                             _p(k_out), _p(v_out), _stream(stream)))
+    return k_out, v_out
+
+
+def attn_workspace_bytes(B: int, H: int, k: int, D: int) -> int:
+    return int(_lib().dd_attn_workspace(B, H, k, D))
+
+
+def sparse_attn(q, k_rows, v_rows, pos=None, cnt=None, k: int | None = None, scale: float = 0.0,
+                out=None, lse=None, with_lse: bool = True, ws=None, stream=None):
+    """dd_sparse_attn.  q fp32 [B][H][D] or [B][H][2][D] (plane 0 attends)."""
+    _dev(q, "q"), _dev(k_rows, "k_rows"), _dev(v_rows, "v_rows")
+    _need(q.dtype == torch.float32, "q must be fp32")
+    B, H, m, D = k_rows.shape
+    _need(v_rows.shape == k_rows.shape and v_rows.dtype == k_rows.dtype, "k_rows/v_rows mismatch")
+    if q.dim() == 3:
+        _need(q.shape == (B, H, D), "q must be [B][H][D]")
+        q_stride = D
+    else:
+        _need(q.dim() == 4 and q.shape[0] == B and q.shape[1] == H and q.shape[3] == D,
+              "q must be [B][H][Q][D]")
+        q_stride = q.shape[2] * D
+    if pos is not None:
+        _dev(pos, "pos")
+        _need(pos.dtype == torch.int32 and pos.dim() == 3 and pos.shape[:2] == (B, H), "pos must be int32 [B][H][k]")
+        kk = pos.shape[2] if k is None else int(k)
+        _need(pos.shape[2] == kk, "pos must have k entries per (b, h)")
+    else:
+        kk = m if k is None else int(k)
+    if cnt is not None:
+        _dev(cnt, "cnt")
+        _need(cnt.dtype == torch.int32 and cnt.numel() == B * H, "cnt must be int32 [B][H]")
+    if out is None:
+        out = torch.empty(B, H, D, dtype=torch.float32, device=q.device)
+    if lse is None and with_lse:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    need = attn_workspace_bytes(B, H, kk, D)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    L.check(_lib().dd_sparse_attn(_p(q), q_stride, _p(k_rows), _p(v_rows), _p(pos), _p(cnt), B, H,
+                                  kk, m, D, kv_dtype(k_rows), float(scale), _p(out), _p(lse),
+                                  _p(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                  _stream(stream)))
+    return out, lse
+
+
+def stream_copy(src, dst, stream=None):
+    """dd_stream_copy: device-to-device streaming copy of src's bytes into dst."""
+    _dev(src, "src"), _dev(dst, "dst")
+    n = src.numel() * src.element_size()
+    _need(dst.numel() * dst.element_size() >= n, "dst too small")
+    L.check(_lib().dd_stream_copy(_p(src), _p(dst), n, _stream(stream)))
+    return dst
+
+
+# --------------------------------------------------------------------------- layer step
+def ring_bytes(ring_slots: int, B: int, H: int, D: int, k: int, dtype: int) -> int:
+    return int(_lib().dd_ring_bytes(ring_slots, B, H, D, k, dtype))
+
+
+def layer_step_workspace_bytes(B: int, H: int, D: int, n_max: int, k: int) -> int:
+    return int(_lib().dd_layer_step_workspace(B, H, D, n_max, k))
+
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = None if t is None else t.data_ptr()
+    return arr
+
+
+class Context:
+    """dd_ctx: the side stream, events and ring configuration of the layer step."""
+
+    def __init__(self, ring_slots: int = 2, gather_cus: int = 0):
+        lib = _lib()
+        cfg = L.CtxConfig(ring_slots=int(ring_slots), gather_cus=int(gather_cus), reserved=0)
+        h = ctypes.c_void_p()
+        L.check(lib.dd_ctx_create(ctypes.byref(cfg), ctypes.byref(h)))
+        self._h = h
+        self.ring_slots = int(ring_slots)
+        self._ring = None
+        self._ws = None
+        self._fin = weakref.finalize(self, lib.dd_ctx_destroy, h)
+
+    def close(self):
+        self._fin()
+
+    def _buffer(self, attr, nbytes, device):
+        buf = getattr(self, attr)
+        if buf is None or buf.numel() < nbytes or buf.device != device:
+            buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+            setattr(self, attr, buf)
+        return buf
+
+    def layer_step(self, q, k_dev, k_host, v_host, lens, k: int, pred=None, scale: float = 0.0,
+                   cur=None, spec=None, out=None, lse=None, stats=None, ring=None, ws=None,
+                   timing=None, stream=None):
+        """dd_layer_step over the layers given as lists (one tensor per layer).
+
+        q[l] fp32 [B][H][2][D]; k_dev[l] device [B][H][n_max][D]; k_host[l], v_host[l]
+        pinned host tensors of the same shape; pred: None or a list whose entries are
+        None or int32 [B][H][k].  Returns dict(cur, spec, out, lse, stats).
+        `timing` is None or a sequence of L * DD_STAGE_EVENTS raw hipEvent_t handles.
+        """
+        Lyr = len(q)
+        _need(Lyr == len(k_dev) == len(k_host) == len(v_host), "per-layer lists differ in length")
+        B, H, two, D = q[0].shape
+        _need(two == 2, "q must hold two query planes")
+        n_max = k_dev[0].shape[2]
+        dt = kv_dtype(k_dev[0])
+        dev = q[0].device
+        for l in range(Lyr):
+            _dev(q[l], "q"), _dev(k_dev[l], "k_dev")
+            _need(q[l].shape == (B, H, 2, D) and q[l].dtype == torch.float32, "q shape")
+            _need(k_dev[l].shape == (B, H, n_max, D) and kv_dtype(k_dev[l]) == dt, "k_dev shape")
+            for t in (k_host[l], v_host[l]):
+                _need(not t.is_cuda and t.is_contiguous() and t.shape == (B, H, n_max, D)
+                      and t.dtype == k_dev[l].dtype, "host K/V must be contiguous [B][H][n_max][D]")
+            if pred is not None and pred[l] is not None:
+                _dev(pred[l], "pred")
+                _need(pred[l].shape == (B, H, k) and pred[l].dtype == torch.int32, "pred must be int32 [B][H][k]")
+        _dev(lens, "lens")
+        _need(lens.dtype == torch.int32 and lens.numel() == B, "lens must be int32 [B]")
+        if cur is None:
+            cur = [torch.empty(B, H, k, dtype=torch.int32, device=dev) for _ in range(Lyr)]
+        if spec is None:
+            spec = [torch.empty(B, H, k, dtype=torch.int32, device=dev) for _ in range(Lyr)]
+        if out is None:
+            out = [torch.empty(B, H, D, dtype=torch.float32, device=dev) for _ in range(Lyr)]
+        if lse is None:
+            lse = [torch.empty(B, H, dtype=torch.float32, device=dev) for _ in range(Lyr)]
+        if stats is None:
+            stats = torch.zeros(Lyr, 3, dtype=torch.int64, device=dev)
+        rb = ring_bytes(self.ring_slots, B, H, D, k, dt)
+        wb = layer_step_workspace_bytes(B, H, D, n_max, k)
+        if ring is None:
+            ring = self._buffer("_ring", rb, dev)
+        if ws is None:
+            ws = self._buffer("_ws", wb, dev)
+        keep = [_ptr_array(q), _ptr_array(k_dev), _ptr_array(k_host), _ptr_array(v_host),
+                _ptr_array(pred) if pred is not None else None,
+                _ptr_array(cur), _ptr_array(spec), _ptr_array(out),
+                _ptr_array(lse) if lse is not None else None]
+        tarr = None
+        if timing is not None:
+            tarr = (ctypes.c_void_p * len(timing))(*timing)
+        a = L.LayerStepArgs(
+            L=Lyr, B=B, H=H, D=D, k=int(k), dtype=dt, n_max=n_max, scale=float(scale),
+            lens=lens.data_ptr(),
+            q=ctypes.cast(keep[0], ctypes.c_void_p), k_dev=ctypes.cast(keep[1], ctypes.c_void_p),
+            k_host=ctypes.cast(keep[2], ctypes.c_void_p), v_host=ctypes.cast(keep[3], ctypes.c_void_p),
+            pred=None if keep[4] is None else ctypes.cast(keep[4], ctypes.c_void_p),
+            cur_idx=ctypes.cast(keep[5], ctypes.c_void_p), spec_idx=ctypes.cast(keep[6], ctypes.c_void_p),
+            out=ctypes.cast(keep[7], ctypes.c_void_p),
+            lse=None if keep[8] is None else ctypes.cast(keep[8], ctypes.c_void_p),
+            stats=stats.data_ptr(),
+            ring=ring.data_ptr(), ring_bytes=ring.numel() * ring.element_size(),
+            ws=ws.data_ptr(), ws_bytes=ws.numel() * ws.element_size(),
+            stream=_stream(stream).value,
+            timing=None if tarr is None else ctypes.cast(tarr, ctypes.c_void_p),
+        )
+        L.check(_lib().dd_layer_step(self._h, ctypes.byref(a)))
+        return {"cur": cur, "spec": spec, "out": out, "lse": lse, "stats": stats}

@@ -1,0 +1,397 @@
+// The C ABI: argument validation, error reporting, pinned host memory, the
+// per-stage entry points and the layer step (the layer-aware transfer
+// schedule over a ring of layer-scoped slots, arXiv page of DualDecoder,
+// section 1; paper-daily summary, technical-method section).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+#include <vector>
+
+#include "dd.h"
+#include "dd_internal.h"
+
+struct dd_ctx {
+  int device = -1;
+  int ring_slots = 1;
+  int gather_cus = 0;
+  hipStream_t side = nullptr;       // prefetch gathers
+  hipStream_t main_own = nullptr;   // CU-masked main stream (gather_cus > 0 only)
+  hipEvent_t ev_start = nullptr;    // caller stream at entry
+  hipEvent_t ev_end = nullptr;      // own main stream at exit
+  std::vector<hipEvent_t> ev_gathered;  // per slot: prefetch finished
+  std::vector<hipEvent_t> ev_free;      // per slot: attention finished
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DD_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+#define DD_CHECK_HIP(expr, what)              \
+  do {                                        \
+    hipError_t e_ = (expr);                   \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+int check_shape(int B, int H, int D, int64_t n_max, int dtype) {
+  if (B < 0 || H < 0) return fail(DD_ERR_INVALID_ARG, "B and H must be >= 0 (B=%d H=%d)", B, H);
+  if ((int64_t)B * H > (int64_t)1 << 24) return fail(DD_ERR_UNSUPPORTED, "B*H too large");
+  if (D != 64 && D != 128) return fail(DD_ERR_UNSUPPORTED, "D must be 64 or 128 (got %d)", D);
+  if (dtype != DD_F32 && dtype != DD_BF16)
+    return fail(DD_ERR_UNSUPPORTED, "dtype must be DD_F32 or DD_BF16 (got %d)", dtype);
+  if (n_max < 0 || n_max >= ((int64_t)1 << 31))
+    return fail(DD_ERR_UNSUPPORTED, "n_max must be in [0, 2^31) (got %lld)", (long long)n_max);
+  return DD_OK;
+}
+
+int check_k(int k) {
+  if (k < 1 || k > DD_MAX_K) return fail(DD_ERR_UNSUPPORTED, "k must be in [1, %d] (got %d)", DD_MAX_K, k);
+  return DD_OK;
+}
+
+// Workspace of the layer step, carved in this order.
+struct StepLayout {
+  size_t scores, pos, miss, counts, attn, total;
+};
+
+StepLayout step_layout(int B, int H, int D, int64_t n_max, int k) {
+  const size_t BH = (size_t)B * H;
+  StepLayout l{};
+  size_t off = 0;
+  l.scores = off;
+  off += align_up(BH * 2 * (size_t)n_max * sizeof(float));
+  l.pos = off;
+  off += align_up(BH * k * sizeof(int32_t));
+  l.miss = off;
+  off += align_up(BH * k * sizeof(int32_t));
+  l.counts = off;
+  off += align_up(3 * BH * sizeof(int32_t));
+  l.attn = off;
+  off += align_up(dd::attn_workspace(B, H, k, D));
+  l.total = off;
+  return l;
+}
+
+size_t slot_bytes(int B, int H, int D, int k, int dtype) {
+  return 2 * (size_t)B * H * 2 * k * D * dd::elem_bytes(dtype);
+}
+
+}  // namespace
+
+extern "C" {
+
+DD_API const char* dd_last_error(void) { return g_err.c_str(); }
+
+DD_API int dd_version(void) { return 100; }
+
+DD_API int dd_host_alloc(size_t bytes, void** host_ptr) {
+  if (host_ptr == nullptr) return fail(DD_ERR_INVALID_ARG, "host_ptr is NULL");
+  *host_ptr = nullptr;
+  if (bytes == 0) return DD_OK;
+  void* p = nullptr;
+  hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocMapped | hipHostMallocPortable);
+  if (e != hipSuccess || p == nullptr)
+    return fail(DD_ERR_ALLOC, "hipHostMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+  void* dp = nullptr;
+  e = hipHostGetDevicePointer(&dp, p, 0);
+  if (e != hipSuccess || dp != p) {
+    (void)hipHostFree(p);
+    return fail(DD_ERR_ALLOC, "pinned memory is not mapped at the same address on the device");
+  }
+  *host_ptr = p;
+  return DD_OK;
+}
+
+DD_API int dd_host_free(void* host_ptr) {
+  if (host_ptr == nullptr) return DD_OK;
+  DD_CHECK_HIP(hipHostFree(host_ptr), "hipHostFree");
+  return DD_OK;
+}
+
+DD_API int dd_score(const float* q, const void* keys, const int32_t* lens, int B, int H, int Q,
+                    int D, int64_t n_max, int kv_dtype, float scale, int kind, float* scores,
+                    hipStream_t stream) {
+  int rc = check_shape(B, H, D, n_max, kv_dtype);
+  if (rc) return rc;
+  if (Q != 1 && Q != 2) return fail(DD_ERR_UNSUPPORTED, "Q must be 1 or 2 (got %d)", Q);
+  if (kind != DD_LOGITS && kind != DD_ALPHA) return fail(DD_ERR_UNSUPPORTED, "unknown kind %d", kind);
+  if ((int64_t)B * H == 0 || n_max == 0) return DD_OK;
+  if (!q || !keys || !lens || !scores) return fail(DD_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(keys)) return fail(DD_ERR_INVALID_ARG, "keys must be 16-byte aligned");
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
+  hipError_t e = dd::launch_score(q, keys, lens, B, H, Q, D, n_max, kv_dtype, sc, true, scores, stream);
+  if (e != hipSuccess) return hip_fail(e, "score kernel launch");
+  if (kind == DD_ALPHA) {
+    e = dd::launch_softmax_rows(scores, lens, B, H, Q, n_max, stream);
+    if (e != hipSuccess) return hip_fail(e, "softmax kernel launch");
+  }
+  return DD_OK;
+}
+
+DD_API int dd_topk(const float* scores, const int32_t* lens, int B, int H, int Q, int64_t n_max,
+                   int k, int32_t* idx, hipStream_t stream) {
+  int rc = check_shape(B, H, 64, n_max, DD_F32);
+  if (rc) return rc;
+  rc = check_k(k);
+  if (rc) return rc;
+  if (Q != 1 && Q != 2) return fail(DD_ERR_UNSUPPORTED, "Q must be 1 or 2 (got %d)", Q);
+  if ((int64_t)B * H == 0) return DD_OK;
+  if (!lens || !idx || (!scores && n_max > 0)) return fail(DD_ERR_INVALID_ARG, "null pointer argument");
+  hipError_t e = dd::launch_topk(scores, lens, B, H, Q, n_max, k, idx, idx + k, (int64_t)Q * k,
+                                 nullptr, stream);
+  if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
+  return DD_OK;
+}
+
+DD_API int dd_gather(const void* k_host, const void* v_host, const int32_t* idx,
+                     const int32_t* cnt, int B, int H, int m, int D, int64_t n_max, int dtype,
+                     void* k_rows, void* v_rows, hipStream_t stream) {
+  int rc = check_shape(B, H, D, n_max, dtype);
+  if (rc) return rc;
+  if (m < 0) return fail(DD_ERR_INVALID_ARG, "m must be >= 0 (got %d)", m);
+  if ((int64_t)B * H * m == 0) return DD_OK;
+  if (!idx) return fail(DD_ERR_INVALID_ARG, "idx is NULL");
+  if (!k_host && !v_host) return fail(DD_ERR_INVALID_ARG, "both host planes are NULL");
+  if ((k_host && !k_rows) || (v_host && !v_rows))
+    return fail(DD_ERR_INVALID_ARG, "destination missing for a host plane");
+  if ((k_host && (!aligned16(k_host) || !aligned16(k_rows))) ||
+      (v_host && (!aligned16(v_host) || !aligned16(v_rows))))
+    return fail(DD_ERR_INVALID_ARG, "host and row buffers must be 16-byte aligned");
+  const int rowb = D * dd::elem_bytes(dtype);
+  hipError_t e = dd::launch_gather(k_host, v_host, n_max, rowb, idx, m, cnt, B * H,
+                                   k_host ? k_rows : nullptr, v_host ? v_rows : nullptr, m, 0,
+                                   nullptr, nullptr, stream);
+  if (e != hipSuccess) return hip_fail(e, "gather kernel launch");
+  return DD_OK;
+}
+
+DD_API size_t dd_attn_workspace(int B, int H, int k, int D) {
+  if (B <= 0 || H <= 0 || k <= 0) return 0;
+  return dd::attn_workspace(B, H, k, D);
+}
+
+DD_API int dd_sparse_attn(const float* q, int64_t q_stride_bh, const void* k_rows,
+                          const void* v_rows, const int32_t* pos, const int32_t* cnt, int B,
+                          int H, int k, int m, int D, int dtype, float scale, float* out,
+                          float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(B, H, D, 0, dtype);
+  if (rc) return rc;
+  rc = check_k(k);
+  if (rc) return rc;
+  if (m < 0) return fail(DD_ERR_INVALID_ARG, "m must be >= 0 (got %d)", m);
+  if ((int64_t)B * H == 0) return DD_OK;
+  if (!q || !out || (m > 0 && (!k_rows || !v_rows)))
+    return fail(DD_ERR_INVALID_ARG, "null pointer argument");
+  if (q_stride_bh < D) return fail(DD_ERR_INVALID_ARG, "q_stride_bh must be >= D");
+  if (m > 0 && (!aligned16(k_rows) || !aligned16(v_rows)))
+    return fail(DD_ERR_INVALID_ARG, "row buffers must be 16-byte aligned");
+  const size_t need = dd::attn_workspace(B, H, k, D);
+  if (ws_bytes < need || (need > 0 && ws == nullptr))
+    return fail(DD_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
+  hipError_t e = dd::launch_attn(q, q_stride_bh, k_rows, v_rows, pos, cnt, B, H, k, m, D, dtype,
+                                 sc, out, lse, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return DD_OK;
+}
+
+DD_API size_t dd_ring_bytes(int ring_slots, int B, int H, int D, int k, int dtype) {
+  if (ring_slots <= 0 || B <= 0 || H <= 0 || k <= 0) return 0;
+  return (size_t)ring_slots * slot_bytes(B, H, D, k, dtype);
+}
+
+DD_API size_t dd_layer_step_workspace(int B, int H, int D, int64_t n_max, int k) {
+  if (B <= 0 || H <= 0 || k <= 0 || n_max < 0) return 0;
+  return step_layout(B, H, D, n_max, k).total;
+}
+
+DD_API int dd_ctx_create(const dd_ctx_config* cfg, dd_ctx** ctx) {
+  if (!cfg || !ctx) return fail(DD_ERR_INVALID_ARG, "null pointer argument");
+  *ctx = nullptr;
+  if (cfg->ring_slots < 1 || cfg->ring_slots > 64)
+    return fail(DD_ERR_INVALID_ARG, "ring_slots must be in [1, 64] (got %d)", cfg->ring_slots);
+  if (cfg->gather_cus < 0 || cfg->reserved != 0)
+    return fail(DD_ERR_INVALID_ARG, "gather_cus must be >= 0 and reserved 0");
+  dd_ctx* c = new dd_ctx();
+  c->ring_slots = cfg->ring_slots;
+  c->gather_cus = cfg->gather_cus;
+  hipError_t e = hipGetDevice(&c->device);
+  const int cus = dd::device_info().cus;
+  if (e == hipSuccess && c->gather_cus > 0) {
+    if (c->gather_cus >= cus) {
+      delete c;
+      return fail(DD_ERR_INVALID_ARG, "gather_cus must be below the CU count (%d)", cus);
+    }
+    // Side stream on the last gather_cus CUs, own main stream on the rest.
+    std::vector<uint32_t> side_mask((cus + 31) / 32, 0u), main_mask((cus + 31) / 32, 0u);
+    for (int i = 0; i < cus; ++i) {
+      if (i >= cus - c->gather_cus) side_mask[i / 32] |= 1u << (i % 32);
+      else main_mask[i / 32] |= 1u << (i % 32);
+    }
+    e = hipExtStreamCreateWithCUMask(&c->side, (uint32_t)side_mask.size(), side_mask.data());
+    if (e == hipSuccess)
+      e = hipExtStreamCreateWithCUMask(&c->main_own, (uint32_t)main_mask.size(), main_mask.data());
+  } else if (e == hipSuccess) {
+    e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
+  }
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_start, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_end, hipEventDisableTiming);
+  for (int i = 0; e == hipSuccess && i < c->ring_slots; ++i) {
+    hipEvent_t a = nullptr, b = nullptr;
+    e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&b, hipEventDisableTiming);
+    if (a) c->ev_gathered.push_back(a);
+    if (b) c->ev_free.push_back(b);
+  }
+  if (e != hipSuccess) {
+    dd_ctx_destroy(c);
+    return hip_fail(e, "context creation");
+  }
+  *ctx = c;
+  return DD_OK;
+}
+
+DD_API int dd_ctx_destroy(dd_ctx* c) {
+  if (c == nullptr) return DD_OK;
+  if (c->side) (void)hipStreamSynchronize(c->side);
+  if (c->main_own) (void)hipStreamSynchronize(c->main_own);
+  for (hipEvent_t e : c->ev_gathered) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
+  if (c->ev_start) (void)hipEventDestroy(c->ev_start);
+  if (c->ev_end) (void)hipEventDestroy(c->ev_end);
+  if (c->side) (void)hipStreamDestroy(c->side);
+  if (c->main_own) (void)hipStreamDestroy(c->main_own);
+  delete c;
+  return DD_OK;
+}
+
+DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
+  if (!c || !a) return fail(DD_ERR_INVALID_ARG, "null pointer argument");
+  int dev = -1;
+  DD_CHECK_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev != c->device) return fail(DD_ERR_INVALID_ARG, "context belongs to device %d, current is %d", c->device, dev);
+  int rc = check_shape(a->B, a->H, a->D, a->n_max, a->dtype);
+  if (rc) return rc;
+  rc = check_k(a->k);
+  if (rc) return rc;
+  if (a->L < 0) return fail(DD_ERR_INVALID_ARG, "L must be >= 0");
+  if (a->L == 0 || (int64_t)a->B * a->H == 0) return DD_OK;
+  if (!a->lens || !a->q || !a->k_dev || !a->k_host || !a->v_host || !a->cur_idx ||
+      !a->spec_idx || !a->out)
+    return fail(DD_ERR_INVALID_ARG, "null pointer argument");
+  for (int l = 0; l < a->L; ++l) {
+    if (!a->q[l] || !a->k_dev[l] || !a->k_host[l] || !a->v_host[l] || !a->cur_idx[l] ||
+        !a->spec_idx[l] || !a->out[l])
+      return fail(DD_ERR_INVALID_ARG, "null pointer for layer %d", l);
+    if (!aligned16(a->k_dev[l]) || !aligned16(a->k_host[l]) || !aligned16(a->v_host[l]))
+      return fail(DD_ERR_INVALID_ARG, "K/V buffers of layer %d must be 16-byte aligned", l);
+  }
+  const int B = a->B, H = a->H, D = a->D, k = a->k, BH = B * H;
+  const size_t sbytes = slot_bytes(B, H, D, k, a->dtype);
+  const size_t ring_need = (size_t)c->ring_slots * sbytes;
+  if (!a->ring || a->ring_bytes < ring_need || !aligned16(a->ring))
+    return fail(DD_ERR_WORKSPACE, "ring too small: need %zu bytes, got %zu", ring_need, a->ring_bytes);
+  const StepLayout lay = step_layout(B, H, D, a->n_max, k);
+  if (!a->ws || a->ws_bytes < lay.total)
+    return fail(DD_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", lay.total, a->ws_bytes);
+
+  const float sc = a->scale > 0.f ? a->scale : 1.0f / sqrtf((float)D);
+  const int rowb = D * dd::elem_bytes(a->dtype);
+  char* ws = static_cast<char*>(a->ws);
+  float* scores = reinterpret_cast<float*>(ws + lay.scores);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + lay.pos);
+  int32_t* miss = reinterpret_cast<int32_t*>(ws + lay.miss);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + lay.counts);
+  void* attn_ws = ws + lay.attn;
+  const int R = c->ring_slots;
+  hipStream_t caller = a->stream;
+  hipStream_t ms = c->main_own ? c->main_own : caller;
+  hipStream_t side = c->side;
+
+  bool any_pred = false;
+  if (a->pred)
+    for (int l = 0; l < a->L; ++l) any_pred = any_pred || (a->pred[l] != nullptr);
+
+  DD_CHECK_HIP(hipEventRecord(c->ev_start, caller), "record start");
+  if (ms != caller) DD_CHECK_HIP(hipStreamWaitEvent(ms, c->ev_start, 0), "main waits start");
+  if (any_pred) DD_CHECK_HIP(hipStreamWaitEvent(side, c->ev_start, 0), "side waits start");
+
+  auto tev = [&](int l, int i) -> hipEvent_t {
+    return a->timing ? a->timing[(size_t)l * DD_STAGE_EVENTS + i] : nullptr;
+  };
+
+  for (int l = 0; l < a->L; ++l) {
+    const int slot = l % R;
+    char* kslot = static_cast<char*>(a->ring) + (size_t)slot * sbytes;
+    char* vslot = kslot + sbytes / 2;
+    const int32_t* P = a->pred ? a->pred[l] : nullptr;
+
+    if (P) {
+      if (l >= R) DD_CHECK_HIP(hipStreamWaitEvent(side, c->ev_free[slot], 0), "side waits slot");
+      if (tev(l, 5)) DD_CHECK_HIP(hipEventRecord(tev(l, 5), side), "timing");
+      hipError_t e = dd::launch_gather(a->k_host[l], a->v_host[l], a->n_max, rowb, P, k, nullptr,
+                                       BH, kslot, vslot, 2 * (int64_t)k, 0, nullptr, nullptr, side);
+      if (e != hipSuccess) return hip_fail(e, "prefetch gather launch");
+      if (tev(l, 6)) DD_CHECK_HIP(hipEventRecord(tev(l, 6), side), "timing");
+      DD_CHECK_HIP(hipEventRecord(c->ev_gathered[slot], side), "record gathered");
+    }
+
+    if (tev(l, 0)) DD_CHECK_HIP(hipEventRecord(tev(l, 0), ms), "timing");
+    hipError_t e = dd::launch_score(a->q[l], a->k_dev[l], a->lens, B, H, 2, D, a->n_max, a->dtype,
+                                    sc, false, scores, ms);
+    if (e != hipSuccess) return hip_fail(e, "score kernel launch");
+    if (tev(l, 1)) DD_CHECK_HIP(hipEventRecord(tev(l, 1), ms), "timing");
+    const dd::TopkBook book{P, pos, miss, counts};
+    e = dd::launch_topk(scores, a->lens, B, H, 2, a->n_max, k, a->cur_idx[l], a->spec_idx[l], k,
+                        &book, ms);
+    if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
+    if (tev(l, 2)) DD_CHECK_HIP(hipEventRecord(tev(l, 2), ms), "timing");
+    if (P) DD_CHECK_HIP(hipStreamWaitEvent(ms, c->ev_gathered[slot], 0), "main waits prefetch");
+    e = dd::launch_gather(a->k_host[l], a->v_host[l], a->n_max, rowb, miss, k, counts, BH, kslot,
+                          vslot, 2 * (int64_t)k, k, counts, a->stats ? a->stats + 3 * (size_t)l : nullptr, ms);
+    if (e != hipSuccess) return hip_fail(e, "miss gather launch");
+    if (tev(l, 3)) DD_CHECK_HIP(hipEventRecord(tev(l, 3), ms), "timing");
+    e = dd::launch_attn(a->q[l], 2 * (int64_t)D, kslot, vslot, pos, nullptr, B, H, k, 2 * k, D,
+                        a->dtype, sc, a->out[l], a->lse ? a->lse[l] : nullptr, attn_ws, ms);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    if (tev(l, 4)) DD_CHECK_HIP(hipEventRecord(tev(l, 4), ms), "timing");
+    DD_CHECK_HIP(hipEventRecord(c->ev_free[slot], ms), "record slot free");
+  }
+  if (ms != caller) {
+    DD_CHECK_HIP(hipEventRecord(c->ev_end, ms), "record end");
+    DD_CHECK_HIP(hipStreamWaitEvent(caller, c->ev_end, 0), "caller waits end");
+  }
+  return DD_OK;
+}
+
+DD_API int dd_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return DD_OK;
+  if (!src || !dst) return fail(DD_ERR_INVALID_ARG, "null pointer argument");
+  if ((bytes & 15) != 0 || !aligned16(src) || !aligned16(dst))
+    return fail(DD_ERR_INVALID_ARG, "bytes and pointers must be multiples of 16");
+  hipError_t e = dd::launch_stream_copy(src, dst, bytes, stream);
+  if (e != hipSuccess) return hip_fail(e, "copy kernel launch");
+  return DD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Internal launchers behind the C ABI.  Arguments are validated by the
+// callers in abi.cpp; these functions only compute launch shapes and
+// enqueue kernels on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dd {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+struct DeviceInfo {
+  int device = -1;
+  int cus = 0;
+  int lds_per_block = 65536;  // usable dynamic LDS bytes for one workgroup
+};
+
+// Properties of the current device (queried once per device).
+const DeviceInfo& device_info();
+
+inline int elem_bytes(int dtype) { return dtype == kF32 ? 4 : 2; }
+
+// Scaled logits of Q queries against every key; rows past lens[b] become
+// -inf when fill_pad is set and are left untouched otherwise.
+hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, int B, int H,
+                        int Q, int D, int64_t n_max, int dtype, float scale, bool fill_pad,
+                        float* scores, hipStream_t s);
+
+// In-place softmax of each score row over its valid keys; 0 past lens[b].
+hipError_t launch_softmax_rows(float* scores, const int32_t* lens, int B, int H, int Q,
+                               int64_t n_max, hipStream_t s);
+
+// Prediction bookkeeping fused into the top-k of query plane 0.
+struct TopkBook {
+  const int32_t* pred;  // [BH][k] or nullptr (no prediction)
+  int32_t* pos;         // [BH][k] slot row of each selected entry
+  int32_t* miss;        // [BH][k] missed entries, ascending, -1 padded
+  int32_t* counts;      // [3][BH]: misses, hits, fetchable prediction entries
+};
+
+// Top-k of each score row.  Plane j of slab bh is written at
+// (j == 0 ? out0 : out1) + bh * out_stride_bh.
+hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, int Q,
+                       int64_t n_max, int k, int32_t* out0, int32_t* out1,
+                       int64_t out_stride_bh, const TopkBook* book, hipStream_t s);
+
+// Row gather from pinned host memory.  Entry j < cnt[bh] (m if cnt is null)
+// of slab bh copies host row idx[bh*m + j] (zero row if out of range) to
+// destination row bh*dst_rows_per_bh + dst_row0 + j.  When stats is set,
+// workgroup 0 also writes stats[0..2] = sums over slabs of counts planes
+// (misses, hits, fetchable prediction entries + misses).
+hipError_t launch_gather(const void* k_host, const void* v_host, int64_t n_max, int row_bytes,
+                         const int32_t* idx, int m, const int32_t* cnt, int BH, void* k_dst,
+                         void* v_dst, int64_t dst_rows_per_bh, int dst_row0,
+                         const int32_t* counts, int64_t* stats, hipStream_t s);
+
+size_t attn_workspace(int B, int H, int k, int D);
+
+hipError_t launch_attn(const float* q, int64_t q_stride_bh, const void* k_rows,
+                       const void* v_rows, const int32_t* pos, const int32_t* cnt, int B, int H,
+                       int k, int m, int D, int dtype, float scale, float* out, float* lse,
+                       void* ws, hipStream_t s);
+
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+}  // namespace dd

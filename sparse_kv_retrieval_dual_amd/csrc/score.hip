@@ -1,0 +1,180 @@
+// Dual-query scoring: s = scale * q . K for the current and the speculated
+// query against every cached key (paper-daily summary of DualDecoder,
+// core-formulas section; its worked example scores the whole key matrix).
+//
+// HBM-bound: each key row (D elements, 256 B for bf16 D=128) is streamed
+// once and serves both queries; 2 flop/B is far below the VALU ridge, so the
+// contraction stays on the VALU (MFMA would idle 15/16 of its tile on a
+// 2-column operand).  A row is read by LPR lanes, 16 B each, so one wave
+// load instruction covers 64*16 contiguous bytes.  Each lane keeps U = LPR/Q
+// rows in flight and the Q*U partial dot products are folded across the LPR
+// lanes with a transposing butterfly that leaves exactly one finished score
+// per lane.
+#include "dd_device.h"
+#include "dd_internal.h"
+
+namespace dd {
+
+namespace {
+
+constexpr int kScoreWaves = 4;
+constexpr int kScoreIters = 4;
+
+template <typename T, int D, int Q>
+struct ScoreShape {
+  static constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane per load
+  static constexpr int LPR = D / EPL;              // lanes per key row
+  static constexpr int RPI = 64 / LPR;             // rows per wave load instruction
+  static constexpr int U = LPR / Q;                // loads per lane per iteration
+  static constexpr int KPI = U * RPI;              // keys per wave iteration (= 64 / Q)
+  static constexpr int TILE = kScoreWaves * kScoreIters * KPI;
+  static_assert(U >= 1 && U * Q == LPR, "shape");
+};
+
+template <typename T, int D, int Q>
+__global__ __launch_bounds__(kScoreWaves * 64) void k_score(
+    const float* __restrict__ q, const T* __restrict__ keys, const int32_t* __restrict__ lens,
+    int BH, int H, int64_t n_max, int tiles, float scale, float* __restrict__ scores,
+    int fill_pad) {
+  using S = ScoreShape<T, D, Q>;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int bh, tile;
+  xcd_tile_map(blockIdx.x, tiles, BH, bh, tile);
+  const int64_t n = clamp_len(lens[bh / H], n_max);
+  const int64_t tile0 = (int64_t)tile * S::TILE;
+  if (tile0 >= n && !fill_pad) return;
+
+  const int col = lane % S::LPR;
+  const int rsub = lane / S::LPR;
+  float qr[Q][S::EPL];
+#pragma unroll
+  for (int j = 0; j < Q; ++j)
+#pragma unroll
+    for (int e = 0; e < S::EPL; ++e) qr[j][e] = q[((int64_t)bh * Q + j) * D + col * S::EPL + e];
+
+  const T* kb = keys + (int64_t)bh * n_max * D + col * S::EPL;
+  float* sb = scores + (int64_t)bh * Q * n_max;
+  // The score this lane finishes: value index v = lane % LPR = u * Q + j.
+  const int vj = col % Q;
+  const int vu = col / Q;
+
+  for (int it = 0; it < kScoreIters; ++it) {
+    const int64_t key0 = tile0 + ((int64_t)it * kScoreWaves + wave) * S::KPI;
+    if (key0 >= n_max) break;
+    const int64_t my_row = key0 + vu * S::RPI + rsub;
+    if (key0 >= n) {
+      if (fill_pad && my_row < n_max) sb[vj * n_max + my_row] = -INFINITY;
+      continue;
+    }
+    // Rows past n load row n-1 instead (n >= 1 here): the loads stay
+    // unconditional so all U of them are in flight together, and the
+    // butterfly never mixes rows, so those lanes' scores are simply not stored.
+    u32x4 raw[S::U];
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      const int64_t row = key0 + u * S::RPI + rsub;
+      const int64_t rr = row < n ? row : n - 1;
+      raw[u] = *reinterpret_cast<const u32x4*>(kb + rr * D);
+    }
+    float acc[S::U * Q];
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      float f[S::EPL];
+      Unpack<T>::run(raw[u], f);
+#pragma unroll
+      for (int j = 0; j < Q; ++j) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < S::EPL; ++e) a = fmaf(f[e], qr[j][e], a);
+        acc[u * Q + j] = a;
+      }
+    }
+    Butterfly<S::LPR, S::U * Q>::run(acc, lane);
+    if (my_row < n) {
+      sb[vj * n_max + my_row] = acc[0] * scale;
+    } else if (fill_pad && my_row < n_max) {
+      sb[vj * n_max + my_row] = -INFINITY;
+    }
+  }
+}
+
+// One workgroup per score row: max, sum of exp, normalise (0 past len).
+__global__ __launch_bounds__(1024) void k_softmax_rows(float* __restrict__ scores,
+                                                       const int32_t* __restrict__ lens, int H,
+                                                       int Q, int64_t n_max) {
+  __shared__ float s_red[16];
+  const int row = blockIdx.x;
+  const int b = (row / Q) / H;
+  const int64_t n = clamp_len(lens[b], n_max);
+  float* s = scores + (int64_t)row * n_max;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+
+  float m = -INFINITY;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) m = fmaxf(m, s[i]);
+  m = wave_max(m);
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  m = -INFINITY;
+  for (int w = 0; w < nw; ++w) m = fmaxf(m, s_red[w]);
+  __syncthreads();
+
+  float t = 0.f;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) t += expf(s[i] - m);
+  t = wave_sum(t);
+  if (lane == 0) s_red[wave] = t;
+  __syncthreads();
+  t = 0.f;
+  for (int w = 0; w < nw; ++w) t += s_red[w];
+  const float inv = 1.0f / t;
+
+  for (int64_t i = threadIdx.x; i < n_max; i += blockDim.x)
+    s[i] = (i < n) ? expf(s[i] - m) * inv : 0.f;
+}
+
+template <typename T, int D, int Q>
+hipError_t launch_score_t(const float* q, const void* keys, const int32_t* lens, int B, int H,
+                          int64_t n_max, float scale, bool fill_pad, float* scores,
+                          hipStream_t s) {
+  using S = ScoreShape<T, D, Q>;
+  const int BH = B * H;
+  const int64_t tiles = (n_max + S::TILE - 1) / S::TILE;
+  if (BH == 0 || tiles == 0) return hipSuccess;
+  const int64_t grid = tiles * BH;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), 0, s, q,
+                     static_cast<const T*>(keys), lens, BH, H, n_max, (int)tiles, scale, scores,
+                     fill_pad ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_score_q(int Q, const float* q, const void* keys, const int32_t* lens, int B,
+                          int H, int64_t n_max, float scale, bool fill_pad, float* scores,
+                          hipStream_t s) {
+  if (Q == 1) return launch_score_t<T, D, 1>(q, keys, lens, B, H, n_max, scale, fill_pad, scores, s);
+  return launch_score_t<T, D, 2>(q, keys, lens, B, H, n_max, scale, fill_pad, scores, s);
+}
+
+}  // namespace
+
+hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, int B, int H,
+                        int Q, int D, int64_t n_max, int dtype, float scale, bool fill_pad,
+                        float* scores, hipStream_t s) {
+  if (dtype == kBF16) {
+    if (D == 128) return launch_score_q<uint16_t, 128>(Q, q, keys, lens, B, H, n_max, scale, fill_pad, scores, s);
+    return launch_score_q<uint16_t, 64>(Q, q, keys, lens, B, H, n_max, scale, fill_pad, scores, s);
+  }
+  if (D == 128) return launch_score_q<float, 128>(Q, q, keys, lens, B, H, n_max, scale, fill_pad, scores, s);
+  return launch_score_q<float, 64>(Q, q, keys, lens, B, H, n_max, scale, fill_pad, scores, s);
+}
+
+hipError_t launch_softmax_rows(float* scores, const int32_t* lens, int B, int H, int Q,
+                               int64_t n_max, hipStream_t s) {
+  const int rows = B * H * Q;
+  if (rows == 0 || n_max == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_softmax_rows, dim3(rows), dim3(1024), 0, s, scores, lens, H, Q, n_max);
+  return hipGetLastError();
+}
+
+}  // namespace dd

@@ -1,0 +1,163 @@
+"""Parity of dd_layer_step with the oracle's layer step, its independence of
+the prediction, the ring-slot contents, and the statistics."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from tests import parity
+from tests.gpu_util import announce, require_gpu, stored, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _stage(dd, w, layers):
+    data = []
+    for l in range(layers):
+        lay = gen.make_layer(w, l, "cpu")
+        data.append({
+            "q": lay["q"], "k": lay["k"], "v": lay["v"], "lens": lay["lens"],
+            "q_dev": lay["q"].cuda(), "k_dev": lay["k"].cuda(),
+            "k_host": to_host(dd, lay["k"]), "v_host": to_host(dd, lay["v"]),
+        })
+    return data
+
+
+def _run(dd, ctx, w, data, pred=None, ring=None, ws=None):
+    res = ctx.layer_step([d["q_dev"] for d in data], [d["k_dev"] for d in data],
+                         [d["k_host"] for d in data], [d["v_host"] for d in data],
+                         data[0]["lens"].cuda(), w.k, pred=pred, ring=ring, ws=ws)
+    torch.cuda.synchronize()
+    return res
+
+
+def _check_layer(w, d, res, l, pred_np=None):
+    """Sets (tie rule), attention (with exchange slack) and statistics of layer l."""
+    B, H, k = w.B, w.H, w.k
+    ref = oracle.layer_step(d["q"].numpy(), stored(d["k"]), stored(d["k"]), stored(d["v"]),
+                            d["lens"].numpy(), k, w.dtype, pred=pred_np)
+    lens_rows = np.repeat(d["lens"].numpy(), H)
+    s = ref["scores"]
+    cur = res["cur"][l].cpu().numpy().reshape(B * H, k)
+    spec = res["spec"][l].cpu().numpy().reshape(B * H, k)
+    diff_cur = parity.check_index_sets(cur, ref["cur"].reshape(B * H, k), s[:, :, 0].reshape(B * H, -1), lens_rows, k)
+    parity.check_index_sets(spec, ref["spec"].reshape(B * H, k), s[:, :, 1].reshape(B * H, -1), lens_rows, k)
+    slack = np.zeros(B * H)
+    vf = oracle.upcast(stored(d["v"]), w.dtype)
+    for r in diff_cur:
+        b, h = divmod(r, H)
+        n = int(lens_rows[r])
+        slack[r] = parity.exchange_slack(s[b, h, 0, :n], ref["cur"][b, h], vf[b, h, :n], k,
+                                         ref["out"][b, h])
+    got = res["out"][l].cpu().numpy().reshape(B * H, w.D)
+    worst = parity.check_attention(got, ref["out"].reshape(B * H, w.D), slack)
+    st = res["stats"][l].cpu().numpy()
+    valid = int(np.minimum(d["lens"].numpy(), k).sum()) * H
+    assert st[0] + st[1] == valid
+    if not diff_cur:
+        assert np.array_equal(st, ref["stats"]), (st, ref["stats"])
+    return worst, ref
+
+
+@pytest.mark.parametrize("name,kw,R", [
+    ("tiny", {}, 2),
+    ("llama7b_32k_layer", dict(H=4, n_max=8192), 2),
+    ("llama7b_32k_step", dict(L=1, B=2, H=2, n_max=8192, k=1024), 1),
+    ("llama13b_128k", dict(L=1, B=1, H=2, n_max=16384, k=2048), 2),
+    ("hiconc_64", dict(B=3, H=2, n_max=20000, len_lo=300, len_hi=20000, k=512), 3),
+])
+def test_layer_step_matches_oracle(name, kw, R):
+    dd = require_gpu()
+    w = gen.workload(name).scaled(**kw)
+    announce(f"layer_step {name} {kw} R={R}")
+    data = _stage(dd, w, w.L)
+    ctx = dd.Context(ring_slots=R)
+    cold = _run(dd, ctx, w, data)
+    for l in range(w.L):
+        worst, ref = _check_layer(w, data[l], cold, l)
+    # the oracle's own speculated set as the prediction: statistics must match
+    pred = [torch.from_numpy(ref["spec"]).cuda()]
+    hot = _run(dd, ctx, w, data, pred=pred)
+    _check_layer(w, data[0], hot, 0, pred_np=ref["spec"])
+    assert torch.equal(hot["out"][0], cold["out"][0])
+    ctx.close()
+    print(f"worst relative attention error {worst:.2e}")
+
+
+def test_outputs_do_not_depend_on_prediction_or_ring():
+    """Misses are fetched on the critical path, so any prediction (none,
+    perfect, speculated, random, another request's) and any ring size give
+    bitwise identical outputs; the slot holds the right rows."""
+    dd = require_gpu()
+    w = gen.workload("llama7b_32k_layer").scaled(L=3, B=2, H=4, n_max=6000, k=256)
+    announce("layer_step prediction independence")
+    data = _stage(dd, w, w.L)
+    B, H, k = w.B, w.H, w.k
+    base_ctx = dd.Context(ring_slots=2)
+    base = _run(dd, base_ctx, w, data)
+    rand = [gen.random_sorted_indices(B * H, k, torch.tensor([w.n_max] * (B * H)), seed=50 + l,
+                                      fill=0.9).reshape(B, H, k).cuda() for l in range(w.L)]
+    other = [c.flip(0).contiguous() for c in base["cur"]]  # request 1's set for request 0 and back
+    preds = {"spec": base["spec"], "perfect": base["cur"], "random": rand, "other": other,
+             "partial": [None, base["spec"][1], None]}
+    for R in (1, 2, 3):
+        ctx = dd.Context(ring_slots=R)
+        ring = torch.zeros(dd.ring_bytes(R, B, H, w.D, k, 1), dtype=torch.uint8, device="cuda")
+        for pname, pred in preds.items():
+            announce(f"  R={R} pred={pname}")
+            res = _run(dd, ctx, w, data, pred=pred, ring=ring)
+            for l in range(w.L):
+                assert torch.equal(res["out"][l], base["out"][l]), (R, pname, l)
+                assert torch.equal(res["lse"][l], base["lse"][l]), (R, pname, l)
+                assert torch.equal(res["cur"][l], base["cur"][l])
+                assert torch.equal(res["spec"][l], base["spec"][l])
+                cur_l = res["cur"][l].cpu().numpy()
+                p_l = None if pred[l] is None else pred[l].cpu().numpy()
+                st = res["stats"][l].cpu().numpy()
+                for_sets = [(set(cur_l[b, h][cur_l[b, h] >= 0].tolist()),
+                             set() if p_l is None else set(p_l[b, h][p_l[b, h] >= 0].tolist()))
+                            for b in range(B) for h in range(H)]
+                misses = sum(len(c - p) for c, p in for_sets)
+                hits = sum(len(c & p) for c, p in for_sets)
+                fetched = sum(len(p) for _, p in for_sets) + misses
+                assert st.tolist() == [misses, hits, fetched], (R, pname, l, st)
+            # slot of the last layer: row pos[j] holds host row cur[j] (K and V)
+            l = w.L - 1
+            slot = l % R
+            cur_l = res["cur"][l].cpu().numpy()
+            p_l = None if pred[l] is None else pred[l].cpu().numpy()
+            bk = oracle.bookkeeping(cur_l, p_l, w.n_max)
+            eb = 2
+            sb = 2 * B * H * 2 * k * w.D * eb
+            ring_np = ring[slot * sb:(slot + 1) * sb].cpu().numpy()
+            kslot = ring_np[:sb // 2].view(np.int16).reshape(B, H, 2 * k, w.D)
+            vslot = ring_np[sb // 2:].view(np.int16).reshape(B, H, 2 * k, w.D)
+            kh, vh = stored(data[l]["k_host"]), stored(data[l]["v_host"])
+            for b in range(B):
+                for h in range(H):
+                    for j in range(k):
+                        c = cur_l[b, h, j]
+                        if c < 0:
+                            continue
+                        r = bk["pos"][b, h, j]
+                        assert np.array_equal(kslot[b, h, r], kh[b, h, c])
+                        assert np.array_equal(vslot[b, h, r], vh[b, h, c])
+        ctx.close()
+    base_ctx.close()
+
+
+def test_layer_step_workspace_errors():
+    dd = require_gpu()
+    w = gen.workload("tiny")
+    announce("layer_step workspace errors")
+    data = _stage(dd, w, 1)
+    ctx = dd.Context(ring_slots=2)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(dd.DDError) as e:
+        _run(dd, ctx, w, data, ring=small)
+    assert e.value.code == 3
+    with pytest.raises(dd.DDError) as e:
+        _run(dd, ctx, w, data, ws=small)
+    assert e.value.code == 3
+    ctx.close()
