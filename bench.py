@@ -94,6 +94,9 @@ def main():
     ap.add_argument("--gather-cus", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time the eager loop only")
+    ap.add_argument("--prefetch-wgs", type=int, default=0)
+    ap.add_argument("--prefetch", default="auto", choices=["auto", "side", "fused"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -126,7 +129,8 @@ def main():
     eb = w.elem_bytes
     torch.cuda.synchronize()
 
-    ctx = dd.Context(ring_slots=args.ring, gather_cus=args.gather_cus)
+    ctx = dd.Context(ring_slots=args.ring, gather_cus=args.gather_cus,
+                     prefetch_wgs=args.prefetch_wgs, prefetch=args.prefetch)
     cur = [torch.empty(B, H, k, dtype=torch.int32, device=dev)]
     spec = [torch.empty(B, H, k, dtype=torch.int32, device=dev)]
     out = [torch.empty(B, H, D, dtype=torch.float32, device=dev)]
@@ -146,27 +150,82 @@ def main():
     for i in range(args.warmup):
         step(i, pred)
     torch.cuda.synchronize()
+    ref_out = out[0].clone()
+
+    # A decode loop replays the step from a HIP graph (one per key copy);
+    # each graph is checked against the eager result on several replays with
+    # eager work in between, else the eager loop is the headline.
+    # One graph holds one full step per key copy, back to back (each step
+    # still starts only after the previous one ended, as in decode).
+    graph, graph_note = None, None
+    S = len(k_copies)
+    if not args.no_graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in range(S):
+                    step(c, pred)
+            for rep in range(3):
+                out[0].zero_()
+                g.replay()
+                torch.cuda.synchronize()
+                if not torch.equal(out[0], ref_out):
+                    raise RuntimeError(f"graph replay {rep} differs from the eager step")
+                step(rep, pred)
+                torch.cuda.synchronize()
+            graph = g
+        except Exception as e:  # noqa: BLE001
+            graph, graph_note = None, f"graph replay unavailable: {e}"
 
     K = args.steps
-    stage = EventSet(K * dd.DD_STAGE_EVENTS)
-    bounds = EventSet(2)
+    E = dd.DD_STAGE_EVENTS
+    bounds = EventSet(4)
+    if graph is not None:
+        reps = max(1, K // S)
+        for i in range(max(1, args.warmup // S)):
+            graph.replay()
+        torch.cuda.synchronize()
+        bounds.record(2)
+        for i in range(reps):
+            graph.replay()
+        bounds.record(3)
+        torch.cuda.synchronize()
+        graph_ms = bounds.elapsed_ms(2, 3) / (reps * S)
+        if not torch.equal(out[0], ref_out):
+            raise RuntimeError("graph replays changed the output")
+
+    # Eager timed region: K steps; the only events inside a step bracket the
+    # scoring kernel (the dominant one), on the stream it runs on.
+    score_ev = EventSet(2 * K)
     torch.cuda.synchronize()
     bounds.record(0)
     for i in range(K):
-        step(i, pred, timing=stage.handles[i * dd.DD_STAGE_EVENTS:(i + 1) * dd.DD_STAGE_EVENTS])
+        t = [None] * E
+        t[0], t[1] = score_ev.handles[2 * i], score_ev.handles[2 * i + 1]
+        step(i, pred, timing=t)
     bounds.record(1)
     torch.cuda.synchronize()
-    total_ms = bounds.elapsed_ms(0, 1)
-    ms_per_step = total_ms / K
+    eager_ms = bounds.elapsed_ms(0, 1) / K
+    ms_per_step = graph_ms if graph is not None else eager_ms
+    t_score = float(np.mean([score_ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)]))
+
+    # Breakdown: the same steps again with every stage bracketed (the extra
+    # event records make these steps slightly longer; not the headline).
+    stage = EventSet(K * E)
+    for i in range(K):
+        step(i, pred, timing=stage.handles[i * E:(i + 1) * E])
+    torch.cuda.synchronize()
 
     def avg(a, b):
-        return float(np.mean([stage.elapsed_ms(i * 7 + a, i * 7 + b) for i in range(K)]))
+        return float(np.mean([stage.elapsed_ms(i * E + a, i * E + b) for i in range(K)]))
 
-    t_score = avg(0, 1)
     t_topk = avg(1, 2)
-    t_miss = avg(2, 3)
+    t_wait = avg(2, 3)
     t_attn = avg(3, 4)
-    t_prefetch = avg(5, 6)
+    # Events 5 and 6 are recorded only when the prediction is fetched on the
+    # side stream (the default for a single layer is the fused fetch).
+    t_prefetch = avg(5, 6) if args.prefetch == "side" else None
+    t_step_instr = avg(0, 4)
     st = stats[0].cpu().tolist()
     misses, hits, fetched = st
     valid = int(torch.clamp(lens, max=k).sum().item()) * H
@@ -176,7 +235,10 @@ def main():
     score_bytes = n_keys * D * eb + n_keys * 2 * 4
     score_gbps = score_bytes / (t_score * 1e-3) / 1e9
     prefetch_bytes = valid * 2 * D * eb              # k rows of K and V per (b, h)
-    prefetch_gbps = prefetch_bytes / (t_prefetch * 1e-3) / 1e9
+    # The prefetch runs on the side stream (own events) or inside the scoring
+    # kernel (then its rate is bounded below by that kernel's duration).
+    t_pf = t_prefetch if t_prefetch is not None else t_score
+    prefetch_gbps = prefetch_bytes / (t_pf * 1e-3) / 1e9
     miss_bytes = misses * 2 * D * eb
 
     # Reference rates measured in the same process.
@@ -231,9 +293,14 @@ def main():
                      "avg_launch_us": t_score * 1e3},
         "cpu_baseline": cpu,
         "layer_step_us": ms_per_step * 1e3,
-        "stages_us": {"score": t_score * 1e3, "topk_bookkeeping": t_topk * 1e3,
-                      "miss_fetch": t_miss * 1e3, "attention": t_attn * 1e3,
-                      "prefetch_side_stream": t_prefetch * 1e3},
+        "timing": (f"hip-graph replay, {S} steps per graph" if graph is not None else "eager"),
+        "eager_layer_step_us": eager_ms * 1e3,
+        "graph_note": graph_note,
+        "stages_us": {"score": t_score * 1e3,
+                      "topk_bookkeeping_missfetch": t_topk * 1e3,
+                      "wait_for_prefetch": t_wait * 1e3, "attention": t_attn * 1e3,
+                      "prefetch_side_stream": None if t_prefetch is None else t_prefetch * 1e3,
+                      "instrumented_step": t_step_instr * 1e3},
         "score_keys_per_s": n_keys / (t_score * 1e-3),
         "score_frac_of_measured_hbm_copy": score_gbps / hbm_copy,
         "gather_GBps": prefetch_gbps,

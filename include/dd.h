@@ -175,8 +175,20 @@ typedef struct dd_ctx_config {
   int gather_cus;  /* 0: side stream without a CU mask.  > 0: the side stream
                       is restricted to this many CUs and the layer step's own
                       main stream to the others */
-  int reserved;    /* must be 0 */
+  int prefetch_wgs; /* workgroups of the prefetch gather (0: 16).  Fewer keep
+                      fewer host reads outstanding, which disturbs the
+                      concurrent HBM-bound scoring less; enough of them
+                      still saturate the host link */
+  int prefetch_mode; /* DD_PREFETCH_AUTO (fused for L == 1, side stream
+                      otherwise), DD_PREFETCH_SIDE or DD_PREFETCH_FUSED */
 } dd_ctx_config;
+
+/* DD_PREFETCH_SIDE: the prediction of layer l is fetched on the side stream
+ * as soon as its ring slot is free, so it overlaps earlier layers' work.
+ * DD_PREFETCH_FUSED: it is fetched by extra workgroups of layer l's own
+ * scoring kernel (one stream, no cross-stream wait; it overlaps that
+ * layer's key scan).  Results are identical either way. */
+enum { DD_PREFETCH_AUTO = 0, DD_PREFETCH_SIDE = 1, DD_PREFETCH_FUSED = 2 };
 
 /* Creates the side stream and events on the current device.  The context
  * may only be used with that device current. */

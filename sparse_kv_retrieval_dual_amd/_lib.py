@@ -32,7 +32,8 @@ P = c_void_p  # every pointer crosses as an address
 
 
 class CtxConfig(ctypes.Structure):
-    _fields_ = [("ring_slots", c_int), ("gather_cus", c_int), ("reserved", c_int)]
+    _fields_ = [("ring_slots", c_int), ("gather_cus", c_int), ("prefetch_wgs", c_int),
+                ("prefetch_mode", c_int)]
 
 
 class LayerStepArgs(ctypes.Structure):

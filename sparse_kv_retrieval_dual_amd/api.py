@@ -200,9 +200,14 @@ def _ptr_array(ts):
 class Context:
     """dd_ctx: the side stream, events and ring configuration of the layer step."""
 
-    def __init__(self, ring_slots: int = 2, gather_cus: int = 0):
+    PREFETCH_MODES = {"auto": 0, "side": 1, "fused": 2}
+
+    def __init__(self, ring_slots: int = 2, gather_cus: int = 0, prefetch_wgs: int = 0,
+                 prefetch: str = "auto"):
         lib = _lib()
-        cfg = L.CtxConfig(ring_slots=int(ring_slots), gather_cus=int(gather_cus), reserved=0)
+        cfg = L.CtxConfig(ring_slots=int(ring_slots), gather_cus=int(gather_cus),
+                          prefetch_wgs=int(prefetch_wgs),
+                          prefetch_mode=self.PREFETCH_MODES[prefetch])
         h = ctypes.c_void_p()
         L.check(lib.dd_ctx_create(ctypes.byref(cfg), ctypes.byref(h)))
         self._h = h

@@ -12,11 +12,14 @@
 
 #include "dd.h"
 #include "dd_internal.h"
+#include "gather_body.h"
 
 struct dd_ctx {
   int device = -1;
   int ring_slots = 1;
   int gather_cus = 0;
+  int prefetch_wgs = 16;
+  int prefetch_mode = DD_PREFETCH_AUTO;
   hipStream_t side = nullptr;       // prefetch gathers
   hipStream_t main_own = nullptr;   // CU-masked main stream (gather_cus > 0 only)
   hipEvent_t ev_start = nullptr;    // caller stream at entry
@@ -139,7 +142,8 @@ DD_API int dd_score(const float* q, const void* keys, const int32_t* lens, int B
   if (!q || !keys || !lens || !scores) return fail(DD_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(keys)) return fail(DD_ERR_INVALID_ARG, "keys must be 16-byte aligned");
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
-  hipError_t e = dd::launch_score(q, keys, lens, B, H, Q, D, n_max, kv_dtype, sc, true, scores, stream);
+  hipError_t e = dd::launch_score(q, keys, lens, B, H, Q, D, n_max, kv_dtype, sc, true, scores,
+                                  nullptr, 0, stream);
   if (e != hipSuccess) return hip_fail(e, "score kernel launch");
   if (kind == DD_ALPHA) {
     e = dd::launch_softmax_rows(scores, lens, B, H, Q, n_max, stream);
@@ -179,8 +183,8 @@ DD_API int dd_gather(const void* k_host, const void* v_host, const int32_t* idx,
     return fail(DD_ERR_INVALID_ARG, "host and row buffers must be 16-byte aligned");
   const int rowb = D * dd::elem_bytes(dtype);
   hipError_t e = dd::launch_gather(k_host, v_host, n_max, rowb, idx, m, cnt, B * H,
-                                   k_host ? k_rows : nullptr, v_host ? v_rows : nullptr, m, 0,
-                                   nullptr, nullptr, stream);
+                                   k_host ? k_rows : nullptr, v_host ? v_rows : nullptr, m, 0, 0,
+                                   stream);
   if (e != hipSuccess) return hip_fail(e, "gather kernel launch");
   return DD_OK;
 }
@@ -210,7 +214,7 @@ DD_API int dd_sparse_attn(const float* q, int64_t q_stride_bh, const void* k_row
     return fail(DD_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
   hipError_t e = dd::launch_attn(q, q_stride_bh, k_rows, v_rows, pos, cnt, B, H, k, m, D, dtype,
-                                 sc, out, lse, ws, stream);
+                                 sc, out, lse, ws, nullptr, nullptr, nullptr, stream);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   return DD_OK;
 }
@@ -230,11 +234,15 @@ DD_API int dd_ctx_create(const dd_ctx_config* cfg, dd_ctx** ctx) {
   *ctx = nullptr;
   if (cfg->ring_slots < 1 || cfg->ring_slots > 64)
     return fail(DD_ERR_INVALID_ARG, "ring_slots must be in [1, 64] (got %d)", cfg->ring_slots);
-  if (cfg->gather_cus < 0 || cfg->reserved != 0)
-    return fail(DD_ERR_INVALID_ARG, "gather_cus must be >= 0 and reserved 0");
+  if (cfg->gather_cus < 0 || cfg->prefetch_wgs < 0)
+    return fail(DD_ERR_INVALID_ARG, "gather_cus and prefetch_wgs must be >= 0");
+  if (cfg->prefetch_mode < DD_PREFETCH_AUTO || cfg->prefetch_mode > DD_PREFETCH_FUSED)
+    return fail(DD_ERR_INVALID_ARG, "unknown prefetch_mode %d", cfg->prefetch_mode);
   dd_ctx* c = new dd_ctx();
   c->ring_slots = cfg->ring_slots;
   c->gather_cus = cfg->gather_cus;
+  c->prefetch_wgs = cfg->prefetch_wgs > 0 ? cfg->prefetch_wgs : 16;
+  c->prefetch_mode = cfg->prefetch_mode;
   hipError_t e = hipGetDevice(&c->device);
   const int cus = dd::device_info().cus;
   if (e == hipSuccess && c->gather_cus > 0) {
@@ -331,10 +339,17 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
   bool any_pred = false;
   if (a->pred)
     for (int l = 0; l < a->L; ++l) any_pred = any_pred || (a->pred[l] != nullptr);
+  // Where the prediction is fetched: on the side stream ahead of the layer
+  // (it can then overlap the previous layer's work), or by extra workgroups
+  // of the layer's own scoring kernel (no second stream, no cross-stream
+  // wait; the transfer overlaps that layer's key scan only).
+  const bool fused = c->prefetch_mode == DD_PREFETCH_FUSED ||
+                     (c->prefetch_mode == DD_PREFETCH_AUTO && a->L == 1);
+  const bool use_side = any_pred && !fused;
 
   DD_CHECK_HIP(hipEventRecord(c->ev_start, caller), "record start");
   if (ms != caller) DD_CHECK_HIP(hipStreamWaitEvent(ms, c->ev_start, 0), "main waits start");
-  if (any_pred) DD_CHECK_HIP(hipStreamWaitEvent(side, c->ev_start, 0), "side waits start");
+  if (use_side) DD_CHECK_HIP(hipStreamWaitEvent(side, c->ev_start, 0), "side waits start");
 
   auto tev = [&](int l, int i) -> hipEvent_t {
     return a->timing ? a->timing[(size_t)l * DD_STAGE_EVENTS + i] : nullptr;
@@ -345,12 +360,16 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     char* kslot = static_cast<char*>(a->ring) + (size_t)slot * sbytes;
     char* vslot = kslot + sbytes / 2;
     const int32_t* P = a->pred ? a->pred[l] : nullptr;
+    const dd::GatherJob pf{static_cast<const uint8_t*>(a->k_host[l]),
+                           static_cast<const uint8_t*>(a->v_host[l]), a->n_max, P, k, nullptr,
+                           (int64_t)BH * k, reinterpret_cast<uint8_t*>(kslot),
+                           reinterpret_cast<uint8_t*>(vslot), 2 * (int64_t)k, 0};
 
-    if (P) {
+    if (P && use_side) {
       if (l >= R) DD_CHECK_HIP(hipStreamWaitEvent(side, c->ev_free[slot], 0), "side waits slot");
       if (tev(l, 5)) DD_CHECK_HIP(hipEventRecord(tev(l, 5), side), "timing");
       hipError_t e = dd::launch_gather(a->k_host[l], a->v_host[l], a->n_max, rowb, P, k, nullptr,
-                                       BH, kslot, vslot, 2 * (int64_t)k, 0, nullptr, nullptr, side);
+                                       BH, kslot, vslot, 2 * (int64_t)k, 0, c->prefetch_wgs, side);
       if (e != hipSuccess) return hip_fail(e, "prefetch gather launch");
       if (tev(l, 6)) DD_CHECK_HIP(hipEventRecord(tev(l, 6), side), "timing");
       DD_CHECK_HIP(hipEventRecord(c->ev_gathered[slot], side), "record gathered");
@@ -358,7 +377,8 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
 
     if (tev(l, 0)) DD_CHECK_HIP(hipEventRecord(tev(l, 0), ms), "timing");
     hipError_t e = dd::launch_score(a->q[l], a->k_dev[l], a->lens, B, H, 2, D, a->n_max, a->dtype,
-                                    sc, false, scores, ms);
+                                    sc, false, scores, (P && fused) ? &pf : nullptr,
+                                    c->prefetch_wgs, ms);
     if (e != hipSuccess) return hip_fail(e, "score kernel launch");
     if (tev(l, 1)) DD_CHECK_HIP(hipEventRecord(tev(l, 1), ms), "timing");
     const dd::TopkBook book{P, pos, miss, counts};
@@ -366,16 +386,17 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
                         &book, ms);
     if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
     if (tev(l, 2)) DD_CHECK_HIP(hipEventRecord(tev(l, 2), ms), "timing");
-    if (P) DD_CHECK_HIP(hipStreamWaitEvent(ms, c->ev_gathered[slot], 0), "main waits prefetch");
-    e = dd::launch_gather(a->k_host[l], a->v_host[l], a->n_max, rowb, miss, k, counts, BH, kslot,
-                          vslot, 2 * (int64_t)k, k, counts, a->stats ? a->stats + 3 * (size_t)l : nullptr, ms);
-    if (e != hipSuccess) return hip_fail(e, "miss gather launch");
+    if (P && use_side) DD_CHECK_HIP(hipStreamWaitEvent(ms, c->ev_gathered[slot], 0), "main waits prefetch");
     if (tev(l, 3)) DD_CHECK_HIP(hipEventRecord(tev(l, 3), ms), "timing");
+    // Misses are read from host memory by the attention kernel itself (and
+    // stored into their slot rows k + t), overlapping the slot reads.
+    const dd::AttnMiss am{a->k_host[l], a->v_host[l], a->cur_idx[l], a->n_max, k};
     e = dd::launch_attn(a->q[l], 2 * (int64_t)D, kslot, vslot, pos, nullptr, B, H, k, 2 * k, D,
-                        a->dtype, sc, a->out[l], a->lse ? a->lse[l] : nullptr, attn_ws, ms);
+                        a->dtype, sc, a->out[l], a->lse ? a->lse[l] : nullptr, attn_ws, counts,
+                        a->stats ? a->stats + 3 * (size_t)l : nullptr, &am, ms);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
     if (tev(l, 4)) DD_CHECK_HIP(hipEventRecord(tev(l, 4), ms), "timing");
-    DD_CHECK_HIP(hipEventRecord(c->ev_free[slot], ms), "record slot free");
+    if (use_side) DD_CHECK_HIP(hipEventRecord(c->ev_free[slot], ms), "record slot free");
   }
   if (ms != caller) {
     DD_CHECK_HIP(hipEventRecord(c->ev_end, ms), "record end");

@@ -23,11 +23,15 @@ const DeviceInfo& device_info();
 
 inline int elem_bytes(int dtype) { return dtype == kF32 ? 4 : 2; }
 
+struct GatherJob;
+
 // Scaled logits of Q queries against every key; rows past lens[b] become
-// -inf when fill_pad is set and are left untouched otherwise.
+// -inf when fill_pad is set and are left untouched otherwise.  When pf is
+// set, pf_wgs extra workgroups (dispatched first) run that row gather
+// alongside the scoring (row_bytes = D * element size).
 hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, int B, int H,
                         int Q, int D, int64_t n_max, int dtype, float scale, bool fill_pad,
-                        float* scores, hipStream_t s);
+                        float* scores, const GatherJob* pf, int pf_wgs, hipStream_t s);
 
 // In-place softmax of each score row over its valid keys; 0 past lens[b].
 hipError_t launch_softmax_rows(float* scores, const int32_t* lens, int B, int H, int Q,
@@ -49,20 +53,33 @@ hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, i
 
 // Row gather from pinned host memory.  Entry j < cnt[bh] (m if cnt is null)
 // of slab bh copies host row idx[bh*m + j] (zero row if out of range) to
-// destination row bh*dst_rows_per_bh + dst_row0 + j.  When stats is set,
-// workgroup 0 also writes stats[0..2] = sums over slabs of counts planes
-// (misses, hits, fetchable prediction entries + misses).
+// destination row bh*dst_rows_per_bh + dst_row0 + j.  At most max_wgs
+// workgroups (0: a default for a standalone copy) keep rows in flight.
 hipError_t launch_gather(const void* k_host, const void* v_host, int64_t n_max, int row_bytes,
                          const int32_t* idx, int m, const int32_t* cnt, int BH, void* k_dst,
-                         void* v_dst, int64_t dst_rows_per_bh, int dst_row0,
-                         const int32_t* counts, int64_t* stats, hipStream_t s);
+                         void* v_dst, int64_t dst_rows_per_bh, int dst_row0, int max_wgs,
+                         hipStream_t s);
 
 size_t attn_workspace(int B, int H, int k, int D);
 
+// Rows the attention kernel reads straight from host memory: an entry j
+// whose row pos[j] is >= first_miss_row is host row cur[bh*k + j]; the
+// kernel also stores it into that row of k_rows / v_rows.
+struct AttnMiss {
+  const void* k_host;  // pinned host [BH][n_max][D]
+  const void* v_host;
+  const int32_t* cur;  // [BH][k]
+  int64_t n_max;
+  int first_miss_row;
+};
+
+// Sparse attention; when stats is set, workgroup 0 also writes stats[0..2]
+// = sums over slabs of the counts planes (misses, hits, fetchable + misses).
 hipError_t launch_attn(const float* q, int64_t q_stride_bh, const void* k_rows,
                        const void* v_rows, const int32_t* pos, const int32_t* cnt, int B, int H,
                        int k, int m, int D, int dtype, float scale, float* out, float* lse,
-                       void* ws, hipStream_t s);
+                       void* ws, const int32_t* counts, int64_t* stats, const AttnMiss* miss,
+                       hipStream_t s);
 
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 

@@ -10,15 +10,25 @@
 // rows in flight and the Q*U partial dot products are folded across the LPR
 // lanes with a transposing butterfly that leaves exactly one finished score
 // per lane.
+//
+// Optionally the first few workgroups of the grid do not score: they gather
+// the layer's predicted K/V rows from host memory into its slot (the
+// prefetch), so that the host-link transfer overlaps the HBM-bound scan
+// inside one kernel, with no second stream and no cross-stream wait.
 #include "dd_device.h"
 #include "dd_internal.h"
+#include "gather_body.h"
 
 namespace dd {
 
 namespace {
 
+// A workgroup scores 4 waves x 2 iterations x (64 / Q) keys: 256 keys of
+// 256 B for the two-query bf16 case (64 KB per workgroup).  Smaller tiles
+// than that lost to launch overhead and larger ones to the last partial
+// round of workgroups (measured on MI355X for 32 x 32768 keys).
 constexpr int kScoreWaves = 4;
-constexpr int kScoreIters = 4;
+constexpr int kScoreIters = 2;
 
 template <typename T, int D, int Q>
 struct ScoreShape {
@@ -35,12 +45,17 @@ template <typename T, int D, int Q>
 __global__ __launch_bounds__(kScoreWaves * 64) void k_score(
     const float* __restrict__ q, const T* __restrict__ keys, const int32_t* __restrict__ lens,
     int BH, int H, int64_t n_max, int tiles, float scale, float* __restrict__ scores,
-    int fill_pad) {
+    int fill_pad, GatherJob pf, int pf_wgs) {
   using S = ScoreShape<T, D, Q>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  if ((int)blockIdx.x < pf_wgs) {
+    gather_rows<D * (int)sizeof(T)>(pf, (int64_t)blockIdx.x * kScoreWaves + wave,
+                                    (int64_t)pf_wgs * kScoreWaves);
+    return;
+  }
   int bh, tile;
-  xcd_tile_map(blockIdx.x, tiles, BH, bh, tile);
+  xcd_tile_map((int)blockIdx.x - pf_wgs, tiles, BH, bh, tile);
   const int64_t n = clamp_len(lens[bh / H], n_max);
   const int64_t tile0 = (int64_t)tile * S::TILE;
   if (tile0 >= n && !fill_pad) return;
@@ -132,41 +147,56 @@ __global__ __launch_bounds__(1024) void k_softmax_rows(float* __restrict__ score
     s[i] = (i < n) ? expf(s[i] - m) * inv : 0.f;
 }
 
+struct ScoreLaunch {
+  const float* q;
+  const void* keys;
+  const int32_t* lens;
+  int B, H;
+  int64_t n_max;
+  float scale;
+  bool fill_pad;
+  float* scores;
+  GatherJob pf;
+  int pf_wgs;
+  hipStream_t s;
+};
+
 template <typename T, int D, int Q>
-hipError_t launch_score_t(const float* q, const void* keys, const int32_t* lens, int B, int H,
-                          int64_t n_max, float scale, bool fill_pad, float* scores,
-                          hipStream_t s) {
+hipError_t launch_score_t(const ScoreLaunch& a) {
   using S = ScoreShape<T, D, Q>;
-  const int BH = B * H;
-  const int64_t tiles = (n_max + S::TILE - 1) / S::TILE;
-  if (BH == 0 || tiles == 0) return hipSuccess;
-  const int64_t grid = tiles * BH;
+  const int BH = a.B * a.H;
+  const int64_t tiles = (a.n_max + S::TILE - 1) / S::TILE;
+  if (BH == 0 || (tiles == 0 && a.pf_wgs == 0)) return hipSuccess;
+  const int64_t grid = tiles * BH + a.pf_wgs;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), 0, s, q,
-                     static_cast<const T*>(keys), lens, BH, H, n_max, (int)tiles, scale, scores,
-                     fill_pad ? 1 : 0);
+  hipLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), 0, a.s,
+                     a.q, static_cast<const T*>(a.keys), a.lens, BH, a.H, a.n_max, (int)tiles,
+                     a.scale, a.scores, a.fill_pad ? 1 : 0, a.pf, a.pf_wgs);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_score_q(int Q, const float* q, const void* keys, const int32_t* lens, int B,
-                          int H, int64_t n_max, float scale, bool fill_pad, float* scores,
-                          hipStream_t s) {
-  if (Q == 1) return launch_score_t<T, D, 1>(q, keys, lens, B, H, n_max, scale, fill_pad, scores, s);
-  return launch_score_t<T, D, 2>(q, keys, lens, B, H, n_max, scale, fill_pad, scores, s);
+hipError_t launch_score_q(int Q, const ScoreLaunch& a) {
+  if (Q == 1) return launch_score_t<T, D, 1>(a);
+  return launch_score_t<T, D, 2>(a);
 }
 
 }  // namespace
 
 hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, int B, int H,
                         int Q, int D, int64_t n_max, int dtype, float scale, bool fill_pad,
-                        float* scores, hipStream_t s) {
-  if (dtype == kBF16) {
-    if (D == 128) return launch_score_q<uint16_t, 128>(Q, q, keys, lens, B, H, n_max, scale, fill_pad, scores, s);
-    return launch_score_q<uint16_t, 64>(Q, q, keys, lens, B, H, n_max, scale, fill_pad, scores, s);
+                        float* scores, const GatherJob* pf, int pf_wgs, hipStream_t s) {
+  ScoreLaunch a{q, keys, lens, B, H, n_max, scale, fill_pad, scores, GatherJob{}, 0, s};
+  if (pf != nullptr && pf->total > 0 && pf_wgs > 0) {
+    a.pf = *pf;
+    a.pf_wgs = (pf_wgs + 7) & ~7;  // keeps the scoring tiles' XCD placement
   }
-  if (D == 128) return launch_score_q<float, 128>(Q, q, keys, lens, B, H, n_max, scale, fill_pad, scores, s);
-  return launch_score_q<float, 64>(Q, q, keys, lens, B, H, n_max, scale, fill_pad, scores, s);
+  if (dtype == kBF16) {
+    if (D == 128) return launch_score_q<uint16_t, 128>(Q, a);
+    return launch_score_q<uint16_t, 64>(Q, a);
+  }
+  if (D == 128) return launch_score_q<float, 128>(Q, a);
+  return launch_score_q<float, 64>(Q, a);
 }
 
 hipError_t launch_softmax_rows(float* scores, const int32_t* lens, int B, int H, int Q,

@@ -28,12 +28,15 @@ def _rt():
         h.hipEventSynchronize.restype = ctypes.c_int
         h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         h.hipEventElapsedTime.restype = ctypes.c_int
+        h.hipGetLastError.argtypes = []
+        h.hipGetLastError.restype = ctypes.c_int
         _hip = h
     return _hip
 
 
 def _ok(rc, what):
     if rc != 0:
+        _rt().hipGetLastError()  # do not leave the error for the next runtime call
         raise RuntimeError(f"{what} failed with HIP error {rc}")
 
 

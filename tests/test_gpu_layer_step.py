@@ -101,11 +101,11 @@ def test_outputs_do_not_depend_on_prediction_or_ring():
     other = [c.flip(0).contiguous() for c in base["cur"]]  # request 1's set for request 0 and back
     preds = {"spec": base["spec"], "perfect": base["cur"], "random": rand, "other": other,
              "partial": [None, base["spec"][1], None]}
-    for R in (1, 2, 3):
-        ctx = dd.Context(ring_slots=R)
+    for R, mode in ((1, "side"), (2, "side"), (3, "side"), (1, "fused"), (2, "fused")):
+        ctx = dd.Context(ring_slots=R, prefetch=mode, prefetch_wgs=8 if R == 1 else 0)
         ring = torch.zeros(dd.ring_bytes(R, B, H, w.D, k, 1), dtype=torch.uint8, device="cuda")
         for pname, pred in preds.items():
-            announce(f"  R={R} pred={pname}")
+            announce(f"  R={R} prefetch={mode} pred={pname}")
             res = _run(dd, ctx, w, data, pred=pred, ring=ring)
             for l in range(w.L):
                 assert torch.equal(res["out"][l], base["out"][l]), (R, pname, l)
