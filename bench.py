@@ -30,23 +30,31 @@ HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def _source_hash(name: str) -> str:
-    p = os.path.join(ROOT, "sparse_kv_retrieval_dual_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+# The scoring kernel's source: its file and the headers it includes.
+SCORE_SOURCES = ("score.hip", "dd_device.h", "gather_body.h")
 
 
-def _counter_traffic(kernel_file: str, workload: str):
+def _source_hash(files) -> str:
+    h = hashlib.sha256()
+    for name in files:
+        with open(os.path.join(ROOT, "sparse_kv_retrieval_dual_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_traffic(kernel: str, sources, workload: str):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current kernel source (else None)."""
-    path = os.path.join(PROFILES, f"{os.path.splitext(kernel_file)[0]}_{workload}_counters.txt")
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(path):
-        if ":" in line and not line.startswith("#"):
-            key, val = line.split(":", 1)
-            fields[key.strip()] = val.strip()
-    if fields.get("source_sha256_16") != _source_hash(kernel_file):
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("source_sha256_16") != _source_hash(sources):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -269,7 +277,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, lay, args.cpu_seconds)
 
-    traffic = _counter_traffic("score.hip", w.name)
+    traffic = _counter_traffic("score", SCORE_SOURCES, w.name)
     result = {
         "metric": METRIC,
         "value": n_keys / (ms_per_step * 1e-3),
@@ -288,7 +296,7 @@ def main():
                    "ring_slots": args.ring, "hbm_key_copies": len(k_copies)},
         "roofline": {"bound": "hbm", "achieved": score_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": score_gbps / HBM_PEAK_GBPS,
-                     "traffic": None if traffic is None else traffic,
+                     "traffic": traffic,
                      "kernel": "score", "algorithmic_bytes": score_bytes,
                      "avg_launch_us": t_score * 1e3},
         "cpu_baseline": cpu,
@@ -297,7 +305,7 @@ def main():
         "eager_layer_step_us": eager_ms * 1e3,
         "graph_note": graph_note,
         "stages_us": {"score": t_score * 1e3,
-                      "topk_bookkeeping_missfetch": t_topk * 1e3,
+                      "topk_bookkeeping": t_topk * 1e3,
                       "wait_for_prefetch": t_wait * 1e3, "attention": t_attn * 1e3,
                       "prefetch_side_stream": None if t_prefetch is None else t_prefetch * 1e3,
                       "instrumented_step": t_step_instr * 1e3},

@@ -64,11 +64,14 @@ enum { DD_F32 = 0, DD_BF16 = 1 };      /* element type of K and V */
 enum { DD_LOGITS = 0, DD_ALPHA = 1 };  /* what dd_score writes */
 
 #define DD_MAX_K 4096
-/* Events per layer recorded by dd_layer_step when args.timing is set:
- * [0] before scoring, [1] after scoring, [2] after top-k and bookkeeping,
- * [3] after the miss fetch, [4] after attention (all on the main stream),
- * [5] before and [6] after the prefetch gather (on the side stream; left
- * unrecorded for a layer without a prediction). */
+/* Events per layer recorded by dd_layer_step when args.timing is set (an
+ * entry may be NULL to skip it): [0] start and [1] end of the scoring
+ * kernel (taken by that dispatch itself when both are given), [2] after
+ * top-k and bookkeeping, [3] after the wait for a side-stream prefetch,
+ * [4] after attention (which also fetches the misses) -- all on the main
+ * stream -- and [5] before and [6] after the prefetch gather on the side
+ * stream (left unrecorded when the prediction is fetched inside the
+ * scoring kernel or the layer has none). */
 #define DD_STAGE_EVENTS 7
 
 /* Text of the last non-OK status returned on this thread ("" if none). */
@@ -175,7 +178,7 @@ typedef struct dd_ctx_config {
   int gather_cus;  /* 0: side stream without a CU mask.  > 0: the side stream
                       is restricted to this many CUs and the layer step's own
                       main stream to the others */
-  int prefetch_wgs; /* workgroups of the prefetch gather (0: 16).  Fewer keep
+  int prefetch_wgs; /* workgroups of the prefetch gather (0: 32).  Fewer keep
                       fewer host reads outstanding, which disturbs the
                       concurrent HBM-bound scoring less; enough of them
                       still saturate the host link */

@@ -18,7 +18,7 @@ struct dd_ctx {
   int device = -1;
   int ring_slots = 1;
   int gather_cus = 0;
-  int prefetch_wgs = 16;
+  int prefetch_wgs = 32;
   int prefetch_mode = DD_PREFETCH_AUTO;
   hipStream_t side = nullptr;       // prefetch gathers
   hipStream_t main_own = nullptr;   // CU-masked main stream (gather_cus > 0 only)
@@ -241,7 +241,7 @@ DD_API int dd_ctx_create(const dd_ctx_config* cfg, dd_ctx** ctx) {
   dd_ctx* c = new dd_ctx();
   c->ring_slots = cfg->ring_slots;
   c->gather_cus = cfg->gather_cus;
-  c->prefetch_wgs = cfg->prefetch_wgs > 0 ? cfg->prefetch_wgs : 16;
+  c->prefetch_wgs = cfg->prefetch_wgs > 0 ? cfg->prefetch_wgs : 32;
   c->prefetch_mode = cfg->prefetch_mode;
   hipError_t e = hipGetDevice(&c->device);
   const int cus = dd::device_info().cus;
@@ -375,12 +375,16 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
       DD_CHECK_HIP(hipEventRecord(c->ev_gathered[slot], side), "record gathered");
     }
 
-    if (tev(l, 0)) DD_CHECK_HIP(hipEventRecord(tev(l, 0), ms), "timing");
+    // Events 0 and 1 are taken by the scoring dispatch itself (its start and
+    // end), so they time exactly that kernel.
+    const bool score_ev = tev(l, 0) && tev(l, 1);
+    if (tev(l, 0) && !score_ev) DD_CHECK_HIP(hipEventRecord(tev(l, 0), ms), "timing");
     hipError_t e = dd::launch_score(a->q[l], a->k_dev[l], a->lens, B, H, 2, D, a->n_max, a->dtype,
                                     sc, false, scores, (P && fused) ? &pf : nullptr,
-                                    c->prefetch_wgs, ms);
+                                    c->prefetch_wgs, ms, score_ev ? tev(l, 0) : nullptr,
+                                    score_ev ? tev(l, 1) : nullptr);
     if (e != hipSuccess) return hip_fail(e, "score kernel launch");
-    if (tev(l, 1)) DD_CHECK_HIP(hipEventRecord(tev(l, 1), ms), "timing");
+    if (tev(l, 1) && !score_ev) DD_CHECK_HIP(hipEventRecord(tev(l, 1), ms), "timing");
     const dd::TopkBook book{P, pos, miss, counts};
     e = dd::launch_topk(scores, a->lens, B, H, 2, a->n_max, k, a->cur_idx[l], a->spec_idx[l], k,
                         &book, ms);

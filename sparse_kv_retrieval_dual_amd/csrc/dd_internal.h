@@ -28,10 +28,12 @@ struct GatherJob;
 // Scaled logits of Q queries against every key; rows past lens[b] become
 // -inf when fill_pad is set and are left untouched otherwise.  When pf is
 // set, pf_wgs extra workgroups (dispatched first) run that row gather
-// alongside the scoring (row_bytes = D * element size).
+// alongside the scoring (row_bytes = D * element size).  When both events
+// are given they are recorded at the kernel's own start and end.
 hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, int B, int H,
                         int Q, int D, int64_t n_max, int dtype, float scale, bool fill_pad,
-                        float* scores, const GatherJob* pf, int pf_wgs, hipStream_t s);
+                        float* scores, const GatherJob* pf, int pf_wgs, hipStream_t s,
+                        hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // In-place softmax of each score row over its valid keys; 0 past lens[b].
 hipError_t launch_softmax_rows(float* scores, const int32_t* lens, int B, int H, int Q,

@@ -15,6 +15,8 @@
 // the layer's predicted K/V rows from host memory into its slot (the
 // prefetch), so that the host-link transfer overlaps the HBM-bound scan
 // inside one kernel, with no second stream and no cross-stream wait.
+#include <hip/hip_ext.h>
+
 #include "dd_device.h"
 #include "dd_internal.h"
 #include "gather_body.h"
@@ -159,6 +161,7 @@ struct ScoreLaunch {
   GatherJob pf;
   int pf_wgs;
   hipStream_t s;
+  hipEvent_t ev_start, ev_stop;
 };
 
 template <typename T, int D, int Q>
@@ -169,9 +172,17 @@ hipError_t launch_score_t(const ScoreLaunch& a) {
   if (BH == 0 || (tiles == 0 && a.pf_wgs == 0)) return hipSuccess;
   const int64_t grid = tiles * BH + a.pf_wgs;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), 0, a.s,
-                     a.q, static_cast<const T*>(a.keys), a.lens, BH, a.H, a.n_max, (int)tiles,
-                     a.scale, a.scores, a.fill_pad ? 1 : 0, a.pf, a.pf_wgs);
+  if (a.ev_start != nullptr && a.ev_stop != nullptr) {
+    // Events taken by the dispatch itself: the kernel's own duration.
+    hipExtLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), 0,
+                          a.s, a.ev_start, a.ev_stop, 0, a.q, static_cast<const T*>(a.keys),
+                          a.lens, BH, a.H, a.n_max, (int)tiles, a.scale, a.scores,
+                          a.fill_pad ? 1 : 0, a.pf, a.pf_wgs);
+  } else {
+    hipLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), 0, a.s,
+                       a.q, static_cast<const T*>(a.keys), a.lens, BH, a.H, a.n_max, (int)tiles,
+                       a.scale, a.scores, a.fill_pad ? 1 : 0, a.pf, a.pf_wgs);
+  }
   return hipGetLastError();
 }
 
@@ -185,8 +196,10 @@ hipError_t launch_score_q(int Q, const ScoreLaunch& a) {
 
 hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, int B, int H,
                         int Q, int D, int64_t n_max, int dtype, float scale, bool fill_pad,
-                        float* scores, const GatherJob* pf, int pf_wgs, hipStream_t s) {
-  ScoreLaunch a{q, keys, lens, B, H, n_max, scale, fill_pad, scores, GatherJob{}, 0, s};
+                        float* scores, const GatherJob* pf, int pf_wgs, hipStream_t s,
+                        hipEvent_t ev_start, hipEvent_t ev_stop) {
+  ScoreLaunch a{q, keys, lens, B, H, n_max, scale, fill_pad, scores, GatherJob{}, 0, s,
+                ev_start, ev_stop};
   if (pf != nullptr && pf->total > 0 && pf_wgs > 0) {
     a.pf = *pf;
     a.pf_wgs = (pf_wgs + 7) & ~7;  // keeps the scoring tiles' XCD placement
