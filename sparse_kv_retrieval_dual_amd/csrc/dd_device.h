@@ -114,6 +114,95 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, all in DPP: shifts by
+// 1, 2, 4 and 8 lanes within each row of 16, then the row broadcasts of
+// lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3).  Lanes with
+// no source lane add 0.
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr1, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr2, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr4, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr8, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast15, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast31, 0xC, 0xF, false);
+  return x;
+}
+
+// Two alternating LDS scan buffers of 2 * NW ints each.  A block scan
+// writes the per-wave totals of one buffer, waits at one barrier and reads
+// them back; the next scan uses the other buffer, so a thread still reading
+// this one is never overwritten (any writer of it has passed the next
+// scan's barrier, which this reader has not reached yet).  All threads make
+// the same sequence of scans, so the phase is uniform.
+struct ScanBufs {
+  int* base;  // 4 * NW ints
+  int phase;
+  __device__ __forceinline__ int* next(int nw) {
+    int* p = base + phase * 2 * nw;
+    phase ^= 1;
+    return p;
+  }
+};
+
+// Exclusive prefix sums of a and b over a block of NW waves, with one
+// barrier; also returns both block totals.  All threads must call it.
+template <int NW>
+__device__ __forceinline__ void block_scan_pair(int a, int b, ScanBufs& sb, int& ea, int& eb,
+                                                int& ta, int& tb) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int* buf = sb.next(NW);
+  const int ia = wave_inclusive_scan(a);
+  const int ib = wave_inclusive_scan(b);
+  if (lane == 63) {
+    buf[wave] = ia;
+    buf[NW + wave] = ib;
+  }
+  __syncthreads();
+  int pa = 0, pb = 0, sa = 0, sbt = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int va = buf[w];
+    const int vb = buf[NW + w];
+    pa += (w < wave) ? va : 0;
+    pb += (w < wave) ? vb : 0;
+    sa += va;
+    sbt += vb;
+  }
+  ea = pa + ia - a;
+  eb = pb + ib - b;
+  ta = sa;
+  tb = sbt;
+}
+
+// Exclusive prefix sum of a over a block of NW waves, with one barrier;
+// also returns the block total.  All threads must call it.
+template <int NW>
+__device__ __forceinline__ int block_scan(int a, ScanBufs& sb, int& total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int* buf = sb.next(NW);
+  const int ia = wave_inclusive_scan(a);
+  if (lane == 63) buf[wave] = ia;
+  __syncthreads();
+  int pa = 0, sa = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int va = buf[w];
+    pa += (w < wave) ? va : 0;
+    sa += va;
+  }
+  total = sa;
+  return pa + ia - a;
+}
+
 // Exclusive prefix sum over the block (blockDim.x a multiple of 64, at most
 // 1024 threads).  s_tmp needs 16 ints.  Returns this thread's exclusive sum
 // and the block total; all threads must call it.

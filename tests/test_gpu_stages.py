@@ -101,24 +101,32 @@ TOPK_CASES = [
     ("planted", (2, 2, 1), 20000, [20000, 16384], 40),
     ("planted", (1, 1, 2), 70000, [70000], 39),
     ("normal", (3, 1, 1), 50, [0, 1, 2], 1),
+    # shapes of the split path: several 8192-key segments, ragged and unaligned rows
+    ("normal", (2, 4, 2), 32768, [32768, 20001], 128),
+    ("planted", (1, 2, 2), 65536, [65536], 200),
+    ("normal", (1, 1, 2), 65536, [50000], 256),
+    ("normal", (1, 2, 1), 9999, [9999], 50),
 ]
 
 
 @pytest.mark.parametrize("kind,shape,n_max,lens,k", TOPK_CASES)
 def test_topk_exact(kind, shape, n_max, lens, k):
     """Both sides rank the same fp32 values, so the sets must be identical,
-    including every tie (lower index wins)."""
+    including every tie (lower index wins).  With the workspace, small-k rows
+    take the split path; without it, the one-workgroup path."""
     dd = require_gpu()
-    announce(f"topk {kind} shape={shape} n_max={n_max} lens={lens} k={k}")
     s = _topk_case(kind, shape, n_max, seed=n_max + k)
     lens_t = torch.tensor(lens, dtype=torch.int32)
-    got = dd.topk(s.cuda(), lens_t.cuda(), k).cpu().numpy()
     ref = oracle.select_topk(s.numpy().astype(np.float64), lens_t.numpy(), k)
     B, H, Q = shape
-    for b in range(B):
-        for h in range(H):
-            for j in range(Q):
-                assert np.array_equal(got[b, h, j], ref[b, h, j]), (b, h, j, got[b, h, j][:10], ref[b, h, j][:10])
+    for ws in ("auto", None):
+        announce(f"topk {kind} shape={shape} n_max={n_max} lens={lens} k={k} ws={ws}")
+        got = dd.topk(s.cuda(), lens_t.cuda(), k, ws=ws).cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                for j in range(Q):
+                    assert np.array_equal(got[b, h, j], ref[b, h, j]), (
+                        ws, b, h, j, got[b, h, j][:10], ref[b, h, j][:10])
 
 
 # --------------------------------------------------------------------------- gather
