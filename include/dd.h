@@ -106,10 +106,6 @@ DD_API int dd_score(const float* q, const void* keys, const int32_t* lens, int B
                     int Q, int D, int64_t n_max, int kv_dtype, float scale, int kind,
                     float* scores, hipStream_t stream);
 
-/* Bytes of the optional dd_topk workspace for these sizes (0 when no
- * workspace is used for them, and for invalid sizes). */
-DD_API size_t dd_topk_workspace(int B, int H, int Q, int64_t n_max, int k);
-
 /* Selection I = argtopk(alpha, k) (paper-daily summary, core-formulas
  * section; Figure 1 "Top-k" on the arXiv page).  Softmax is increasing, so
  * selecting on logits gives the same set.
@@ -119,15 +115,9 @@ DD_API size_t dd_topk_workspace(int B, int H, int Q, int64_t n_max, int k);
  *           order.  Ties go to the lower index; -0.0 equals +0.0.  When
  *           lens[b] < k, the first lens[b] slots hold 0..lens[b]-1 and the
  *           rest hold -1.
- *   ws      NULL, or device scratch of at least dd_topk_workspace(...)
- *           bytes, 16-byte aligned (DD_ERR_WORKSPACE when smaller).  With
- *           it, rows of small k are split over several workgroups; the
- *           result is the same either way.  The contents need no
- *           initialisation and are overwritten.
  */
 DD_API int dd_topk(const float* scores, const int32_t* lens, int B, int H, int Q,
-                   int64_t n_max, int k, int32_t* idx, void* ws, size_t ws_bytes,
-                   hipStream_t stream);
+                   int64_t n_max, int k, int32_t* idx, hipStream_t stream);
 
 /* Gather of selected rows from the host KV cache into device memory
  * (arXiv page, section 2.2 and Figure 1, "Sparse KV" / "Gather"; the

@@ -57,8 +57,7 @@ _SIGNATURES = {
     "dd_host_alloc": (c_int, [c_size_t, ctypes.POINTER(c_void_p)]),
     "dd_host_free": (c_int, [P]),
     "dd_score": (c_int, [P, P, P, c_int, c_int, c_int, c_int, c_int64, c_int, c_float, c_int, P, P]),
-    "dd_topk_workspace": (c_size_t, [c_int, c_int, c_int, c_int64, c_int]),
-    "dd_topk": (c_int, [P, P, c_int, c_int, c_int, c_int64, c_int, P, P, c_size_t, P]),
+    "dd_topk": (c_int, [P, P, c_int, c_int, c_int, c_int64, c_int, P, P]),
     "dd_gather": (c_int, [P, P, P, P, c_int, c_int, c_int, c_int, c_int64, c_int, P, P, P]),
     "dd_attn_workspace": (c_size_t, [c_int, c_int, c_int, c_int]),
     "dd_sparse_attn": (c_int, [P, c_int64, P, P, P, P, c_int, c_int, c_int, c_int, c_int, c_int,

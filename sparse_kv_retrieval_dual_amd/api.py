@@ -86,16 +86,8 @@ def score(q, keys, lens, kind: str = "logits", scale: float = 0.0, out=None, str
     return out
 
 
-def topk_workspace_bytes(B: int, H: int, Q: int, n_max: int, k: int) -> int:
-    return int(_lib().dd_topk_workspace(B, H, Q, n_max, k))
-
-
-def topk(scores, lens, k: int, out=None, ws="auto", stream=None):
-    """dd_topk.  scores fp32 [B][H][Q][n_max] -> int32 [B][H][Q][k], ascending, -1 padded.
-
-    ws: "auto" allocates the workspace dd_topk_workspace asks for, None runs
-    without one, or a device uint8 tensor is used as given.
-    """
+def topk(scores, lens, k: int, out=None, stream=None):
+    """dd_topk.  scores fp32 [B][H][Q][n_max] -> int32 [B][H][Q][k], ascending, -1 padded."""
     _dev(scores, "scores"), _dev(lens, "lens")
     _need(scores.dtype == torch.float32 and scores.dim() == 4, "scores must be fp32 [B][H][Q][n_max]")
     B, H, Q, n_max = scores.shape
@@ -104,15 +96,7 @@ def topk(scores, lens, k: int, out=None, ws="auto", stream=None):
         out = torch.empty(B, H, Q, k, dtype=torch.int32, device=scores.device)
     _dev(out, "out")
     _need(out.shape == (B, H, Q, k) and out.dtype == torch.int32, "out must be int32 [B][H][Q][k]")
-    if isinstance(ws, str):
-        _need(ws == "auto", "ws must be 'auto', None or a device tensor")
-        nb = topk_workspace_bytes(B, H, Q, n_max, k)
-        ws = torch.empty(nb, dtype=torch.uint8, device=scores.device) if nb > 0 else None
-    if ws is not None:
-        _dev(ws, "ws")
-    L.check(_lib().dd_topk(_p(scores), _p(lens), B, H, Q, n_max, int(k), _p(out),
-                           None if ws is None else _p(ws),
-                           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    L.check(_lib().dd_topk(_p(scores), _p(lens), B, H, Q, n_max, int(k), _p(out), _stream(stream)))
     return out
 
 

@@ -74,7 +74,7 @@ int check_k(int k) {
 
 // Workspace of the layer step, carved in this order.
 struct StepLayout {
-  size_t scores, pos, miss, counts, attn, topk, total;
+  size_t scores, pos, miss, counts, attn, total;
 };
 
 StepLayout step_layout(int B, int H, int D, int64_t n_max, int k) {
@@ -91,8 +91,6 @@ StepLayout step_layout(int B, int H, int D, int64_t n_max, int k) {
   off += align_up(3 * BH * sizeof(int32_t));
   l.attn = off;
   off += align_up(dd::attn_workspace(B, H, k, D));
-  l.topk = off;
-  off += align_up(dd::topk_scratch_bytes(B, H, 2, n_max, k));
   l.total = off;
   return l;
 }
@@ -154,13 +152,8 @@ DD_API int dd_score(const float* q, const void* keys, const int32_t* lens, int B
   return DD_OK;
 }
 
-DD_API size_t dd_topk_workspace(int B, int H, int Q, int64_t n_max, int k) {
-  if (B <= 0 || H <= 0 || (Q != 1 && Q != 2) || k < 1 || k > DD_MAX_K || n_max <= 0) return 0;
-  return dd::topk_scratch_bytes(B, H, Q, n_max, k);
-}
-
 DD_API int dd_topk(const float* scores, const int32_t* lens, int B, int H, int Q, int64_t n_max,
-                   int k, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+                   int k, int32_t* idx, hipStream_t stream) {
   int rc = check_shape(B, H, 64, n_max, DD_F32);
   if (rc) return rc;
   rc = check_k(k);
@@ -168,13 +161,8 @@ DD_API int dd_topk(const float* scores, const int32_t* lens, int B, int H, int Q
   if (Q != 1 && Q != 2) return fail(DD_ERR_UNSUPPORTED, "Q must be 1 or 2 (got %d)", Q);
   if ((int64_t)B * H == 0) return DD_OK;
   if (!lens || !idx || (!scores && n_max > 0)) return fail(DD_ERR_INVALID_ARG, "null pointer argument");
-  const size_t need = dd::topk_scratch_bytes(B, H, Q, n_max, k);
-  if (ws != nullptr && ws_bytes < need)
-    return fail(DD_ERR_WORKSPACE, "top-k workspace too small: %zu < %zu bytes", ws_bytes, need);
-  if (ws != nullptr && !aligned16(ws)) return fail(DD_ERR_INVALID_ARG, "ws must be 16-byte aligned");
-  const dd::TopkScratch ts = dd::topk_scratch(need > 0 ? ws : nullptr, B, H, Q, n_max);
   hipError_t e = dd::launch_topk(scores, lens, B, H, Q, n_max, k, idx, idx + k, (int64_t)Q * k,
-                                 nullptr, &ts, stream);
+                                 nullptr, stream);
   if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
   return DD_OK;
 }
@@ -343,8 +331,6 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
   int32_t* miss = reinterpret_cast<int32_t*>(ws + lay.miss);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + lay.counts);
   void* attn_ws = ws + lay.attn;
-  const dd::TopkScratch topk_ts =
-      dd::topk_scratch(lay.topk < lay.total ? ws + lay.topk : nullptr, B, H, 2, a->n_max);
   const int R = c->ring_slots;
   hipStream_t caller = a->stream;
   hipStream_t ms = c->main_own ? c->main_own : caller;
@@ -401,7 +387,7 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     if (tev(l, 1) && !score_ev) DD_CHECK_HIP(hipEventRecord(tev(l, 1), ms), "timing");
     const dd::TopkBook book{P, pos, miss, counts};
     e = dd::launch_topk(scores, a->lens, B, H, 2, a->n_max, k, a->cur_idx[l], a->spec_idx[l], k,
-                        &book, &topk_ts, ms);
+                        &book, ms);
     if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
     if (tev(l, 2)) DD_CHECK_HIP(hipEventRecord(tev(l, 2), ms), "timing");
     if (P && use_side) DD_CHECK_HIP(hipStreamWaitEvent(ms, c->ev_gathered[slot], 0), "main waits prefetch");

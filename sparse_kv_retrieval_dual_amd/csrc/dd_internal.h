@@ -47,26 +47,11 @@ struct TopkBook {
   int32_t* counts;      // [3][BH]: misses, hits, fetchable prediction entries
 };
 
-// Device scratch of the split top-k (candidates handed from the segment
-// workgroups of a row to the row's workgroup).
-struct TopkScratch {
-  uint32_t* ckey;
-  int32_t* cidx;
-  int32_t* ccnt;
-};
-
-// Bytes of that scratch for these sizes (0 when the split path does not
-// apply), and its layout in a buffer of at least that many bytes.
-size_t topk_scratch_bytes(int B, int H, int Q, int64_t n_max, int k);
-TopkScratch topk_scratch(void* ws, int B, int H, int Q, int64_t n_max);
-
 // Top-k of each score row.  Plane j of slab bh is written at
-// (j == 0 ? out0 : out1) + bh * out_stride_bh.  scratch (or null) enables
-// the split path where it applies.
+// (j == 0 ? out0 : out1) + bh * out_stride_bh.
 hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, int Q,
                        int64_t n_max, int k, int32_t* out0, int32_t* out1,
-                       int64_t out_stride_bh, const TopkBook* book, const TopkScratch* scratch,
-                       hipStream_t s);
+                       int64_t out_stride_bh, const TopkBook* book, hipStream_t s);
 
 // Row gather from pinned host memory.  Entry j < cnt[bh] (m if cnt is null)
 // of slab bh copies host row idx[bh*m + j] (zero row if out of range) to

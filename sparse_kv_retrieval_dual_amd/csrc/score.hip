@@ -87,12 +87,14 @@ __global__ __launch_bounds__(kScoreWaves * 64) void k_score(
     // Rows past n load row n-1 instead (n >= 1 here): the loads stay
     // unconditional so all U of them are in flight together, and the
     // butterfly never mixes rows, so those lanes' scores are simply not stored.
+    // The keys are read once: non-temporal loads keep them from evicting
+    // the scores (and prefetched rows) that the next kernels read from L2.
     u32x4 raw[S::U];
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
       const int64_t row = key0 + u * S::RPI + rsub;
       const int64_t rr = row < n ? row : n - 1;
-      raw[u] = *reinterpret_cast<const u32x4*>(kb + rr * D);
+      raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + rr * D));
     }
     float acc[S::U * Q];
 #pragma unroll

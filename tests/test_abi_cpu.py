@@ -47,14 +47,6 @@ def test_buffer_sizes(lib):
     ws = lib.dd_layer_step_workspace(1, 32, 128, 32768, 128)
     assert ws >= 32 * 2 * 32768 * 4 + 2 * 32 * 128 * 4
     assert ws % 256 == 0
-    # top-k workspace: candidate (key, index) slots of every 8192-key segment
-    # of every row for small k, none otherwise
-    tk = lib.dd_topk_workspace(1, 32, 2, 32768, 128)
-    assert tk >= 64 * 4 * 2048 * 8
-    assert ws >= 32 * 2 * 32768 * 4 + tk
-    assert lib.dd_topk_workspace(1, 32, 2, 32768, 1024) == 0
-    assert lib.dd_topk_workspace(1, 32, 2, 1 << 20, 128) == 0
-    assert lib.dd_topk_workspace(0, 32, 2, 32768, 128) == 0
 
 
 @pytest.mark.parametrize("call,code", [
@@ -70,9 +62,9 @@ def test_argument_errors_are_reported(lib, call, code):
     elif call == "score_bad_dtype":
         rc = lib.dd_score(z, z, z, 1, 1, 2, 128, 10, 7, 0.0, 0, z, None)
     elif call == "topk_k0":
-        rc = lib.dd_topk(z, z, 1, 1, 1, 10, 0, z, None, 0, None)
+        rc = lib.dd_topk(z, z, 1, 1, 1, 10, 0, z, None)
     elif call == "topk_k_too_big":
-        rc = lib.dd_topk(z, z, 1, 1, 1, 10, 4097, z, None, 0, None)
+        rc = lib.dd_topk(z, z, 1, 1, 1, 10, 4097, z, None)
     elif call == "gather_null_idx":
         rc = lib.dd_gather(z, z, None, None, 1, 1, 4, 128, 10, 1, z, z, None)
     elif call == "gather_neg_m":
@@ -86,5 +78,5 @@ def test_argument_errors_are_reported(lib, call, code):
 def test_empty_shapes_are_no_ops(lib):
     z = ctypes.c_void_p(16)
     assert lib.dd_score(z, z, z, 0, 8, 2, 128, 10, 1, 0.0, 0, z, None) == 0
-    assert lib.dd_topk(z, z, 1, 0, 2, 10, 4, z, None, 0, None) == 0
+    assert lib.dd_topk(z, z, 1, 0, 2, 10, 4, z, None) == 0
     assert lib.dd_gather(z, z, z, None, 1, 1, 0, 128, 10, 1, z, z, None) == 0

@@ -112,21 +112,19 @@ TOPK_CASES = [
 @pytest.mark.parametrize("kind,shape,n_max,lens,k", TOPK_CASES)
 def test_topk_exact(kind, shape, n_max, lens, k):
     """Both sides rank the same fp32 values, so the sets must be identical,
-    including every tie (lower index wins).  With the workspace, small-k rows
-    take the split path; without it, the one-workgroup path."""
+    including every tie (lower index wins)."""
     dd = require_gpu()
+    announce(f"topk {kind} shape={shape} n_max={n_max} lens={lens} k={k}")
     s = _topk_case(kind, shape, n_max, seed=n_max + k)
     lens_t = torch.tensor(lens, dtype=torch.int32)
     ref = oracle.select_topk(s.numpy().astype(np.float64), lens_t.numpy(), k)
+    got = dd.topk(s.cuda(), lens_t.cuda(), k).cpu().numpy()
     B, H, Q = shape
-    for ws in ("auto", None):
-        announce(f"topk {kind} shape={shape} n_max={n_max} lens={lens} k={k} ws={ws}")
-        got = dd.topk(s.cuda(), lens_t.cuda(), k, ws=ws).cpu().numpy()
-        for b in range(B):
-            for h in range(H):
-                for j in range(Q):
-                    assert np.array_equal(got[b, h, j], ref[b, h, j]), (
-                        ws, b, h, j, got[b, h, j][:10], ref[b, h, j][:10])
+    for b in range(B):
+        for h in range(H):
+            for j in range(Q):
+                assert np.array_equal(got[b, h, j], ref[b, h, j]), (
+                    b, h, j, got[b, h, j][:10], ref[b, h, j][:10])
 
 
 # --------------------------------------------------------------------------- gather
