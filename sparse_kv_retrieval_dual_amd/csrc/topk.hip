@@ -78,6 +78,7 @@ __device__ __forceinline__ void clear(uint32_t* p, int words) {
 // Lowest `take` set bits of w (take <= popcount(w)).
 __device__ __forceinline__ uint32_t lowest_bits(uint32_t w, int take) {
   uint32_t r = 0u;
+#pragma unroll 1
   for (int q = 0; q < take; ++q) {
     const uint32_t low = w & (0u - w);
     r |= low;
@@ -89,6 +90,7 @@ __device__ __forceinline__ uint32_t lowest_bits(uint32_t w, int take) {
 // Position of c in the ascending list s[0, len), or -1.
 __device__ __forceinline__ int find_in(const int32_t* s, int len, int c) {
   int lo = 0, hi = len;
+#pragma unroll 1
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     if (s[mid] < c) lo = mid + 1;
@@ -161,7 +163,7 @@ __device__ __forceinline__ void select_kth(const uint32_t* fkey, int cnt, int k,
   for (int r = 0; r < R; ++r) x[r] = tid + kNT * r < cnt ? fkey[tid + kNT * r] : 0u;
   uint32_t prefix = 0u, pmask = 0u;
   int kr = k;
-#pragma unroll
+#pragma unroll 1
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     uint32_t* h = h4 + 256 * pass;
@@ -212,13 +214,14 @@ struct Sink {
 // bitmap words w0, w0 + 1, ...: g (the "> T" set, extended here by the
 // taken "== T" bits of e).  gt_before / eq_before: the counts in lower
 // words; misses are numbered from miss_base.  Returns this block's misses.
-__device__ __forceinline__ int emit_words(uint32_t (&g)[kMaxWords], const uint32_t (&e)[kMaxWords],
-                                          int w0, int gt_before, int eq_before, int take_eq,
-                                          int k, const Sink& sk, ScanBufs& sb, int miss_base) {
+template <int MAXW>
+__device__ __forceinline__ int emit_words(uint32_t (&g)[MAXW], const uint32_t (&e)[MAXW], int w0,
+                                          int gt_before, int eq_before, int take_eq, int k,
+                                          const Sink& sk, ScanBufs& sb, int miss_base) {
   int take = take_eq - eq_before;
   const int j0 = gt_before + (eq_before < take_eq ? eq_before : take_eq);
 #pragma unroll
-  for (int w = 0; w < kMaxWords; ++w) {
+  for (int w = 0; w < MAXW; ++w) {
     const int pe = __popc(e[w]);
     const int tw = take < 0 ? 0 : (take > pe ? pe : take);
     g[w] |= lowest_bits(e[w], tw);
@@ -227,7 +230,8 @@ __device__ __forceinline__ int emit_words(uint32_t (&g)[kMaxWords], const uint32
   int j = j0;
   if (sk.s_pred == nullptr) {
 #pragma unroll
-    for (int w = 0; w < kMaxWords; ++w) {
+    for (int w = 0; w < MAXW; ++w) {
+#pragma unroll 1
       for (uint32_t x = g[w]; x != 0u; x &= x - 1u) {
         if (j < k) sk.out[j] = (w0 + w) * 32 + __ffs(x) - 1;
         ++j;
@@ -237,11 +241,12 @@ __device__ __forceinline__ int emit_words(uint32_t (&g)[kMaxWords], const uint32
   }
   // Each selected entry is looked up once: hits get their prediction row
   // now, misses are marked and get slot rows after the scan of miss counts.
-  uint32_t mm[kMaxWords];
+  uint32_t mm[MAXW];
   int my_miss = 0;
 #pragma unroll
-  for (int w = 0; w < kMaxWords; ++w) {
+  for (int w = 0; w < MAXW; ++w) {
     mm[w] = 0u;
+#pragma unroll 1
     for (uint32_t x = g[w]; x != 0u; x &= x - 1u) {
       const int b = __ffs(x) - 1;
       const int c = (w0 + w) * 32 + b;
@@ -262,7 +267,8 @@ __device__ __forceinline__ int emit_words(uint32_t (&g)[kMaxWords], const uint32
   int mr = miss_base + block_scan<kNW>(my_miss, sb, mtot);
   int jb = j0;  // output position of word w's first selected entry
 #pragma unroll
-  for (int w = 0; w < kMaxWords; ++w) {
+  for (int w = 0; w < MAXW; ++w) {
+#pragma unroll 1
     for (uint32_t x = mm[w]; x != 0u; x &= x - 1u) {
       const int b = __ffs(x) - 1;
       sk.pos[jb + __popc(g[w] & ((1u << b) - 1u))] = k + mr;
@@ -278,15 +284,16 @@ __device__ __forceinline__ int emit_words(uint32_t (&g)[kMaxWords], const uint32
 // row of nw words; thread t owns words [t W, t W + W).  pf / pn: this
 // thread's count of fetchable / non-negative prediction entries.  Returns
 // the misses; sets fetchable and sk.plen from the block totals.
+template <int MAXW>
 __device__ __forceinline__ int emit_bitmaps(const uint32_t* gt, const uint32_t* eq, int nw,
                                             int take_eq, int k, Sink& sk, int pf, int pn,
                                             ScanBufs& sb, int& fetchable) {
   const int W = (nw + kNT - 1) / kNT;
   const int w0 = (int)threadIdx.x * W;
-  uint32_t g[kMaxWords], e[kMaxWords];
+  uint32_t g[MAXW], e[MAXW];
   int gc = 0, ec = 0;
 #pragma unroll
-  for (int w = 0; w < kMaxWords; ++w) {
+  for (int w = 0; w < MAXW; ++w) {
     const bool in = w < W && w0 + w < nw;
     g[w] = in ? gt[w0 + w] : 0u;
     e[w] = in ? eq[w0 + w] : 0u;
@@ -299,7 +306,7 @@ __device__ __forceinline__ int emit_bitmaps(const uint32_t* gt, const uint32_t* 
   block_scan_pair<kNW>(gc | (ec << 16), pf | (pn << 16), sb, ex, ep, tx, tp);
   fetchable = tp & 0xFFFF;
   if (sk.s_pred != nullptr) sk.plen = tp >> 16;
-  return emit_words(g, e, w0, ex & 0xFFFF, ex >> 16, take_eq, k, sk, sb, 0);
+  return emit_words<MAXW>(g, e, w0, ex & 0xFFFF, ex >> 16, take_eq, k, sk, sb, 0);
 }
 
 // Stores this thread's prediction entries in s_pred; counts the fetchable
@@ -427,14 +434,17 @@ __device__ bool filter_select(const float* __restrict__ row, int n, int64_t n_ma
     for (int u = 0; u < kU; ++u)
       um |= (4 * (tid + kNT * u) < n && f4max[u] >= fb) ? (1u << u) : 0u;
     int my = 0;
+#pragma unroll 1
     for (uint32_t x = um; x != 0u; x &= x - 1u) {
       const int q = tid + kNT * (__ffs(x) - 1);
       my += __popc(passing(reinterpret_cast<const f32x4*>(regc)[q], 4 * q, n, fb));
     }
     int off = block_scan<kNW>(my, sb, cnt);
     if (cnt > CAP) return false;
+#pragma unroll 1
     for (uint32_t x = um; x != 0u; x &= x - 1u) {
       const int q = tid + kNT * (__ffs(x) - 1);
+#pragma unroll 1
       for (uint32_t m = passing(reinterpret_cast<const f32x4*>(regc)[q], 4 * q, n, fb); m != 0u;
            m &= m - 1u)
         fidx[off++] = 4 * q + __ffs(m) - 1;
@@ -461,6 +471,7 @@ __device__ bool filter_select(const float* __restrict__ row, int n, int64_t n_ma
       if (cnt + tot > CAP) return false;
 #pragma unroll
       for (int w = 0; w < kU / 8; ++w) {
+#pragma unroll 1
         for (uint32_t m = mk[w]; m != 0u; m &= m - 1u) {
           const int b = __ffs(m) - 1;
           const int u = 8 * w + (b >> 2);
@@ -495,7 +506,9 @@ __device__ bool filter_select(const float* __restrict__ row, int n, int64_t n_ma
     else if (x == thr) atomicOr(&eq[c >> 5], 1u << (c & 31));
   }
   __syncthreads();
-  misses = emit_bitmaps(gt, eq, nw, take_eq, k, sk, pf, pn, sb, fetchable);
+  // A cached row has at most kTile / 32 bitmap words: 4 per thread.
+  misses = emit_bitmaps<CACHED ? kTile / 32 / kNT : kMaxWords>(gt, eq, nw, take_eq, k, sk, pf, pn,
+                                                                  sb, fetchable);
   return true;
 }
 
@@ -563,9 +576,7 @@ __device__ int radix_select(const float* __restrict__ row, int n, int64_t n_max,
   int out_run = 0, eq_run = 0, miss_run = 0;
   for (int seg0 = 0; seg0 < n; seg0 += kSegKeys) {
     const int base = seg0 + 32 * tid;
-    uint32_t g[kMaxWords], e[kMaxWords];
-#pragma unroll
-    for (int w = 0; w < kMaxWords; ++w) g[w] = e[w] = 0u;
+    uint32_t g[1] = {0u}, e[1] = {0u};
     if (base < n) {
 #pragma unroll
       for (int b = 0; b < 32; ++b) {
@@ -583,8 +594,8 @@ __device__ int radix_select(const float* __restrict__ row, int n, int64_t n_max,
       if (sk.s_pred != nullptr) sk.plen = tp >> 16;
     }
     // Per-segment counts stay below 2^16 (8192 keys).
-    const int mtot = emit_words(g, e, base / 32, out_run + (ex & 0xFFFF), eq_run + (ex >> 16),
-                                kr, k, sk, sb, miss_run);
+    const int mtot = emit_words<1>(g, e, base / 32, out_run + (ex & 0xFFFF),
+                                   eq_run + (ex >> 16), kr, k, sk, sb, miss_run);
     out_run += tx & 0xFFFF;
     eq_run += tx >> 16;
     miss_run += mtot;
