@@ -227,11 +227,9 @@ def main():
     def avg(a, b):
         return float(np.mean([stage.elapsed_ms(i * E + a, i * E + b) for i in range(K)]))
 
-    t_topk = avg(1, 2)
-    t_wait = avg(2, 3)
-    t_attn = avg(3, 4)
-    # Events 5 and 6 are recorded only when the prediction is fetched on the
-    # side stream (the default for a single layer is the fused fetch).
+    # Events 2-4 all follow the kernel that selects, does the bookkeeping and
+    # attends; 5 and 6 bracket a side-stream prefetch (when there is one).
+    t_select_attn = avg(1, 4)
     t_prefetch = avg(5, 6) if args.prefetch == "side" else None
     t_step_instr = avg(0, 4)
     st = stats[0].cpu().tolist()
@@ -305,8 +303,7 @@ def main():
         "eager_layer_step_us": eager_ms * 1e3,
         "graph_note": graph_note,
         "stages_us": {"score": t_score * 1e3,
-                      "topk_bookkeeping": t_topk * 1e3,
-                      "wait_for_prefetch": t_wait * 1e3, "attention": t_attn * 1e3,
+                      "select_bookkeeping_attention": t_select_attn * 1e3,
                       "prefetch_side_stream": None if t_prefetch is None else t_prefetch * 1e3,
                       "instrumented_step": t_step_instr * 1e3},
         "score_keys_per_s": n_keys / (t_score * 1e-3),

@@ -66,12 +66,12 @@ enum { DD_LOGITS = 0, DD_ALPHA = 1 };  /* what dd_score writes */
 #define DD_MAX_K 4096
 /* Events per layer recorded by dd_layer_step when args.timing is set (an
  * entry may be NULL to skip it): [0] start and [1] end of the scoring
- * kernel (taken by that dispatch itself when both are given), [2] after
- * top-k and bookkeeping, [3] after the wait for a side-stream prefetch,
- * [4] after attention (which also fetches the misses) -- all on the main
- * stream -- and [5] before and [6] after the prefetch gather on the side
- * stream (left unrecorded when the prediction is fetched inside the
- * scoring kernel or the layer has none). */
+ * kernel (taken by that dispatch itself when both are given); [2], [3] and
+ * [4] all after the kernel that selects, does the bookkeeping, fetches the
+ * misses and attends (a wait for a side-stream prefetch comes before it) --
+ * all on the main stream -- and [5] before and [6] after the prefetch
+ * gather on the side stream (left unrecorded when the prediction is fetched
+ * inside the scoring kernel or the layer has none). */
 #define DD_STAGE_EVENTS 7
 
 /* Text of the last non-OK status returned on this thread ("" if none). */
@@ -203,8 +203,8 @@ DD_API int dd_ctx_destroy(dd_ctx* ctx);
  * [k, 2k) the misses. */
 DD_API size_t dd_ring_bytes(int ring_slots, int B, int H, int D, int k, int dtype);
 
-/* Workspace bytes of dd_layer_step (scores of one layer, bookkeeping and
- * attention partials; reused layer after layer). */
+/* Workspace bytes of dd_layer_step (the scores of one layer, reused layer
+ * after layer). */
 DD_API size_t dd_layer_step_workspace(int B, int H, int D, int64_t n_max, int k);
 
 typedef struct dd_layer_step_args {

@@ -74,7 +74,7 @@ int check_k(int k) {
 
 // Workspace of the layer step, carved in this order.
 struct StepLayout {
-  size_t scores, pos, miss, counts, attn, total;
+  size_t scores, total;
 };
 
 StepLayout step_layout(int B, int H, int D, int64_t n_max, int k) {
@@ -83,15 +83,9 @@ StepLayout step_layout(int B, int H, int D, int64_t n_max, int k) {
   size_t off = 0;
   l.scores = off;
   off += align_up(BH * 2 * (size_t)n_max * sizeof(float));
-  l.pos = off;
-  off += align_up(BH * k * sizeof(int32_t));
-  l.miss = off;
-  off += align_up(BH * k * sizeof(int32_t));
-  l.counts = off;
-  off += align_up(3 * BH * sizeof(int32_t));
-  l.attn = off;
-  off += align_up(dd::attn_workspace(B, H, k, D));
   l.total = off;
+  (void)D;
+  (void)k;
   return l;
 }
 
@@ -162,7 +156,7 @@ DD_API int dd_topk(const float* scores, const int32_t* lens, int B, int H, int Q
   if ((int64_t)B * H == 0) return DD_OK;
   if (!lens || !idx || (!scores && n_max > 0)) return fail(DD_ERR_INVALID_ARG, "null pointer argument");
   hipError_t e = dd::launch_topk(scores, lens, B, H, Q, n_max, k, idx, idx + k, (int64_t)Q * k,
-                                 nullptr, stream);
+                                 nullptr, nullptr, stream);
   if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
   return DD_OK;
 }
@@ -327,10 +321,6 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
   const int rowb = D * dd::elem_bytes(a->dtype);
   char* ws = static_cast<char*>(a->ws);
   float* scores = reinterpret_cast<float*>(ws + lay.scores);
-  int32_t* pos = reinterpret_cast<int32_t*>(ws + lay.pos);
-  int32_t* miss = reinterpret_cast<int32_t*>(ws + lay.miss);
-  int32_t* counts = reinterpret_cast<int32_t*>(ws + lay.counts);
-  void* attn_ws = ws + lay.attn;
   const int R = c->ring_slots;
   hipStream_t caller = a->stream;
   hipStream_t ms = c->main_own ? c->main_own : caller;
@@ -376,30 +366,30 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     }
 
     // Events 0 and 1 are taken by the scoring dispatch itself (its start and
-    // end), so they time exactly that kernel.
+    // end), so they time exactly that kernel.  The scoring kernel also zeroes
+    // the layer's statistics, which the next kernel adds to.
+    int64_t* st = a->stats ? a->stats + 3 * (size_t)l : nullptr;
     const bool score_ev = tev(l, 0) && tev(l, 1);
     if (tev(l, 0) && !score_ev) DD_CHECK_HIP(hipEventRecord(tev(l, 0), ms), "timing");
     hipError_t e = dd::launch_score(a->q[l], a->k_dev[l], a->lens, B, H, 2, D, a->n_max, a->dtype,
                                     sc, false, scores, (P && fused) ? &pf : nullptr,
                                     c->prefetch_wgs, ms, score_ev ? tev(l, 0) : nullptr,
-                                    score_ev ? tev(l, 1) : nullptr);
+                                    score_ev ? tev(l, 1) : nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "score kernel launch");
     if (tev(l, 1) && !score_ev) DD_CHECK_HIP(hipEventRecord(tev(l, 1), ms), "timing");
-    const dd::TopkBook book{P, pos, miss, counts};
-    e = dd::launch_topk(scores, a->lens, B, H, 2, a->n_max, k, a->cur_idx[l], a->spec_idx[l], k,
-                        &book, ms);
-    if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
-    if (tev(l, 2)) DD_CHECK_HIP(hipEventRecord(tev(l, 2), ms), "timing");
     if (P && use_side) DD_CHECK_HIP(hipStreamWaitEvent(ms, c->ev_gathered[slot], 0), "main waits prefetch");
-    if (tev(l, 3)) DD_CHECK_HIP(hipEventRecord(tev(l, 3), ms), "timing");
-    // Misses are read from host memory by the attention kernel itself (and
-    // stored into their slot rows k + t), overlapping the slot reads.
-    const dd::AttnMiss am{a->k_host[l], a->v_host[l], a->cur_idx[l], a->n_max, k};
-    e = dd::launch_attn(a->q[l], 2 * (int64_t)D, kslot, vslot, pos, nullptr, B, H, k, 2 * k, D,
-                        a->dtype, sc, a->out[l], a->lse ? a->lse[l] : nullptr, attn_ws, counts,
-                        a->stats ? a->stats + 3 * (size_t)l : nullptr, &am, ms);
-    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-    if (tev(l, 4)) DD_CHECK_HIP(hipEventRecord(tev(l, 4), ms), "timing");
+    // Top-k of both queries, the bookkeeping of the current one and its
+    // attention in one kernel: each current-query row's workgroup attends
+    // right after its selection, reading misses from host memory itself
+    // (and storing them into their slot rows k + t).
+    const dd::TopkBook book{P, nullptr, nullptr, nullptr};
+    const dd::FusedAttn fa{a->q[l], kslot, vslot, a->k_host[l], a->v_host[l], D, a->dtype, sc,
+                           a->out[l], a->lse ? a->lse[l] : nullptr, st};
+    e = dd::launch_topk(scores, a->lens, B, H, 2, a->n_max, k, a->cur_idx[l], a->spec_idx[l], k,
+                        &book, &fa, ms);
+    if (e != hipSuccess) return hip_fail(e, "top-k and attention kernel launch");
+    for (int ev = 2; ev <= 4; ++ev)
+      if (tev(l, ev)) DD_CHECK_HIP(hipEventRecord(tev(l, ev), ms), "timing");
     if (use_side) DD_CHECK_HIP(hipEventRecord(c->ev_free[slot], ms), "record slot free");
   }
   if (ms != caller) {

@@ -1,0 +1,230 @@
+// One chunk of sparse decode attention for one (b, h), shared by the
+// attention kernel and the layer step's fused top-k + attention kernel.
+//
+// A 256-thread workgroup handles up to 128 entries; each wave owns 32.  A
+// row is read by LPR lanes, 16 B each; every lane issues its K and V loads
+// for all of its entries at once (one memory round trip), the dot products
+// are summed across the LPR lanes by a DPP butterfly that leaves every lane
+// with all of its entries' logits, and the wave forms its own max, weights
+// and weighted V sum without a workgroup barrier.  The four waves are
+// merged in LDS by log-sum-exp in a fixed order.  Every reduction runs in
+// the order of the entry number j, never of the row it is stored in, so the
+// result does not depend on where rows sit.
+#pragma once
+
+#include "dd_device.h"
+
+namespace dd {
+
+constexpr int kAttnThreads = 256;
+constexpr int kAttnWaves = kAttnThreads / 64;
+constexpr int kWaveEntries = 32;
+constexpr int kAttnChunk = kAttnWaves * kWaveEntries;
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T, int D>
+struct AttnShape {
+  static constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane per load
+  static constexpr int LPR = D / EPL;              // lanes per row
+  static constexpr int RPI = 64 / LPR;             // rows per wave load instruction
+  static constexpr int U = kWaveEntries / RPI;     // entries (K and V loads) per lane
+  static_assert(U >= 1 && U * RPI == kWaveEntries, "shape");
+};
+
+// All-reduce of NV values over aligned groups of G lanes.
+template <int G, int NV>
+__device__ __forceinline__ void group_allreduce(float* x) {
+  if constexpr (G > 1) {
+    constexpr int HALF = G / 2;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) x[v] += partner<HALF>(x[v]);
+    group_allreduce<HALF, NV>(x);
+  }
+}
+
+// The rows of one (b, h): slot rows kb / vb ([m][D]), and for entries whose
+// slot row is >= first_miss_row the host rows khb / vhb ([n_max][D]) they
+// are read from (and copied into their slot row); khb null: no host rows.
+template <typename T>
+struct AttnRows {
+  const T* kb;
+  const T* vb;
+  const T* khb;
+  const T* vhb;
+  int m;
+  int first_miss_row;
+  int64_t n_max;
+};
+
+// LDS of one chunk merge: per-wave max, weight sum and weighted V.
+template <int D>
+struct AttnLds {
+  float m[kAttnWaves];
+  float l[kAttnWaves];
+  float o[kAttnWaves][D];
+};
+
+// Entries c0 .. c0 + 127 (those < lim) of query q (D floats).  entry(j, r,
+// c) gives entry j's slot row r (-1: skipped) and host row c.  Afterwards
+// cm and cl (all threads) are the chunk's max logit and weight sum, and
+// threads d < D hold od = the chunk's weighted V sum of column d.  The
+// caller must not touch lds until a barrier after this returns.
+template <typename T, int D, class Entry>
+__device__ __forceinline__ void attend_chunk(const float* __restrict__ q, const AttnRows<T>& R,
+                                             int c0, int lim, float scale, Entry entry,
+                                             AttnLds<D>& lds, float& cm, float& cl, float& od) {
+  using S = AttnShape<T, D>;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane % S::LPR;
+  const int rsub = lane / S::LPR;
+  const int e0 = c0 + wave * kWaveEntries;  // this wave's first entry
+  const bool from_host = R.khb != nullptr;
+  int rows[S::U];
+  int hrow[S::U];
+#pragma unroll
+  for (int u = 0; u < S::U; ++u) {
+    const int j = e0 + u * S::RPI + rsub;
+    int r = -1, c = -1;
+    if (j < lim && R.m > 0) {
+      entry(j, r, c);
+      if (r < 0 || r >= R.m) r = -1;
+    }
+    if (r >= R.first_miss_row && from_host) {
+      if (c < 0 || (int64_t)c >= R.n_max) r = -1;
+    } else {
+      c = -1;
+    }
+    rows[u] = r;
+    hrow[u] = r >= 0 ? c : -1;
+  }
+  // K and V of every entry in flight together (slot rows from HBM, missed
+  // rows over the host link); a skipped entry reads row 0 of the slab (when
+  // there is one) and is masked below.
+  const T* kb = R.kb + col * S::EPL;
+  const T* vb = R.vb + col * S::EPL;
+  const T* khb = from_host ? R.khb + col * S::EPL : kb;
+  const T* vhb = from_host ? R.vhb + col * S::EPL : vb;
+  const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+  u32x4 kr[S::U], vr[S::U];
+  if (R.m > 0) {
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      const bool h = hrow[u] >= 0;
+      const int64_t off = (int64_t)(h ? hrow[u] : (rows[u] >= 0 ? rows[u] : 0)) * D;
+      kr[u] = *reinterpret_cast<const u32x4*>((h ? khb : kb) + off);
+      vr[u] = *reinterpret_cast<const u32x4*>((h ? vhb : vb) + off);
+    }
+    if (from_host) {  // the slot keeps a copy of every fetched miss
+#pragma unroll
+      for (int u = 0; u < S::U; ++u) {
+        if (hrow[u] >= 0) {
+          T* kd = const_cast<T*>(kb) + (int64_t)rows[u] * D;
+          T* vd = const_cast<T*>(vb) + (int64_t)rows[u] * D;
+          *reinterpret_cast<u32x4*>(kd) = kr[u];
+          *reinterpret_cast<u32x4*>(vd) = vr[u];
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) kr[u] = vr[u] = zero;
+  }
+  float qr[S::EPL];
+#pragma unroll
+  for (int e = 0; e < S::EPL; ++e) qr[e] = q[col * S::EPL + e];
+
+  float s[S::U];
+#pragma unroll
+  for (int u = 0; u < S::U; ++u) {
+    float f[S::EPL];
+    Unpack<T>::run(kr[u], f);
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < S::EPL; ++e) a = fmaf(f[e], qr[e], a);
+    s[u] = a;
+  }
+  group_allreduce<S::LPR, S::U>(s);
+
+  // Wave-local softmax over its 32 entries (RPI row groups x U).
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < S::U; ++u) {
+    s[u] = (rows[u] >= 0) ? s[u] * scale : -INFINITY;
+    mx = fmaxf(mx, s[u]);
+  }
+#pragma unroll
+  for (int off = S::LPR; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float l = 0.f;
+  float o[S::EPL];
+#pragma unroll
+  for (int e = 0; e < S::EPL; ++e) o[e] = 0.f;
+#pragma unroll
+  for (int u = 0; u < S::U; ++u) {
+    const float w = (rows[u] >= 0) ? exp2f((s[u] - mx) * kLog2e) : 0.f;
+    l += w;
+    float f[S::EPL];
+    Unpack<T>::run(rows[u] >= 0 ? vr[u] : zero, f);
+#pragma unroll
+    for (int e = 0; e < S::EPL; ++e) o[e] = fmaf(w, f[e], o[e]);
+  }
+#pragma unroll
+  for (int off = S::LPR; off < 64; off <<= 1) {
+    l += __shfl_xor(l, off);
+#pragma unroll
+    for (int e = 0; e < S::EPL; ++e) o[e] += __shfl_xor(o[e], off);
+  }
+  if (rsub == 0) {
+#pragma unroll
+    for (int e = 0; e < S::EPL; ++e) lds.o[wave][col * S::EPL + e] = o[e];
+    if (col == 0) {
+      lds.m[wave] = mx;
+      lds.l[wave] = l;
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves (entry order is fixed: wave 0, 1, 2, 3).
+  cm = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kAttnWaves; ++w) cm = fmaxf(cm, lds.m[w]);
+  float f[kAttnWaves];
+  cl = 0.f;
+#pragma unroll
+  for (int w = 0; w < kAttnWaves; ++w) {
+    f[w] = (lds.l[w] > 0.f) ? exp2f((lds.m[w] - cm) * kLog2e) : 0.f;
+    cl += lds.l[w] * f[w];
+  }
+  od = 0.f;
+  const int d = threadIdx.x;
+  if (d < D) {
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) od += lds.o[w][d] * f[w];
+  }
+}
+
+// Merge of the chunk partials of one (b, h) by log-sum-exp, for column d:
+// partial c holds the weighted V sums [0, D), its max logit at D and its
+// weight sum at D + 1.
+template <int D>
+__device__ __forceinline__ void combine_chunks(const float* p, int chunks, int d, float& out_d,
+                                               float& lse) {
+  float mx = -INFINITY;
+  for (int c = 0; c < chunks; ++c) mx = fmaxf(mx, p[c * (D + 2) + D]);
+  float tot = 0.f, od = 0.f;
+  if (mx > -INFINITY) {
+    for (int c = 0; c < chunks; ++c) {
+      const float* pc = p + c * (D + 2);
+      const float wsum = pc[D + 1];
+      if (wsum > 0.f) {
+        const float f = exp2f((pc[D] - mx) * kLog2e);
+        tot += wsum * f;
+        od += pc[d] * f;
+      }
+    }
+  }
+  out_d = (tot > 0.f) ? od / tot : 0.f;
+  lse = (tot > 0.f) ? mx + logf(tot) : -INFINITY;
+}
+
+}  // namespace dd

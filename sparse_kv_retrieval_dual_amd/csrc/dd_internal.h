@@ -29,11 +29,13 @@ struct GatherJob;
 // -inf when fill_pad is set and are left untouched otherwise.  When pf is
 // set, pf_wgs extra workgroups (dispatched first) run that row gather
 // alongside the scoring (row_bytes = D * element size).  When both events
-// are given they are recorded at the kernel's own start and end.
+// are given they are recorded at the kernel's own start and end.  zero3
+// (or null): three int64 counters the kernel sets to zero.
 hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, int B, int H,
                         int Q, int D, int64_t n_max, int dtype, float scale, bool fill_pad,
                         float* scores, const GatherJob* pf, int pf_wgs, hipStream_t s,
-                        hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                        hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
+                        int64_t* zero3 = nullptr);
 
 // In-place softmax of each score row over its valid keys; 0 past lens[b].
 hipError_t launch_softmax_rows(float* scores, const int32_t* lens, int B, int H, int Q,
@@ -47,11 +49,32 @@ struct TopkBook {
   int32_t* counts;      // [3][BH]: misses, hits, fetchable prediction entries
 };
 
+// Attention fused into the top-k of the layer step: after its bookkeeping,
+// the workgroup of each current-query row attends that query over the
+// selection (slot rows, misses read from host memory and stored into
+// their slot rows k + t).
+struct FusedAttn {
+  const float* q;        // [BH][2][D] (plane 0 attends); null: no attention
+  const void* kslot;     // [BH][2k][D]
+  const void* vslot;
+  const void* k_host;    // pinned [BH][n_max][D]
+  const void* v_host;
+  int D, dtype;
+  float scale;
+  float* out;            // [BH][D]
+  float* lse;            // [BH] or null
+  int64_t* stats;        // {misses, hits, rows over the host link}, added to
+                         // atomically (zeroed before the launch), or null
+};
+
 // Top-k of each score row.  Plane j of slab bh is written at
-// (j == 0 ? out0 : out1) + bh * out_stride_bh.
+// (j == 0 ? out0 : out1) + bh * out_stride_bh.  book: bookkeeping of the
+// plane-0 rows (its pos / miss / counts outputs may each be null); attn:
+// the fused attention (needs book).
 hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, int Q,
                        int64_t n_max, int k, int32_t* out0, int32_t* out1,
-                       int64_t out_stride_bh, const TopkBook* book, hipStream_t s);
+                       int64_t out_stride_bh, const TopkBook* book, const FusedAttn* attn,
+                       hipStream_t s);
 
 // Row gather from pinned host memory.  Entry j < cnt[bh] (m if cnt is null)
 // of slab bh copies host row idx[bh*m + j] (zero row if out of range) to

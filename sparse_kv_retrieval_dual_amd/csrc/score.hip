@@ -47,10 +47,12 @@ template <typename T, int D, int Q>
 __global__ __launch_bounds__(kScoreWaves * 64) void k_score(
     const float* __restrict__ q, const T* __restrict__ keys, const int32_t* __restrict__ lens,
     int BH, int H, int64_t n_max, int tiles, float scale, float* __restrict__ scores,
-    int fill_pad, GatherJob pf, int pf_wgs) {
+    int fill_pad, GatherJob pf, int pf_wgs, int64_t* __restrict__ zero3) {
   using S = ScoreShape<T, D, Q>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  if (zero3 != nullptr && (int)blockIdx.x == pf_wgs && threadIdx.x < 3) zero3[threadIdx.x] = 0;
+  if (tiles == 0) return;
   if ((int)blockIdx.x < pf_wgs) {
     gather_rows<D * (int)sizeof(T)>(pf, (int64_t)blockIdx.x * kScoreWaves + wave,
                                     (int64_t)pf_wgs * kScoreWaves);
@@ -164,6 +166,7 @@ struct ScoreLaunch {
   int pf_wgs;
   hipStream_t s;
   hipEvent_t ev_start, ev_stop;
+  int64_t* zero3;
 };
 
 template <typename T, int D, int Q>
@@ -171,19 +174,19 @@ hipError_t launch_score_t(const ScoreLaunch& a) {
   using S = ScoreShape<T, D, Q>;
   const int BH = a.B * a.H;
   const int64_t tiles = (a.n_max + S::TILE - 1) / S::TILE;
-  if (BH == 0 || (tiles == 0 && a.pf_wgs == 0)) return hipSuccess;
-  const int64_t grid = tiles * BH + a.pf_wgs;
+  if (BH == 0 || (tiles == 0 && a.pf_wgs == 0 && a.zero3 == nullptr)) return hipSuccess;
+  const int64_t grid = (tiles > 0 ? tiles * BH : 1) + a.pf_wgs;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (a.ev_start != nullptr && a.ev_stop != nullptr) {
     // Events taken by the dispatch itself: the kernel's own duration.
     hipExtLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), 0,
                           a.s, a.ev_start, a.ev_stop, 0, a.q, static_cast<const T*>(a.keys),
                           a.lens, BH, a.H, a.n_max, (int)tiles, a.scale, a.scores,
-                          a.fill_pad ? 1 : 0, a.pf, a.pf_wgs);
+                          a.fill_pad ? 1 : 0, a.pf, a.pf_wgs, a.zero3);
   } else {
     hipLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), 0, a.s,
                        a.q, static_cast<const T*>(a.keys), a.lens, BH, a.H, a.n_max, (int)tiles,
-                       a.scale, a.scores, a.fill_pad ? 1 : 0, a.pf, a.pf_wgs);
+                       a.scale, a.scores, a.fill_pad ? 1 : 0, a.pf, a.pf_wgs, a.zero3);
   }
   return hipGetLastError();
 }
@@ -199,9 +202,9 @@ hipError_t launch_score_q(int Q, const ScoreLaunch& a) {
 hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, int B, int H,
                         int Q, int D, int64_t n_max, int dtype, float scale, bool fill_pad,
                         float* scores, const GatherJob* pf, int pf_wgs, hipStream_t s,
-                        hipEvent_t ev_start, hipEvent_t ev_stop) {
+                        hipEvent_t ev_start, hipEvent_t ev_stop, int64_t* zero3) {
   ScoreLaunch a{q, keys, lens, B, H, n_max, scale, fill_pad, scores, GatherJob{}, 0, s,
-                ev_start, ev_stop};
+                ev_start, ev_stop, zero3};
   if (pf != nullptr && pf->total > 0 && pf_wgs > 0) {
     a.pf = *pf;
     a.pf_wgs = (pf_wgs + 7) & ~7;  // keeps the scoring tiles' XCD placement

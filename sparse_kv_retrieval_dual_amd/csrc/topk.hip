@@ -30,6 +30,7 @@
 // prediction's slot row, misses get rows k, k + 1, ... in ascending order.
 #include <algorithm>
 
+#include "attn_body.h"
 #include "dd_device.h"
 #include "dd_internal.h"
 
@@ -53,9 +54,11 @@ constexpr int kSegKeys = 32 * kNT;       // keys per radix-path emit segment
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// LDS layout (words).  The filter path's region C holds the cached row,
-// and once the candidates' keys are read from it, the two bitmaps of the
-// row followed by the prediction.
+// LDS layout (words): histogram, scratch, candidate indices and keys (the
+// attention's scratch once the selection is emitted), then region C: the
+// cached row, and once the candidates' keys are read from it, the two
+// bitmaps of the row, the prediction and, for the fused attention, every
+// entry's slot row and row index.
 constexpr int kLHist = 0;                           // kBins counters
 constexpr int kLScr = kLHist + kBins;               // kScr ints
 constexpr int kLIdx = kLScr + kScr;                 // candidate indices
@@ -64,12 +67,17 @@ struct Lay {
   static constexpr int cap = CACHED ? kCapCached : kCapLong;
   static constexpr int key = kLIdx + cap;           // candidate keys
   static constexpr int c = key + cap;               // region C
-  static constexpr int words = c + (CACHED ? kTile : 2 * (kFilterMaxN / 32) + kMaxK);
+  static constexpr int bits = 2 * ((CACHED ? kTile : kFilterMaxN) / 32);
+  static constexpr int pred = c + bits;             // prediction, then slot rows, then rows
+  static constexpr int end = pred + 3 * kMaxK;
+  static constexpr int words = CACHED ? (c + kTile > end ? c + kTile : end) : end;
 };
 static_assert(Lay<true>::words * 4 <= 160 * 1024, "cached layout exceeds LDS");
-static_assert(2 * (kTile / 32) + kMaxK <= kTile, "bitmaps and prediction fit region C");
+static_assert(Lay<false>::words * 4 <= 160 * 1024, "long-row layout exceeds LDS");
 static_assert(4 * 256 <= kBins, "selection histograms fit the bound histogram");
-static_assert(kLIdx + kMaxK <= Lay<true>::words, "radix-path prediction fits");
+// attention scratch: per-wave partials and up to 32 chunk partials of D+2
+constexpr int kAttnScratchWords = 8 + 4 * 128 + 8 + 32 * (128 + 2);
+static_assert(kLIdx + kAttnScratchWords <= Lay<true>::c, "attention scratch fits");
 
 __device__ __forceinline__ void clear(uint32_t* p, int words) {
   for (int i = threadIdx.x; i < words; i += kNT) p[i] = 0u;
@@ -201,13 +209,17 @@ __device__ __forceinline__ void select_kth(const uint32_t* fkey, int cnt, int k,
 }
 
 // Where the selection goes: the output row and, for bookkeeping rows, the
-// prediction (in LDS), its length, the slot-row and miss rows.
+// prediction (in LDS) and its length, and the slot row of every entry and
+// the miss list in global memory and / or (for the fused attention) the
+// slot row and row index of every entry in LDS; each of those may be null.
 struct Sink {
   int32_t* out;
   const int32_t* s_pred;  // nullptr: no bookkeeping
   int plen;
   int32_t* pos;
   int32_t* miss;
+  int32_t* lpos;
+  int32_t* lcur;
 };
 
 // Emits, in ascending index order, the selected entries of this thread's
@@ -253,8 +265,10 @@ __device__ __forceinline__ int emit_words(uint32_t (&g)[MAXW], const uint32_t (&
       const int hit = find_in(sk.s_pred, sk.plen, c);
       if (j < k) {
         sk.out[j] = c;
+        if (sk.lcur != nullptr) sk.lcur[j] = c;
         if (hit >= 0) {
-          sk.pos[j] = hit;
+          if (sk.pos != nullptr) sk.pos[j] = hit;
+          if (sk.lpos != nullptr) sk.lpos[j] = hit;
         } else {
           mm[w] |= 1u << b;
           ++my_miss;
@@ -271,8 +285,10 @@ __device__ __forceinline__ int emit_words(uint32_t (&g)[MAXW], const uint32_t (&
 #pragma unroll 1
     for (uint32_t x = mm[w]; x != 0u; x &= x - 1u) {
       const int b = __ffs(x) - 1;
-      sk.pos[jb + __popc(g[w] & ((1u << b) - 1u))] = k + mr;
-      sk.miss[mr] = (w0 + w) * 32 + b;
+      const int jj = jb + __popc(g[w] & ((1u << b) - 1u));
+      if (sk.pos != nullptr) sk.pos[jj] = k + mr;
+      if (sk.lpos != nullptr) sk.lpos[jj] = k + mr;
+      if (sk.miss != nullptr) sk.miss[mr] = (w0 + w) * 32 + b;
       ++mr;
     }
     jb += __popc(g[w]);
@@ -379,8 +395,8 @@ __device__ __forceinline__ uint32_t passing(const f32x4& v, int i, int n, float 
 // keys pass the bound.
 template <int G, bool CACHED>
 __device__ bool filter_select(const float* __restrict__ row, int n, int64_t n_max, int k,
-                              uint32_t* smem, Sink& sk, const int32_t (&pv)[kPR], int& misses,
-                              int& fetchable) {
+                              uint32_t* smem, Sink& sk, bool book, const int32_t (&pv)[kPR],
+                              int& misses, int& fetchable) {
   using L = Lay<CACHED>;
   constexpr int CAP = L::cap;
   constexpr int UPG = kU / G;  // float4s per group and tile
@@ -489,10 +505,10 @@ __device__ bool filter_select(const float* __restrict__ row, int n, int64_t n_ma
   const int nw = (n + 31) >> 5;
   uint32_t* gt = regc;
   uint32_t* eq = regc + nw;
-  int32_t* s_pred = reinterpret_cast<int32_t*>(regc + 2 * nw);
+  int32_t* s_pred = reinterpret_cast<int32_t*>(smem + L::pred);
   clear(regc, 2 * nw);
   int pf = 0, pn = 0;
-  if (sk.pos != nullptr) {
+  if (book) {
     store_prediction(pv, k, n_max, s_pred, pf, pn);
     sk.s_pred = s_pred;
   }
@@ -537,14 +553,15 @@ __device__ __forceinline__ void row_hist(const float* __restrict__ row, int n, u
 
 // The radix path: T over the whole row, then, 8192 keys at a time, thread
 // t compares keys 32 t .. 32 t + 31 of the segment with T.
+template <bool CACHED>
 __device__ int radix_select(const float* __restrict__ row, int n, int64_t n_max, int k,
-                            uint32_t* smem, Sink& sk, const int32_t (&pv)[kPR],
+                            uint32_t* smem, Sink& sk, bool book, const int32_t (&pv)[kPR],
                             int& fetchable) {
   const int tid = threadIdx.x;
   uint32_t* hist = smem + kLHist;
   ScanBufs sb{reinterpret_cast<int*>(smem + kLScr), 0};
   int* bcast = reinterpret_cast<int*>(smem + kLScr) + 4 * kNW;
-  int32_t* s_pred = reinterpret_cast<int32_t*>(smem + kLIdx);
+  int32_t* s_pred = reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred);
   __syncthreads();
   clear(hist, kBins);
   __syncthreads();
@@ -569,7 +586,7 @@ __device__ int radix_select(const float* __restrict__ row, int n, int64_t n_max,
   const uint32_t thr = prefix | (uint32_t)d2;
 
   int pf = 0, pn = 0;
-  if (sk.pos != nullptr) {
+  if (book) {
     store_prediction(pv, k, n_max, s_pred, pf, pn);
     sk.s_pred = s_pred;
   }
@@ -606,22 +623,85 @@ __device__ int radix_select(const float* __restrict__ row, int n, int64_t n_max,
 
 // ------------------------------------------------------------------ kernel
 
+// Attention of the current query over its own selection (the layer step's
+// last stage), done by the workgroup of each bookkeeping row right after its
+// emit: slot rows and entry rows come from LDS, chunks of 128 entries as in
+// the attention kernel, chunk partials merged the same way.
+template <typename T, int D>
+__device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, int k,
+                                                  int64_t n_max, const int32_t* lpos,
+                                                  const int32_t* lcur, float* scratch) {
+  AttnLds<D>& lds = *reinterpret_cast<AttnLds<D>*>(scratch);
+  float* part = scratch + (sizeof(AttnLds<D>) + 15) / 16 * 4;
+  const int64_t slab = (int64_t)bh * 2 * k * D;
+  const AttnRows<T> R{static_cast<const T*>(fa.kslot) + slab, static_cast<const T*>(fa.vslot) + slab,
+                      static_cast<const T*>(fa.k_host) + (int64_t)bh * n_max * D,
+                      static_cast<const T*>(fa.v_host) + (int64_t)bh * n_max * D, 2 * k, k, n_max};
+  auto entry = [&](int j, int& r, int& c) {
+    r = lpos[j];
+    c = lcur[j];
+  };
+  const int chunks = (k + kAttnChunk - 1) / kAttnChunk;
+  const float* qrow = fa.q + (int64_t)bh * 2 * D;
+  const int d = threadIdx.x;
+  for (int ch = 0; ch < chunks; ++ch) {
+    float cm, cl, od;
+    attend_chunk<T, D>(qrow, R, ch * kAttnChunk, k, fa.scale, entry, lds, cm, cl, od);
+    if (d < D) {
+      if (chunks == 1) {
+        fa.out[(int64_t)bh * D + d] = (cl > 0.f) ? od / cl : 0.f;
+        if (d == 0 && fa.lse != nullptr) fa.lse[bh] = (cl > 0.f) ? cm + logf(cl) : -INFINITY;
+      } else {
+        float* pc = part + ch * (D + 2);
+        pc[d] = od;
+        if (d == 0) {
+          pc[D] = cl > 0.f ? cm : -INFINITY;
+          pc[D + 1] = cl;
+        }
+      }
+    }
+    __syncthreads();  // lds is reused by the next chunk; partials complete
+  }
+  if (chunks > 1 && d < D) {
+    float od, l;
+    combine_chunks<D>(part, chunks, d, od, l);
+    fa.out[(int64_t)bh * D + d] = od;
+    if (d == 0 && fa.lse != nullptr) fa.lse[bh] = l;
+  }
+}
+
+__device__ __forceinline__ void fused_attention(const FusedAttn& fa, int bh, int k, int64_t n_max,
+                                                const int32_t* lpos, const int32_t* lcur,
+                                                float* scratch) {
+  if (fa.dtype == kBF16) {
+    if (fa.D == 128) fused_attention_t<uint16_t, 128>(fa, bh, k, n_max, lpos, lcur, scratch);
+    else fused_attention_t<uint16_t, 64>(fa, bh, k, n_max, lpos, lcur, scratch);
+  } else {
+    if (fa.D == 128) fused_attention_t<float, 128>(fa, bh, k, n_max, lpos, lcur, scratch);
+    else fused_attention_t<float, 64>(fa, bh, k, n_max, lpos, lcur, scratch);
+  }
+}
+
 template <int G, bool CACHED>
 __global__ __launch_bounds__(kNT) void k_topk(
     const float* __restrict__ scores, const int32_t* __restrict__ lens, int H, int Q, int BH,
     int64_t n_max, int k, int32_t* __restrict__ out0, int32_t* __restrict__ out1,
-    int64_t out_stride, const int32_t* __restrict__ pred, int32_t* __restrict__ pos,
-    int32_t* __restrict__ miss, int32_t* __restrict__ counts, int filter) {
+    int64_t out_stride, int book_on, const int32_t* __restrict__ pred, int32_t* __restrict__ pos,
+    int32_t* __restrict__ miss, int32_t* __restrict__ counts, FusedAttn fa) {
   extern __shared__ uint32_t smem[];
   const int tid = threadIdx.x;
   int bh, j;
   xcd_tile_map(blockIdx.x, Q, BH, bh, j);
   const int64_t rowid = (int64_t)bh * Q + j;
   const float* row = scores + rowid * n_max;
-  const bool do_book = (pos != nullptr) && j == 0;
+  const bool do_book = book_on && j == 0;
+  const bool attend = do_book && fa.q != nullptr;
   const int32_t* pred_row = (do_book && pred != nullptr) ? pred + (int64_t)bh * k : nullptr;
   Sink sk{((j == 0) ? out0 : out1) + (int64_t)bh * out_stride, nullptr, 0,
-          do_book ? pos + (int64_t)bh * k : nullptr, do_book ? miss + (int64_t)bh * k : nullptr};
+          (do_book && pos != nullptr) ? pos + (int64_t)bh * k : nullptr,
+          (do_book && miss != nullptr) ? miss + (int64_t)bh * k : nullptr,
+          attend ? reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred) + kMaxK : nullptr,
+          attend ? reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred) + 2 * kMaxK : nullptr};
   // The prediction row, loaded now and stored in LDS once it is needed.
   int32_t pv[kPR];
 #pragma unroll
@@ -636,7 +716,7 @@ __global__ __launch_bounds__(kNT) void k_topk(
   if (n <= k) {
     // Every valid key is selected: entry c is c itself.
     ScanBufs sb{reinterpret_cast<int*>(smem + kLScr), 0};
-    int32_t* s_pred = reinterpret_cast<int32_t*>(smem + kLIdx);
+    int32_t* s_pred = reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred);
     int pf = 0, pn = 0;
     if (do_book) store_prediction(pv, k, n_max, s_pred, pf, pn);
     int e0, e1, t0, t1;
@@ -651,30 +731,46 @@ __global__ __launch_bounds__(kNT) void k_topk(
       if (c < k) {
         sk.out[c] = valid ? c : -1;
         if (do_book) {
-          sk.pos[c] = !valid ? -1 : (hit >= 0 ? hit : k + mr);
-          if (valid && hit < 0) sk.miss[mr] = c;
+          const int pr = !valid ? -1 : (hit >= 0 ? hit : k + mr);
+          if (sk.pos != nullptr) sk.pos[c] = pr;
+          if (sk.lpos != nullptr) {
+            sk.lpos[c] = pr;
+            sk.lcur[c] = valid ? c : -1;
+          }
+          if (valid && hit < 0 && sk.miss != nullptr) sk.miss[mr] = c;
         }
       }
       misses += mtot;
     }
   } else {
     bool done = false;
-    if (filter && n <= kFilterMaxN)
-      done = filter_select<G, CACHED>(row, n, n_max, k, smem, sk, pv, misses, fetchable);
+    if (n <= kFilterMaxN)
+      done = filter_select<G, CACHED>(row, n, n_max, k, smem, sk, do_book, pv, misses, fetchable);
     if (!done) {
       sk.s_pred = nullptr;
-      misses = radix_select(row, n, n_max, k, smem, sk, pv, fetchable);
+      misses = radix_select<CACHED>(row, n, n_max, k, smem, sk, do_book, pv, fetchable);
     }
   }
 
   if (!do_book) return;
-  for (int tt = misses + tid; tt < k; tt += kNT) sk.miss[tt] = -1;
-  if (tid == 0) {
-    const int valid = n < k ? n : k;
+  if (sk.miss != nullptr)
+    for (int tt = misses + tid; tt < k; tt += kNT) sk.miss[tt] = -1;
+  const int valid = n < k ? n : k;
+  if (tid == 0 && counts != nullptr) {
     counts[bh] = misses;
     counts[BH + bh] = valid - misses;
     counts[2 * BH + bh] = fetchable;
   }
+  if (!attend) return;
+  if (tid == 0 && fa.stats != nullptr) {
+    atomicAdd(reinterpret_cast<unsigned long long*>(fa.stats), (unsigned long long)misses);
+    atomicAdd(reinterpret_cast<unsigned long long*>(fa.stats) + 1,
+              (unsigned long long)(valid - misses));
+    atomicAdd(reinterpret_cast<unsigned long long*>(fa.stats) + 2,
+              (unsigned long long)(fetchable + misses));
+  }
+  __syncthreads();  // every entry's slot row and row index are in LDS
+  fused_attention(fa, bh, k, n_max, sk.lpos, sk.lcur, reinterpret_cast<float*>(smem + kLIdx));
 }
 
 template <bool CACHED>
@@ -696,14 +792,15 @@ TopkKernel<CACHED> pick_kernel(int g) {
 
 hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, int Q,
                        int64_t n_max, int k, int32_t* out0, int32_t* out1,
-                       int64_t out_stride_bh, const TopkBook* book, hipStream_t s) {
+                       int64_t out_stride_bh, const TopkBook* book, const FusedAttn* attn,
+                       hipStream_t s) {
   const int BH = B * H;
   if (BH == 0) return hipSuccess;
   const DeviceInfo& di = device_info();
   const bool cached = n_max <= kTile;
   const int64_t words = cached ? Lay<true>::words : Lay<false>::words;
-  const int filter = words * 4 <= di.lds_per_block ? 1 : 0;
-  const size_t shmem = (size_t)(filter ? words : (int64_t)kLIdx + kMaxK) * 4;
+  if (words * 4 > di.lds_per_block) return hipErrorInvalidConfiguration;
+  const size_t shmem = (size_t)words * 4;
   // Groups per thread: at least 4k group maxima (8192 at most).
   int g = 1;
   while (g < 32 && kNT * g < 4 * k) g *= 2;
@@ -717,17 +814,21 @@ hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, i
     }
     attr_set[di.device] = true;
   }
-  const bool do_book = book != nullptr && book->pos != nullptr;
-  const int32_t* pred = do_book ? book->pred : nullptr;
-  int32_t* pos = do_book ? book->pos : nullptr;
-  int32_t* miss = do_book ? book->miss : nullptr;
-  int32_t* counts = do_book ? book->counts : nullptr;
+  const int book_on = book != nullptr ? 1 : 0;
+  const int32_t* pred = book_on ? book->pred : nullptr;
+  int32_t* pos = book_on ? book->pos : nullptr;
+  int32_t* miss = book_on ? book->miss : nullptr;
+  int32_t* counts = book_on ? book->counts : nullptr;
+  FusedAttn fa{};
+  if (book_on && attn != nullptr) fa = *attn;
   if (cached) {
     hipLaunchKernelGGL(pick_kernel<true>(g), dim3(BH * Q), dim3(kNT), shmem, s, scores, lens, H, Q,
-                       BH, n_max, k, out0, out1, out_stride_bh, pred, pos, miss, counts, filter);
+                       BH, n_max, k, out0, out1, out_stride_bh, book_on, pred, pos, miss, counts,
+                       fa);
   } else {
     hipLaunchKernelGGL(pick_kernel<false>(g), dim3(BH * Q), dim3(kNT), shmem, s, scores, lens, H,
-                       Q, BH, n_max, k, out0, out1, out_stride_bh, pred, pos, miss, counts, filter);
+                       Q, BH, n_max, k, out0, out1, out_stride_bh, book_on, pred, pos, miss, counts,
+                       fa);
   }
   return hipGetLastError();
 }
