@@ -394,7 +394,7 @@ __device__ __forceinline__ uint32_t passing(const f32x4& v, int i, int n, float 
 // false, having written nothing, when more than the list's capacity of
 // keys pass the bound.
 template <int G, bool CACHED>
-__device__ bool filter_select(const float* __restrict__ row, int n, int64_t n_max, int k,
+__device__ __forceinline__ bool filter_select(const float* __restrict__ row, int n, int64_t n_max, int k,
                               uint32_t* smem, Sink& sk, bool book, const int32_t (&pv)[kPR],
                               int& misses, int& fetchable) {
   using L = Lay<CACHED>;
@@ -554,7 +554,7 @@ __device__ __forceinline__ void row_hist(const float* __restrict__ row, int n, u
 // The radix path: T over the whole row, then, 8192 keys at a time, thread
 // t compares keys 32 t .. 32 t + 31 of the segment with T.
 template <bool CACHED>
-__device__ int radix_select(const float* __restrict__ row, int n, int64_t n_max, int k,
+__device__ __forceinline__ int radix_select(const float* __restrict__ row, int n, int64_t n_max, int k,
                             uint32_t* smem, Sink& sk, bool book, const int32_t (&pv)[kPR],
                             int& fetchable) {
   const int tid = threadIdx.x;
