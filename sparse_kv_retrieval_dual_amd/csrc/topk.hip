@@ -28,6 +28,10 @@
 // For the current-query row of the layer step, the emit also looks every
 // selected index up in the prediction (binary search in LDS): hits keep the
 // prediction's slot row, misses get rows k, k + 1, ... in ascending order.
+// With attention fused in, that workgroup then runs the sparse decode
+// attention of the current query over its selection (DualDecoder, Figure 1
+// "Attention" box) from the slot rows and entry numbers it left in LDS,
+// reading each miss from host memory and storing it into its slot row.
 #include <algorithm>
 
 #include "attn_body.h"
