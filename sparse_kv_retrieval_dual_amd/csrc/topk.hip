@@ -26,13 +26,16 @@
 // a time.
 //
 // For the current-query row of the layer step, the emit also looks every
-// selected index up in the prediction (binary search in LDS): hits keep the
-// prediction's slot row, misses get rows k, k + 1, ... in ascending order.
+// selected index up in the prediction (held in LDS; each thread walks it
+// forward alongside its own ascending entries, from the first position that
+// falls in its words): hits keep the prediction's slot row, misses get rows
+// k, k + 1, ... in ascending order.
 // With attention fused in, that workgroup then runs the sparse decode
 // attention of the current query over its selection (DualDecoder, Figure 1
 // "Attention" box) from the slot rows and entry numbers it left in LDS,
 // reading each miss from host memory and storing it into its slot row.
 #include <algorithm>
+#include <climits>
 
 #include "attn_body.h"
 #include "dd_device.h"
@@ -79,6 +82,10 @@ struct Lay {
 static_assert(Lay<true>::words * 4 <= 160 * 1024, "cached layout exceeds LDS");
 static_assert(Lay<false>::words * 4 <= 160 * 1024, "long-row layout exceeds LDS");
 static_assert(4 * 256 <= kBins, "selection histograms fit the bound histogram");
+// Once the bound is picked, the filter path keeps, above the selection's
+// histograms, the first prediction position of each thread's words.
+constexpr int kLFirst = kLHist + 4 * 256;
+static_assert(4 * 256 + kNT <= kBins, "walk starts fit the bound histogram");
 // attention scratch: per-wave partials and up to 32 chunk partials of D+2
 constexpr int kAttnScratchWords = 8 + 4 * 128 + 8 + 32 * (128 + 2);
 static_assert(kLIdx + kAttnScratchWords <= Lay<true>::c, "attention scratch fits");
@@ -110,6 +117,23 @@ __device__ __forceinline__ int find_in(const int32_t* s, int len, int c) {
   }
   return (lo < len && s[lo] == c) ? lo : -1;
 }
+
+// First position of the ascending list s[0, len) whose entry is >= c.
+__device__ __forceinline__ int lower_bound_in(const int32_t* s, int len, int c) {
+  int lo = 0, hi = len;
+#pragma unroll 1
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (s[mid] < c) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Start of a thread's walk through the prediction: none of its entries can
+// lie in the thread's words (kNoStart), or to be found by binary search.
+constexpr int kNoStart = -1;
+constexpr int kSearchStart = -2;
 
 // The smallest fp32 value whose key is >= b (-inf when every value's is).
 __device__ __forceinline__ float key_floor(uint32_t b) {
@@ -229,11 +253,13 @@ struct Sink {
 // Emits, in ascending index order, the selected entries of this thread's
 // bitmap words w0, w0 + 1, ...: g (the "> T" set, extended here by the
 // taken "== T" bits of e).  gt_before / eq_before: the counts in lower
-// words; misses are numbered from miss_base.  Returns this block's misses.
+// words; misses are numbered from miss_base.  lo: where this thread's walk
+// through the prediction starts (kNoStart, kSearchStart or a position).
+// Returns this block's misses.
 template <int MAXW>
 __device__ __forceinline__ int emit_words(uint32_t (&g)[MAXW], const uint32_t (&e)[MAXW], int w0,
                                           int gt_before, int eq_before, int take_eq, int k,
-                                          const Sink& sk, ScanBufs& sb, int miss_base) {
+                                          const Sink& sk, ScanBufs& sb, int miss_base, int lo) {
   int take = take_eq - eq_before;
   const int j0 = gt_before + (eq_before < take_eq ? eq_before : take_eq);
 #pragma unroll
@@ -257,6 +283,15 @@ __device__ __forceinline__ int emit_words(uint32_t (&g)[MAXW], const uint32_t (&
   }
   // Each selected entry is looked up once: hits get their prediction row
   // now, misses are marked and get slot rows after the scan of miss counts.
+  // The selected entries and the prediction both ascend, so the lookup
+  // walks the prediction forward from lo; an entry is a hit only where the
+  // prediction holds it (a prediction out of order can only lose hits).
+  if (lo == kSearchStart) {
+    bool any = false;
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) any = any || g[w] != 0u;
+    lo = any ? lower_bound_in(sk.s_pred, sk.plen, w0 * 32) : kNoStart;
+  }
   uint32_t mm[MAXW];
   int my_miss = 0;
 #pragma unroll
@@ -266,7 +301,12 @@ __device__ __forceinline__ int emit_words(uint32_t (&g)[MAXW], const uint32_t (&
     for (uint32_t x = g[w]; x != 0u; x &= x - 1u) {
       const int b = __ffs(x) - 1;
       const int c = (w0 + w) * 32 + b;
-      const int hit = find_in(sk.s_pred, sk.plen, c);
+      int hit = -1;
+      if (lo >= 0) {
+#pragma unroll 1
+        while (lo < sk.plen && sk.s_pred[lo] < c) ++lo;
+        if (lo < sk.plen && sk.s_pred[lo] == c) hit = lo;
+      }
       if (j < k) {
         sk.out[j] = c;
         if (sk.lcur != nullptr) sk.lcur[j] = c;
@@ -303,11 +343,12 @@ __device__ __forceinline__ int emit_words(uint32_t (&g)[MAXW], const uint32_t (&
 // Emits the selection held in the "> T" (gt) and "== T" (eq) bitmaps of a
 // row of nw words; thread t owns words [t W, t W + W).  pf / pn: this
 // thread's count of fetchable / non-negative prediction entries.  Returns
-// the misses; sets fetchable and sk.plen from the block totals.
+// the misses; sets fetchable and sk.plen from the block totals.  lo: the
+// start of this thread's walk through the prediction (see emit_words).
 template <int MAXW>
 __device__ __forceinline__ int emit_bitmaps(const uint32_t* gt, const uint32_t* eq, int nw,
                                             int take_eq, int k, Sink& sk, int pf, int pn,
-                                            ScanBufs& sb, int& fetchable) {
+                                            ScanBufs& sb, int& fetchable, int lo) {
   const int W = (nw + kNT - 1) / kNT;
   const int w0 = (int)threadIdx.x * W;
   uint32_t g[MAXW], e[MAXW];
@@ -326,7 +367,7 @@ __device__ __forceinline__ int emit_bitmaps(const uint32_t* gt, const uint32_t* 
   block_scan_pair<kNW>(gc | (ec << 16), pf | (pn << 16), sb, ex, ep, tx, tp);
   fetchable = tp & 0xFFFF;
   if (sk.s_pred != nullptr) sk.plen = tp >> 16;
-  return emit_words<MAXW>(g, e, w0, ex & 0xFFFF, ex >> 16, take_eq, k, sk, sb, 0);
+  return emit_words<MAXW>(g, e, w0, ex & 0xFFFF, ex >> 16, take_eq, k, sk, sb, 0, lo);
 }
 
 // Stores this thread's prediction entries in s_pred; counts the fetchable
@@ -445,6 +486,8 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
   pick_bin(hist, k, sb, bcast, d0, above);
   const float fb = key_floor((uint32_t)d0 << 21);
   clear(hist, 4 * 256);  // the selection's histograms (ordered by the next barrier)
+  int* s_first = reinterpret_cast<int*>(smem + kLFirst);
+  if (book) s_first[tid] = INT_MAX;
 
   // Candidates: every entry >= fb, by index.  Count, scan, then write.
   int cnt;
@@ -515,6 +558,18 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
   if (book) {
     store_prediction(pv, k, n_max, s_pred, pf, pn);
     sk.s_pred = s_pred;
+    // Where each thread's walk through the prediction starts: the first
+    // position whose entry lies in the thread's bitmap words (the emit's
+    // W words per thread).
+    const int W = (nw + kNT - 1) / kNT;
+#pragma unroll
+    for (int r = 0; r < kPR; ++r) {
+      const int p = tid + kNT * r;
+      if (p < k && pv[r] >= 0 && pv[r] < n) {
+        const int owner = (pv[r] >> 5) / W;
+        atomicMin(&s_first[owner], p);
+      }
+    }
   }
   uint32_t thr;
   int take_eq;
@@ -527,8 +582,13 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
   }
   __syncthreads();
   // A cached row has at most kTile / 32 bitmap words: 4 per thread.
+  int lo = kNoStart;
+  if (book) {
+    const int f = s_first[tid];
+    lo = f == INT_MAX ? kNoStart : f;
+  }
   misses = emit_bitmaps<CACHED ? kTile / 32 / kNT : kMaxWords>(gt, eq, nw, take_eq, k, sk, pf, pn,
-                                                                  sb, fetchable);
+                                                                  sb, fetchable, lo);
   return true;
 }
 
@@ -616,7 +676,7 @@ __device__ __forceinline__ int radix_select(const float* __restrict__ row, int n
     }
     // Per-segment counts stay below 2^16 (8192 keys).
     const int mtot = emit_words<1>(g, e, base / 32, out_run + (ex & 0xFFFF),
-                                   eq_run + (ex >> 16), kr, k, sk, sb, miss_run);
+                                   eq_run + (ex >> 16), kr, k, sk, sb, miss_run, kSearchStart);
     out_run += tx & 0xFFFF;
     eq_run += tx >> 16;
     miss_run += mtot;

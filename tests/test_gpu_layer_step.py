@@ -99,8 +99,15 @@ def test_outputs_do_not_depend_on_prediction_or_ring():
     rand = [gen.random_sorted_indices(B * H, k, torch.tensor([w.n_max] * (B * H)), seed=50 + l,
                                       fill=0.9).reshape(B, H, k).cuda() for l in range(w.L)]
     other = [c.flip(0).contiguous() for c in base["cur"]]  # request 1's set for request 0 and back
+    g = torch.Generator().manual_seed(77)
+    perm = torch.randperm(k, generator=g).cuda()
+    shuffled = [c[:, :, perm].contiguous() for c in base["cur"]]  # out of order
+    dups = [torch.cat([c[:, :, : k // 2], c[:, :, : k // 2]], dim=2).contiguous() for c in base["cur"]]
     preds = {"spec": base["spec"], "perfect": base["cur"], "random": rand, "other": other,
-             "partial": [None, base["spec"][1], None]}
+             "partial": [None, base["spec"][1], None], "shuffled": shuffled, "duplicated": dups}
+    # Reading of the pages (prediction format): a prediction out of order or
+    # with repeats may lose hits, never outputs; the slot rows stay right.
+    unordered = {"shuffled", "duplicated"}
     for R, mode in ((1, "side"), (2, "side"), (3, "side"), (1, "fused"), (2, "fused")):
         ctx = dd.Context(ring_slots=R, prefetch=mode, prefetch_wgs=8 if R == 1 else 0)
         ring = torch.zeros(dd.ring_bytes(R, B, H, w.D, k, 1), dtype=torch.uint8, device="cuda")
@@ -121,10 +128,15 @@ def test_outputs_do_not_depend_on_prediction_or_ring():
                 misses = sum(len(c - p) for c, p in for_sets)
                 hits = sum(len(c & p) for c, p in for_sets)
                 fetched = sum(len(p) for _, p in for_sets) + misses
-                assert st.tolist() == [misses, hits, fetched], (R, pname, l, st)
+                if pname in unordered:
+                    assert st[0] + st[1] == misses + hits and st[1] <= hits, (R, pname, l, st)
+                else:
+                    assert st.tolist() == [misses, hits, fetched], (R, pname, l, st)
             # slot of the last layer: row pos[j] holds host row cur[j] (K and V)
             l = w.L - 1
             slot = l % R
+            if pname in unordered:
+                continue
             cur_l = res["cur"][l].cpu().numpy()
             p_l = None if pred[l] is None else pred[l].cpu().numpy()
             bk = oracle.bookkeeping(cur_l, p_l, w.n_max)
