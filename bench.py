@@ -105,6 +105,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time the eager loop only")
     ap.add_argument("--prefetch-wgs", type=int, default=0)
     ap.add_argument("--prefetch", default="auto", choices=["auto", "side", "fused"])
+    ap.add_argument("--k-rows", default="device", choices=["device", "host"],
+                    help="where attention reads the selected K rows")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -138,7 +140,7 @@ def main():
     torch.cuda.synchronize()
 
     ctx = dd.Context(ring_slots=args.ring, gather_cus=args.gather_cus,
-                     prefetch_wgs=args.prefetch_wgs, prefetch=args.prefetch)
+                     prefetch_wgs=args.prefetch_wgs, prefetch=args.prefetch, k_rows=args.k_rows)
     cur = [torch.empty(B, H, k, dtype=torch.int32, device=dev)]
     spec = [torch.empty(B, H, k, dtype=torch.int32, device=dev)]
     out = [torch.empty(B, H, D, dtype=torch.float32, device=dev)]
@@ -240,12 +242,13 @@ def main():
     # (both queries), plus the two fp32 logits written per key.
     score_bytes = n_keys * D * eb + n_keys * 2 * 4
     score_gbps = score_bytes / (t_score * 1e-3) / 1e9
-    prefetch_bytes = valid * 2 * D * eb              # k rows of K and V per (b, h)
+    planes = 1 if args.k_rows == "device" else 2    # V rows only, or K and V
+    prefetch_bytes = valid * planes * D * eb         # k rows per (b, h)
     # The prefetch runs on the side stream (own events) or inside the scoring
     # kernel (then its rate is bounded below by that kernel's duration).
     t_pf = t_prefetch if t_prefetch is not None else t_score
     prefetch_gbps = prefetch_bytes / (t_pf * 1e-3) / 1e9
-    miss_bytes = misses * 2 * D * eb
+    miss_bytes = misses * planes * D * eb
 
     # Reference rates measured in the same process.
     big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -291,7 +294,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": D, "context": w.n_max,
                    "top_k": k, "queries": 2, "kv_dtype": w.dtype, "accumulate": "f32",
-                   "ring_slots": args.ring, "hbm_key_copies": len(k_copies)},
+                   "ring_slots": args.ring, "hbm_key_copies": len(k_copies),
+                   "k_rows": args.k_rows},
         "roofline": {"bound": "hbm", "achieved": score_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": score_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic,

@@ -184,6 +184,8 @@ typedef struct dd_ctx_config {
                       still saturate the host link */
   int prefetch_mode; /* DD_PREFETCH_AUTO (fused for L == 1, side stream
                       otherwise), DD_PREFETCH_SIDE or DD_PREFETCH_FUSED */
+  int k_rows;       /* DD_KROWS_DEVICE (0) or DD_KROWS_HOST: where attention
+                      reads the K rows of the selected entries */
 } dd_ctx_config;
 
 /* DD_PREFETCH_SIDE: the prediction of layer l is fetched on the side stream
@@ -192,6 +194,15 @@ typedef struct dd_ctx_config {
  * scoring kernel (one stream, no cross-stream wait; it overlaps that
  * layer's key scan).  Results are identical either way. */
 enum { DD_PREFETCH_AUTO = 0, DD_PREFETCH_SIDE = 1, DD_PREFETCH_FUSED = 2 };
+
+/* DD_KROWS_DEVICE: the layer step already holds every key in HBM for
+ * scoring (k_dev), so attention reads the K row of each selected entry
+ * there, and only V rows are fetched from the host (prefetch and misses);
+ * the slot's K plane stays unused.  DD_KROWS_HOST: K and V rows both come
+ * from the host copy into the slot, as for a system that keeps only
+ * compressed keys on the GPU (arXiv page, section 2.2).  K bytes are the
+ * same in both places, so the outputs are bitwise identical. */
+enum { DD_KROWS_DEVICE = 0, DD_KROWS_HOST = 1 };
 
 /* Creates the side stream and events on the current device.  The context
  * may only be used with that device current. */

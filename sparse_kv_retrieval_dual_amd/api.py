@@ -201,17 +201,20 @@ class Context:
     """dd_ctx: the side stream, events and ring configuration of the layer step."""
 
     PREFETCH_MODES = {"auto": 0, "side": 1, "fused": 2}
+    K_ROWS = {"device": 0, "host": 1}
 
     def __init__(self, ring_slots: int = 2, gather_cus: int = 0, prefetch_wgs: int = 0,
-                 prefetch: str = "auto"):
+                 prefetch: str = "auto", k_rows: str = "device"):
         lib = _lib()
         cfg = L.CtxConfig(ring_slots=int(ring_slots), gather_cus=int(gather_cus),
                           prefetch_wgs=int(prefetch_wgs),
-                          prefetch_mode=self.PREFETCH_MODES[prefetch])
+                          prefetch_mode=self.PREFETCH_MODES[prefetch],
+                          k_rows=self.K_ROWS[k_rows])
         h = ctypes.c_void_p()
         L.check(lib.dd_ctx_create(ctypes.byref(cfg), ctypes.byref(h)))
         self._h = h
         self.ring_slots = int(ring_slots)
+        self.k_rows = k_rows
         self._ring = None
         self._ws = None
         self._fin = weakref.finalize(self, lib.dd_ctx_destroy, h)

@@ -20,6 +20,7 @@ struct dd_ctx {
   int gather_cus = 0;
   int prefetch_wgs = 32;
   int prefetch_mode = DD_PREFETCH_AUTO;
+  int k_rows = DD_KROWS_DEVICE;
   hipStream_t side = nullptr;       // prefetch gathers
   hipStream_t main_own = nullptr;   // CU-masked main stream (gather_cus > 0 only)
   hipEvent_t ev_start = nullptr;    // caller stream at entry
@@ -232,11 +233,14 @@ DD_API int dd_ctx_create(const dd_ctx_config* cfg, dd_ctx** ctx) {
     return fail(DD_ERR_INVALID_ARG, "gather_cus and prefetch_wgs must be >= 0");
   if (cfg->prefetch_mode < DD_PREFETCH_AUTO || cfg->prefetch_mode > DD_PREFETCH_FUSED)
     return fail(DD_ERR_INVALID_ARG, "unknown prefetch_mode %d", cfg->prefetch_mode);
+  if (cfg->k_rows != DD_KROWS_DEVICE && cfg->k_rows != DD_KROWS_HOST)
+    return fail(DD_ERR_INVALID_ARG, "unknown k_rows %d", cfg->k_rows);
   dd_ctx* c = new dd_ctx();
   c->ring_slots = cfg->ring_slots;
   c->gather_cus = cfg->gather_cus;
   c->prefetch_wgs = cfg->prefetch_wgs > 0 ? cfg->prefetch_wgs : 32;
   c->prefetch_mode = cfg->prefetch_mode;
+  c->k_rows = cfg->k_rows;
   hipError_t e = hipGetDevice(&c->device);
   const int cus = dd::device_info().cus;
   if (e == hipSuccess && c->gather_cus > 0) {
@@ -350,7 +354,11 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     char* kslot = static_cast<char*>(a->ring) + (size_t)slot * sbytes;
     char* vslot = kslot + sbytes / 2;
     const int32_t* P = a->pred ? a->pred[l] : nullptr;
-    const dd::GatherJob pf{static_cast<const uint8_t*>(a->k_host[l]),
+    // With K rows read from the scoring copy, only V rows cross the host
+    // link (the slot's K plane stays unused).
+    const bool kdev = c->k_rows == DD_KROWS_DEVICE;
+    const void* khost = kdev ? nullptr : a->k_host[l];
+    const dd::GatherJob pf{static_cast<const uint8_t*>(khost),
                            static_cast<const uint8_t*>(a->v_host[l]), a->n_max, P, k, nullptr,
                            (int64_t)BH * k, reinterpret_cast<uint8_t*>(kslot),
                            reinterpret_cast<uint8_t*>(vslot), 2 * (int64_t)k, 0};
@@ -358,7 +366,7 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     if (P && use_side) {
       if (l >= R) DD_CHECK_HIP(hipStreamWaitEvent(side, c->ev_free[slot], 0), "side waits slot");
       if (tev(l, 5)) DD_CHECK_HIP(hipEventRecord(tev(l, 5), side), "timing");
-      hipError_t e = dd::launch_gather(a->k_host[l], a->v_host[l], a->n_max, rowb, P, k, nullptr,
+      hipError_t e = dd::launch_gather(khost, a->v_host[l], a->n_max, rowb, P, k, nullptr,
                                        BH, kslot, vslot, 2 * (int64_t)k, 0, c->prefetch_wgs, side);
       if (e != hipSuccess) return hip_fail(e, "prefetch gather launch");
       if (tev(l, 6)) DD_CHECK_HIP(hipEventRecord(tev(l, 6), side), "timing");
@@ -381,9 +389,11 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     // Top-k of both queries, the bookkeeping of the current one and its
     // attention in one kernel: each current-query row's workgroup attends
     // right after its selection, reading misses from host memory itself
-    // (and storing them into their slot rows k + t).
+    // (and storing them into their slot rows k + t); K rows come from the
+    // scoring copy when kdev.
     const dd::TopkBook book{P, nullptr, nullptr, nullptr};
-    const dd::FusedAttn fa{a->q[l], kslot, vslot, a->k_host[l], a->v_host[l], D, a->dtype, sc,
+    const dd::FusedAttn fa{a->q[l], kslot, vslot, a->k_host[l], a->v_host[l],
+                           kdev ? a->k_dev[l] : nullptr, D, a->dtype, sc,
                            a->out[l], a->lse ? a->lse[l] : nullptr, st};
     e = dd::launch_topk(scores, a->lens, B, H, 2, a->n_max, k, a->cur_idx[l], a->spec_idx[l], k,
                         &book, &fa, ms);

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(
   const AttnRows<T> R{krows + (int64_t)bh * m * D, vrows + (int64_t)bh * m * D,
                       from_host ? static_cast<const T*>(ms.k_host) + (int64_t)bh * ms.n_max * D : nullptr,
                       from_host ? static_cast<const T*>(ms.v_host) + (int64_t)bh * ms.n_max * D : nullptr,
-                      m, ms.first_miss_row, ms.n_max};
+                      nullptr, m, ms.first_miss_row, ms.n_max};
   const int32_t* pos_bh = pos != nullptr ? pos + (int64_t)bh * k : nullptr;
   const int32_t* cur_bh = from_host ? ms.cur + (int64_t)bh * k : nullptr;
   auto entry = [&](int j, int& r, int& hc) {

@@ -44,13 +44,17 @@ __device__ __forceinline__ void group_allreduce(float* x) {
 
 // The rows of one (b, h): slot rows kb / vb ([m][D]), and for entries whose
 // slot row is >= first_miss_row the host rows khb / vhb ([n_max][D]) they
-// are read from (and copied into their slot row); khb null: no host rows.
+// are read from (and copied into their slot row); vhb null: no host rows.
+// kdb (or null): the device copy of the keys ([n_max][D]); when set, every
+// entry's K row is read from it by row index and only V rows come from the
+// slot or the host (khb is then unused).
 template <typename T>
 struct AttnRows {
   const T* kb;
   const T* vb;
   const T* khb;
   const T* vhb;
+  const T* kdb;
   int m;
   int first_miss_row;
   int64_t n_max;
@@ -79,9 +83,11 @@ __device__ __forceinline__ void attend_chunk(const float* __restrict__ q, const 
   const int col = lane % S::LPR;
   const int rsub = lane / S::LPR;
   const int e0 = c0 + wave * kWaveEntries;  // this wave's first entry
-  const bool from_host = R.khb != nullptr;
+  const bool from_host = R.vhb != nullptr;
+  const bool kdev = R.kdb != nullptr;
   int rows[S::U];
-  int hrow[S::U];
+  int hrow[S::U];  // host row of a miss, else -1
+  int krow[S::U];  // row of the device key copy (kdev), else -1
 #pragma unroll
   for (int u = 0; u < S::U; ++u) {
     const int j = e0 + u * S::RPI + rsub;
@@ -90,21 +96,21 @@ __device__ __forceinline__ void attend_chunk(const float* __restrict__ q, const 
       entry(j, r, c);
       if (r < 0 || r >= R.m) r = -1;
     }
-    if (r >= R.first_miss_row && from_host) {
-      if (c < 0 || (int64_t)c >= R.n_max) r = -1;
-    } else {
-      c = -1;
-    }
+    const bool cvalid = c >= 0 && (int64_t)c < R.n_max;
+    const bool miss = r >= R.first_miss_row && from_host;
+    if ((miss || kdev) && !cvalid) r = -1;
     rows[u] = r;
-    hrow[u] = r >= 0 ? c : -1;
+    hrow[u] = (r >= 0 && miss) ? c : -1;
+    krow[u] = (r >= 0 && kdev) ? c : -1;
   }
-  // K and V of every entry in flight together (slot rows from HBM, missed
-  // rows over the host link); a skipped entry reads row 0 of the slab (when
-  // there is one) and is masked below.
+  // K and V of every entry in flight together (slot rows and device keys
+  // from HBM, missed rows over the host link); a skipped entry reads row 0
+  // of the slab (when there is one) and is masked below.
   const T* kb = R.kb + col * S::EPL;
   const T* vb = R.vb + col * S::EPL;
-  const T* khb = from_host ? R.khb + col * S::EPL : kb;
+  const T* khb = (from_host && !kdev) ? R.khb + col * S::EPL : kb;
   const T* vhb = from_host ? R.vhb + col * S::EPL : vb;
+  const T* kdb = kdev ? R.kdb + col * S::EPL : kb;
   const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
   u32x4 kr[S::U], vr[S::U];
   if (R.m > 0) {
@@ -112,17 +118,20 @@ __device__ __forceinline__ void attend_chunk(const float* __restrict__ q, const 
     for (int u = 0; u < S::U; ++u) {
       const bool h = hrow[u] >= 0;
       const int64_t off = (int64_t)(h ? hrow[u] : (rows[u] >= 0 ? rows[u] : 0)) * D;
-      kr[u] = *reinterpret_cast<const u32x4*>((h ? khb : kb) + off);
+      const int64_t koff = (int64_t)(krow[u] >= 0 ? krow[u] : 0) * D;
+      kr[u] = *reinterpret_cast<const u32x4*>(kdev ? kdb + koff : (h ? khb : kb) + off);
       vr[u] = *reinterpret_cast<const u32x4*>((h ? vhb : vb) + off);
     }
     if (from_host) {  // the slot keeps a copy of every fetched miss
 #pragma unroll
       for (int u = 0; u < S::U; ++u) {
         if (hrow[u] >= 0) {
-          T* kd = const_cast<T*>(kb) + (int64_t)rows[u] * D;
           T* vd = const_cast<T*>(vb) + (int64_t)rows[u] * D;
-          *reinterpret_cast<u32x4*>(kd) = kr[u];
           *reinterpret_cast<u32x4*>(vd) = vr[u];
+          if (!kdev) {
+            T* kd = const_cast<T*>(kb) + (int64_t)rows[u] * D;
+            *reinterpret_cast<u32x4*>(kd) = kr[u];
+          }
         }
       }
     }

@@ -57,8 +57,10 @@ struct FusedAttn {
   const float* q;        // [BH][2][D] (plane 0 attends); null: no attention
   const void* kslot;     // [BH][2k][D]
   const void* vslot;
-  const void* k_host;    // pinned [BH][n_max][D]
+  const void* k_host;    // pinned [BH][n_max][D] (unused when k_dev is set)
   const void* v_host;
+  const void* k_dev;     // device keys [BH][n_max][D]: K rows read from here
+                         // (only V rows travel from the host), or null
   int D, dtype;
   float scale;
   float* out;            // [BH][D]

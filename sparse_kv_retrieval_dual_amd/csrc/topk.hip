@@ -698,9 +698,12 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
   AttnLds<D>& lds = *reinterpret_cast<AttnLds<D>*>(scratch);
   float* part = scratch + (sizeof(AttnLds<D>) + 15) / 16 * 4;
   const int64_t slab = (int64_t)bh * 2 * k * D;
+  const int64_t hslab = (int64_t)bh * n_max * D;
+  const bool kdev = fa.k_dev != nullptr;
   const AttnRows<T> R{static_cast<const T*>(fa.kslot) + slab, static_cast<const T*>(fa.vslot) + slab,
-                      static_cast<const T*>(fa.k_host) + (int64_t)bh * n_max * D,
-                      static_cast<const T*>(fa.v_host) + (int64_t)bh * n_max * D, 2 * k, k, n_max};
+                      kdev ? nullptr : static_cast<const T*>(fa.k_host) + hslab,
+                      static_cast<const T*>(fa.v_host) + hslab,
+                      kdev ? static_cast<const T*>(fa.k_dev) + hslab : nullptr, 2 * k, k, n_max};
   auto entry = [&](int j, int& r, int& c) {
     r = lpos[j];
     c = lcur[j];

@@ -130,8 +130,9 @@ def _check_slab(w, lay, res, l, b, h, n, pred_l):
     return worst
 
 
-def _check_slot(w, ring, res, l, R, pred_l, lay, slabs):
-    """Ring slot of layer l: row pos[j] of the slab holds host row cur[j] (K and V)."""
+def _check_slot(w, ring, res, l, R, pred_l, lay, slabs, k_rows="device"):
+    """Ring slot of layer l: row pos[j] of the slab holds host row cur[j] (V, and
+    K when K rows come from the host)."""
     eb = w.elem_bytes
     BH, k, D = w.B * w.H, w.k, w.D
     slot_bytes = 2 * BH * 2 * k * D * eb
@@ -151,7 +152,8 @@ def _check_slot(w, ring, res, l, R, pred_l, lay, slabs):
         ks = ks.reshape(2 * k, D * eb)
         vs = vs.reshape(2 * k, D * eb)
         for j in np.nonzero(cur >= 0)[0]:
-            assert np.array_equal(ks[pos[j]], kh[cur[j]]), (l, b, h, j)
+            if k_rows == "host":
+                assert np.array_equal(ks[pos[j]], kh[cur[j]]), (l, b, h, j)
             assert np.array_equal(vs[pos[j]], vh[cur[j]]), (l, b, h, j)
 
 
@@ -184,6 +186,23 @@ def test_full_size_layer_step(name, m, samples):
     pred = [s.clone() for s in cold["spec"]]
     hot = run(pred)
     _log(t0, "predicted step done")
+    if L == 1:
+        # K rows from the host copy instead of the device copy: the same bits
+        hctx = dd.Context(ring_slots=R, k_rows="host")
+        hring = torch.empty_like(ring)
+        hres = hctx.layer_step([d["q"] for d in sel], [d["k_dev"] for d in sel],
+                               [d["k_host"] for d in sel], [d["v_host"] for d in sel], lens, w.k,
+                               pred=pred, ring=hring)
+        torch.cuda.synchronize()
+        for key in ("out", "lse", "cur", "spec", "stats"):
+            if key == "stats":
+                assert torch.equal(hres[key], hot[key])
+            else:
+                assert torch.equal(hres[key][0], hot[key][0]), key
+        bh_pick = [(0, 0), (w.B - 1, w.H - 1)]
+        _check_slot(w, hring, hres, 0, R, pred[0].cpu().numpy(), layers[0], bh_pick, "host")
+        hctx.close()
+        _log(t0, "K rows from the host copy: bitwise equal")
 
     for l in range(L):
         # the prediction never changes a result

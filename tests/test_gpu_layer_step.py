@@ -108,11 +108,16 @@ def test_outputs_do_not_depend_on_prediction_or_ring():
     # Reading of the pages (prediction format): a prediction out of order or
     # with repeats may lose hits, never outputs; the slot rows stay right.
     unordered = {"shuffled", "duplicated"}
-    for R, mode in ((1, "side"), (2, "side"), (3, "side"), (1, "fused"), (2, "fused")):
-        ctx = dd.Context(ring_slots=R, prefetch=mode, prefetch_wgs=8 if R == 1 else 0)
+    # K rows from the device copy (the base) or the host copy: the same bytes,
+    # so the same bits.
+    for R, mode, k_rows in ((1, "side", "device"), (2, "side", "device"), (3, "side", "device"),
+                            (1, "fused", "device"), (2, "fused", "device"), (2, "side", "host"),
+                            (1, "fused", "host"), (2, "fused", "host")):
+        ctx = dd.Context(ring_slots=R, prefetch=mode, prefetch_wgs=8 if R == 1 else 0,
+                         k_rows=k_rows)
         ring = torch.zeros(dd.ring_bytes(R, B, H, w.D, k, 1), dtype=torch.uint8, device="cuda")
         for pname, pred in preds.items():
-            announce(f"  R={R} prefetch={mode} pred={pname}")
+            announce(f"  R={R} prefetch={mode} k_rows={k_rows} pred={pname}")
             res = _run(dd, ctx, w, data, pred=pred, ring=ring)
             for l in range(w.L):
                 assert torch.equal(res["out"][l], base["out"][l]), (R, pname, l)
@@ -132,7 +137,8 @@ def test_outputs_do_not_depend_on_prediction_or_ring():
                     assert st[0] + st[1] == misses + hits and st[1] <= hits, (R, pname, l, st)
                 else:
                     assert st.tolist() == [misses, hits, fetched], (R, pname, l, st)
-            # slot of the last layer: row pos[j] holds host row cur[j] (K and V)
+            # slot of the last layer: row pos[j] holds host row cur[j] (V, and K
+            # when K rows come from the host)
             l = w.L - 1
             slot = l % R
             if pname in unordered:
@@ -153,7 +159,8 @@ def test_outputs_do_not_depend_on_prediction_or_ring():
                         if c < 0:
                             continue
                         r = bk["pos"][b, h, j]
-                        assert np.array_equal(kslot[b, h, r], kh[b, h, c])
+                        if k_rows == "host":
+                            assert np.array_equal(kslot[b, h, r], kh[b, h, c])
                         assert np.array_equal(vslot[b, h, r], vh[b, h, c])
         ctx.close()
     base_ctx.close()
