@@ -137,6 +137,33 @@ DD_API int dd_gather(const void* k_host, const void* v_host, const int32_t* idx,
                      int dtype, void* k_rows, void* v_rows, hipStream_t stream);
 
 /* Workspace bytes dd_sparse_attn needs for these sizes (0 is possible). */
+/* Chunk gather (arXiv page, section 2.2: the GPU picks important chunks
+ * and retrieves their entries from host memory).  Entry j < cnt[b][h] (m if
+ * cnt is NULL) names chunk idx[b][h][j]: its `chunk` consecutive host rows
+ * from row chunk * idx are copied, byte for byte, to rows
+ * [j * chunk, (j + 1) * chunk) of k_rows / v_rows ([B][H][m * chunk][D]).
+ * A negative index, and every row at or past n_max, gives zero rows; entries
+ * at or past cnt are left untouched.  chunk: a power of two in [1, 64].  The
+ * rows of a chunk are contiguous in host memory, so the link carries runs of
+ * chunk * D * element-size bytes.  Either plane may be NULL (not both). */
+DD_API int dd_gather_chunks(const void* k_host, const void* v_host, const int32_t* idx,
+                            const int32_t* cnt, int B, int H, int m, int chunk, int D,
+                            int64_t n_max, int dtype, void* k_rows, void* v_rows,
+                            hipStream_t stream);
+
+/* Chunk landmarks: the compressed per-chunk keys that selection scores
+ * (arXiv page, section 2.2, ShadowKV's chunk landmarks).  The pages do not
+ * define a landmark; here it is the mean key of the chunk.
+ *   landmarks[b][h][e][:] (fp32, ceil(n_max / chunk) rows per (b, h)) =
+ *   the mean of keys[b][h][i][:] over the rows i of chunk e (i in
+ *   [e * chunk, (e + 1) * chunk)) below lens[b], summed in fp32 in row order
+ *   and divided by their count; 0 for a chunk with no such row.
+ * keys: device [B][H][n_max][D] (dtype); chunk: a power of two in [1, 64].
+ * Landmarks are built once per cache (and as it grows), not per step. */
+DD_API int dd_landmarks(const void* keys, const int32_t* lens, int B, int H, int D,
+                        int64_t n_max, int chunk, int dtype, float* landmarks,
+                        hipStream_t stream);
+
 DD_API size_t dd_attn_workspace(int B, int H, int k, int D);
 
 /* Decode attention over gathered rows only (Figure 1 "Attention" on the
@@ -245,6 +272,18 @@ typedef struct dd_layer_step_args {
   hipStream_t stream;           /* caller's stream; all work is ordered after
                                    earlier work on it and before later work */
   hipEvent_t* timing;           /* NULL or L * DD_STAGE_EVENTS events (see above) */
+  /* Selection by chunk landmarks (arXiv page, section 2.2: chunks of adjacent
+   * entries with compressed landmarks, from which the GPU picks important
+   * chunks and retrieves their entries).  chunk 0 or 1: every key is scored
+   * and k keys are selected (the default).  chunk = c in {2, 4, ..., 64}:
+   * the c-row landmarks of each layer are scored instead of k_dev, k / c
+   * chunks are selected per query (k must be a multiple of c), pred /
+   * cur_idx / spec_idx hold chunk indices ([B][H][k / c]), every selected
+   * chunk brings its c rows (those below lens[b]) to the slot and to
+   * attention, and stats count chunks. */
+  int chunk;
+  const float* const* landmarks; /* chunk > 1: per layer device fp32
+                                    [B][H][ceil(n_max / chunk)][D] (dd_landmarks) */
 } dd_layer_step_args;
 
 /* Runs the layer step for layers 0..L-1.  Per layer, on the main stream:

@@ -6,11 +6,14 @@ this package; the product path never does.
 from .dd_oracle import (  # noqa: F401
     BF16,
     F32,
+    F64,
     attend_rows,
     attention_weights,
     bookkeeping,
+    chunk_rows,
     default_scale,
     gather_rows,
+    landmarks,
     layer_step,
     masked_attention,
     scaled_logits,

@@ -27,6 +27,9 @@ What it computes, and where the pages define it:
 * Sparse attention.  Decode attention of the current query over only the
   selected rows ("Attention" box of Figure 1), written here as dense
   attention with every unselected logit masked to -inf.
+* Chunk landmarks.  Selection may instead score compressed landmarks of
+  chunks of adjacent entries and retrieve whole chunks (arXiv page, section
+  2.2, on ShadowKV); a landmark is read as the mean key of its chunk.
 
 Arithmetic is float64 on exact upcasts of the stored fp32 or bf16 values.
 Where the pages leave a point open, the reading used is stated next to the
@@ -40,6 +43,7 @@ import numpy as np
 
 F32 = "f32"
 BF16 = "bf16"
+F64 = "f64"  # values already exact in float64 (landmarks)
 
 
 def upcast(stored: np.ndarray, dtype: str) -> np.ndarray:
@@ -53,6 +57,8 @@ def upcast(stored: np.ndarray, dtype: str) -> np.ndarray:
         return bits.view(np.float32).astype(np.float64)
     if dtype == F32:
         return np.asarray(stored, dtype=np.float32).astype(np.float64)
+    if dtype == F64:
+        return np.asarray(stored, dtype=np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -276,9 +282,46 @@ def bookkeeping(cur: np.ndarray, pred: np.ndarray | None, n_max: int):
             "prefetched": prefetched}
 
 
+def landmarks(keys: np.ndarray, lens: np.ndarray, chunk: int, dtype: str) -> np.ndarray:
+    """Chunk landmarks, float64 [B][H][ceil(n_max / chunk)][D].
+
+    Chunk e of (b, h) is rows [e*chunk, (e+1)*chunk); its landmark is the mean
+    of those of its keys below lens[b], and zero when it has none.  Reading:
+    the arXiv page (section 2.2) names compressed chunk landmarks without
+    defining them; the mean key of the chunk is the plainest reading.
+    """
+    B, H, n_max, D = keys.shape
+    nc = -(-n_max // chunk)
+    out = np.zeros((B, H, nc, D), dtype=np.float64)
+    for b in range(B):
+        n = int(min(max(int(lens[b]), 0), n_max))
+        kf = upcast(keys[b, :, :n], dtype)                      # [H][n][D]
+        for e in range(-(-n // chunk)):
+            lo, hi = e * chunk, min((e + 1) * chunk, n)
+            out[b, :, e] = kf[:, lo:hi].sum(axis=1) / (hi - lo)
+    return out
+
+
+def chunk_rows(sel: np.ndarray, lens: np.ndarray, chunk: int) -> np.ndarray:
+    """Rows of the selected chunks: int32 [B][H][ks*chunk], ascending, -1 padded.
+
+    Chunk c brings rows c*chunk .. c*chunk + chunk - 1, those below lens[b].
+    """
+    B, H, ks = sel.shape
+    out = np.full((B, H, ks * chunk), -1, dtype=np.int32)
+    for b in range(B):
+        n = int(lens[b])
+        for h in range(H):
+            rows = [c * chunk + i for c in sorted(int(x) for x in sel[b, h] if x >= 0)
+                    for i in range(chunk) if c * chunk + i < n]
+            out[b, h, :len(rows)] = rows
+    return out
+
+
 def layer_step(q: np.ndarray, keys_dev: np.ndarray, keys_host: np.ndarray,
                values_host: np.ndarray, lens: np.ndarray, k: int, dtype: str,
-               pred: np.ndarray | None = None, scale: float | None = None):
+               pred: np.ndarray | None = None, scale: float | None = None,
+               chunk: int = 0):
     """One layer of the predictive decode step, end to end.
 
     Score both queries against every cached key, select each query's top-k,
@@ -286,7 +329,30 @@ def layer_step(q: np.ndarray, keys_dev: np.ndarray, keys_host: np.ndarray,
     over its own set.  Reading: the true set is always the one attended,
     because misses are fetched on the critical path, so `out` does not depend
     on `pred`; the speculated set is returned as the next step's prediction.
+
+    chunk >= 1: selection by chunk landmarks instead.  Both queries score the
+    landmarks (same scale), k // chunk chunks are selected per query (ties to
+    the lower chunk), the prediction and the bookkeeping are in chunks, and
+    the current query attends over the rows of its chunks (those below
+    lens[b]).  chunk = 1 is the per-key step computed through landmarks.
     """
+    if chunk >= 1:
+        D = keys_dev.shape[3]
+        sc = default_scale(D) if scale is None or scale <= 0 else float(scale)
+        lm = landmarks(keys_dev, lens, chunk, dtype)
+        nlen = np.array([-(-int(x) // chunk) if x > 0 else 0 for x in lens], dtype=np.int64)
+        s = scaled_logits(q, lm, nlen, F64, sc)
+        sel = select_topk(s, nlen, k // chunk)
+        cur = np.ascontiguousarray(sel[:, :, 0])
+        spec = np.ascontiguousarray(sel[:, :, 1])
+        bk = bookkeeping(cur, pred, lm.shape[2])
+        rows = chunk_rows(cur, lens, chunk)
+        out, lse = masked_attention(q[:, :, 0], keys_host, values_host, lens, rows, dtype, sc)
+        misses = int(bk["miss_cnt"].sum())
+        stats = np.array([misses, int(bk["hits"].sum()),
+                          int(bk["prefetched"].sum()) + misses], dtype=np.int64)
+        return {"scores": s, "cur": cur, "spec": spec, "out": out, "lse": lse,
+                "stats": stats, "landmarks": lm, "rows": rows, **bk}
     s = scaled_logits(q, keys_dev, lens, dtype, scale)
     sel = select_topk(s, lens, k)
     cur = np.ascontiguousarray(sel[:, :, 0])

@@ -11,8 +11,10 @@ from .api import (  # noqa: F401
     Context,
     attn_workspace_bytes,
     gather,
+    gather_chunks,
     host_empty,
     kv_dtype,
+    landmarks,
     layer_step_workspace_bytes,
     ring_bytes,
     score,

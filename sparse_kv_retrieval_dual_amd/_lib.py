@@ -48,6 +48,7 @@ class LayerStepArgs(ctypes.Structure):
         ("ws", P), ("ws_bytes", c_size_t),
         ("stream", P),
         ("timing", P),
+        ("chunk", c_int), ("landmarks", P),
     ]
 
 
@@ -68,6 +69,9 @@ _SIGNATURES = {
     "dd_layer_step_workspace": (c_size_t, [c_int, c_int, c_int, c_int64, c_int]),
     "dd_layer_step": (c_int, [P, ctypes.POINTER(LayerStepArgs)]),
     "dd_stream_copy": (c_int, [P, P, c_size_t, P]),
+    "dd_gather_chunks": (c_int, [P, P, P, P, c_int, c_int, c_int, c_int, c_int, c_int64, c_int,
+                                 P, P, P]),
+    "dd_landmarks": (c_int, [P, P, c_int, c_int, c_int, c_int64, c_int, c_int, P, P]),
 }
 
 _lib = None

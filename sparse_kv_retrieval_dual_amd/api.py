@@ -130,6 +130,55 @@ def gather(k_host, v_host, idx, cnt=None, k_out=None, v_out=None, stream=None):
     return k_out, v_out
 
 
+def gather_chunks(k_host, v_host, idx, chunk: int, cnt=None, k_out=None, v_out=None, stream=None):
+    """dd_gather_chunks.  idx int32 [B][H][m] chunk indices; rows out [B][H][m*chunk][D]."""
+    ref = k_host if k_host is not None else v_host
+    _need(ref is not None, "need at least one host plane")
+    _dev(idx, "idx")
+    _need(idx.dtype == torch.int32 and idx.dim() == 3, "idx must be int32 [B][H][m]")
+    B, H, m = idx.shape
+    _need(ref.dim() == 4 and ref.shape[0] == B and ref.shape[1] == H, "host planes must be [B][H][n_max][D]")
+    n_max, D = ref.shape[2], ref.shape[3]
+    dt = kv_dtype(ref)
+    for t, name in ((k_host, "k_host"), (v_host, "v_host")):
+        if t is not None:
+            _need(not t.is_cuda and t.is_contiguous() and t.shape == ref.shape and t.dtype == ref.dtype,
+                  f"{name} must be a contiguous host tensor like the other plane")
+    if cnt is not None:
+        _dev(cnt, "cnt")
+        _need(cnt.dtype == torch.int32 and cnt.numel() == B * H, "cnt must be int32 [B][H]")
+    rows = m * int(chunk)
+    if k_host is not None and k_out is None:
+        k_out = torch.empty(B, H, rows, D, dtype=ref.dtype, device=idx.device)
+    if v_host is not None and v_out is None:
+        v_out = torch.empty(B, H, rows, D, dtype=ref.dtype, device=idx.device)
+    for t, name in ((k_out, "k_out"), (v_out, "v_out")):
+        if t is not None:
+            _dev(t, name)
+            _need(t.shape == (B, H, rows, D) and t.dtype == ref.dtype,
+                  f"{name} must be [B][H][m*chunk][D]")
+    L.check(_lib().dd_gather_chunks(_p(k_host), _p(v_host), _p(idx), _p(cnt), B, H, m, int(chunk),
+                                    D, n_max, dt, _p(k_out), _p(v_out), _stream(stream)))
+    return k_out, v_out
+
+
+def landmarks(keys, lens, chunk: int, out=None, stream=None):
+    """dd_landmarks.  keys device [B][H][n_max][D]; returns fp32 [B][H][ceil(n_max/chunk)][D]."""
+    _dev(keys, "keys"), _dev(lens, "lens")
+    _need(keys.dim() == 4 and keys.is_contiguous(), "keys must be contiguous [B][H][n_max][D]")
+    B, H, n_max, D = keys.shape
+    _need(lens.dtype == torch.int32 and lens.numel() == B, "lens must be int32 [B]")
+    nc = (n_max + int(chunk) - 1) // int(chunk)
+    if out is None:
+        out = torch.empty(B, H, nc, D, dtype=torch.float32, device=keys.device)
+    _dev(out, "out")
+    _need(out.shape == (B, H, nc, D) and out.dtype == torch.float32 and out.is_contiguous(),
+          "out must be fp32 [B][H][ceil(n_max/chunk)][D]")
+    L.check(_lib().dd_landmarks(_p(keys), _p(lens), B, H, D, n_max, int(chunk), kv_dtype(keys),
+                                _p(out), _stream(stream)))
+    return out
+
+
 def attn_workspace_bytes(B: int, H: int, k: int, D: int) -> int:
     return int(_lib().dd_attn_workspace(B, H, k, D))
 
@@ -231,12 +280,14 @@ class Context:
 
     def layer_step(self, q, k_dev, k_host, v_host, lens, k: int, pred=None, scale: float = 0.0,
                    cur=None, spec=None, out=None, lse=None, stats=None, ring=None, ws=None,
-                   timing=None, stream=None):
+                   timing=None, stream=None, chunk: int = 0, landmarks=None):
         """dd_layer_step over the layers given as lists (one tensor per layer).
 
         q[l] fp32 [B][H][2][D]; k_dev[l] device [B][H][n_max][D]; k_host[l], v_host[l]
         pinned host tensors of the same shape; pred: None or a list whose entries are
         None or int32 [B][H][k].  Returns dict(cur, spec, out, lse, stats).
+        chunk > 1: landmarks[l] fp32 [B][H][ceil(n_max/chunk)][D] are scored and
+        pred / cur / spec hold k // chunk chunk indices per (b, h).
         `timing` is None or a sequence of L * DD_STAGE_EVENTS raw hipEvent_t handles.
         """
         Lyr = len(q)
@@ -246,6 +297,10 @@ class Context:
         n_max = k_dev[0].shape[2]
         dt = kv_dtype(k_dev[0])
         dev = q[0].device
+        chunk = int(chunk)
+        ks = k // chunk if chunk > 1 else k
+        _need(chunk <= 1 or landmarks is not None and len(landmarks) == Lyr,
+              "chunk > 1 needs one landmark tensor per layer")
         for l in range(Lyr):
             _dev(q[l], "q"), _dev(k_dev[l], "k_dev")
             _need(q[l].shape == (B, H, 2, D) and q[l].dtype == torch.float32, "q shape")
@@ -255,13 +310,19 @@ class Context:
                       and t.dtype == k_dev[l].dtype, "host K/V must be contiguous [B][H][n_max][D]")
             if pred is not None and pred[l] is not None:
                 _dev(pred[l], "pred")
-                _need(pred[l].shape == (B, H, k) and pred[l].dtype == torch.int32, "pred must be int32 [B][H][k]")
+                _need(pred[l].shape == (B, H, ks) and pred[l].dtype == torch.int32,
+                      "pred must be int32 [B][H][k // chunk]")
+            if chunk > 1:
+                _dev(landmarks[l], "landmarks")
+                _need(landmarks[l].shape == (B, H, (n_max + chunk - 1) // chunk, D)
+                      and landmarks[l].dtype == torch.float32 and landmarks[l].is_contiguous(),
+                      "landmarks must be fp32 [B][H][ceil(n_max/chunk)][D]")
         _dev(lens, "lens")
         _need(lens.dtype == torch.int32 and lens.numel() == B, "lens must be int32 [B]")
         if cur is None:
-            cur = [torch.empty(B, H, k, dtype=torch.int32, device=dev) for _ in range(Lyr)]
+            cur = [torch.empty(B, H, ks, dtype=torch.int32, device=dev) for _ in range(Lyr)]
         if spec is None:
-            spec = [torch.empty(B, H, k, dtype=torch.int32, device=dev) for _ in range(Lyr)]
+            spec = [torch.empty(B, H, ks, dtype=torch.int32, device=dev) for _ in range(Lyr)]
         if out is None:
             out = [torch.empty(B, H, D, dtype=torch.float32, device=dev) for _ in range(Lyr)]
         if lse is None:
@@ -277,7 +338,8 @@ class Context:
         keep = [_ptr_array(q), _ptr_array(k_dev), _ptr_array(k_host), _ptr_array(v_host),
                 _ptr_array(pred) if pred is not None else None,
                 _ptr_array(cur), _ptr_array(spec), _ptr_array(out),
-                _ptr_array(lse) if lse is not None else None]
+                _ptr_array(lse) if lse is not None else None,
+                _ptr_array(landmarks) if chunk > 1 else None]
         tarr = None
         if timing is not None:
             tarr = (ctypes.c_void_p * len(timing))(*timing)
@@ -295,6 +357,8 @@ class Context:
             ws=ws.data_ptr(), ws_bytes=ws.numel() * ws.element_size(),
             stream=_stream(stream).value,
             timing=None if tarr is None else ctypes.cast(tarr, ctypes.c_void_p),
+            chunk=chunk,
+            landmarks=None if keep[9] is None else ctypes.cast(keep[9], ctypes.c_void_p),
         )
         L.check(_lib().dd_layer_step(self._h, ctypes.byref(a)))
         return {"cur": cur, "spec": spec, "out": out, "lse": lse, "stats": stats}

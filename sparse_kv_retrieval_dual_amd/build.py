@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdd.so")
 
-SOURCES = ["score.hip", "topk.hip", "gather.hip", "attn.hip", "util.hip", "abi.cpp"]
+SOURCES = ["score.hip", "topk.hip", "gather.hip", "attn.hip", "landmark.hip", "util.hip", "abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -184,6 +184,59 @@ DD_API int dd_gather(const void* k_host, const void* v_host, const int32_t* idx,
   return DD_OK;
 }
 
+static int chunk_shift_of(int chunk, int* cs) {
+  int s = 0;
+  while (s < 7 && (1 << s) < chunk) ++s;
+  if (chunk < 1 || chunk > 64 || (1 << s) != chunk)
+    return fail(DD_ERR_INVALID_ARG, "chunk must be a power of two in [1, 64] (got %d)", chunk);
+  *cs = s;
+  return DD_OK;
+}
+
+DD_API int dd_gather_chunks(const void* k_host, const void* v_host, const int32_t* idx,
+                            const int32_t* cnt, int B, int H, int m, int chunk, int D,
+                            int64_t n_max, int dtype, void* k_rows, void* v_rows,
+                            hipStream_t stream) {
+  int rc = check_shape(B, H, D, n_max, dtype);
+  if (rc) return rc;
+  int cs = 0;
+  rc = chunk_shift_of(chunk, &cs);
+  if (rc) return rc;
+  if (m < 0) return fail(DD_ERR_INVALID_ARG, "m must be >= 0 (got %d)", m);
+  if ((int64_t)m * chunk > 0x7fffffff) return fail(DD_ERR_INVALID_ARG, "m * chunk too large");
+  if ((int64_t)B * H * m == 0) return DD_OK;
+  if (!idx) return fail(DD_ERR_INVALID_ARG, "idx is NULL");
+  if (!k_host && !v_host) return fail(DD_ERR_INVALID_ARG, "both host planes are NULL");
+  if ((k_host && !k_rows) || (v_host && !v_rows))
+    return fail(DD_ERR_INVALID_ARG, "destination missing for a host plane");
+  if ((k_host && (!aligned16(k_host) || !aligned16(k_rows))) ||
+      (v_host && (!aligned16(v_host) || !aligned16(v_rows))))
+    return fail(DD_ERR_INVALID_ARG, "host and row buffers must be 16-byte aligned");
+  const int rowb = D * dd::elem_bytes(dtype);
+  hipError_t e = dd::launch_gather(k_host, v_host, n_max, rowb, idx, m, cnt, B * H,
+                                   k_host ? k_rows : nullptr, v_host ? v_rows : nullptr,
+                                   (int64_t)m * chunk, 0, 0, stream, cs);
+  if (e != hipSuccess) return hip_fail(e, "gather kernel launch");
+  return DD_OK;
+}
+
+DD_API int dd_landmarks(const void* keys, const int32_t* lens, int B, int H, int D,
+                        int64_t n_max, int chunk, int dtype, float* landmarks,
+                        hipStream_t stream) {
+  int rc = check_shape(B, H, D, n_max, dtype);
+  if (rc) return rc;
+  int cs = 0;
+  rc = chunk_shift_of(chunk, &cs);
+  if (rc) return rc;
+  if ((int64_t)B * H == 0 || n_max == 0) return DD_OK;
+  if (!keys || !lens || !landmarks) return fail(DD_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(keys) || !aligned16(landmarks))
+    return fail(DD_ERR_INVALID_ARG, "keys and landmarks must be 16-byte aligned");
+  hipError_t e = dd::launch_landmarks(keys, lens, B, H, D, n_max, cs, dtype, landmarks, stream);
+  if (e != hipSuccess) return hip_fail(e, "landmark kernel launch");
+  return DD_OK;
+}
+
 DD_API size_t dd_attn_workspace(int B, int H, int k, int D) {
   if (B <= 0 || H <= 0 || k <= 0) return 0;
   return dd::attn_workspace(B, H, k, D);
@@ -312,7 +365,25 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     if (!aligned16(a->k_dev[l]) || !aligned16(a->k_host[l]) || !aligned16(a->v_host[l]))
       return fail(DD_ERR_INVALID_ARG, "K/V buffers of layer %d must be 16-byte aligned", l);
   }
+  // Selection by chunk landmarks: ks chunks of 2^cs rows each, k rows in all.
+  int cs = 0;
+  if (a->chunk > 1) {
+    while ((1 << cs) < a->chunk) ++cs;
+    if ((1 << cs) != a->chunk || a->chunk > 64)
+      return fail(DD_ERR_INVALID_ARG, "chunk must be 0, 1 or a power of two up to 64 (got %d)",
+                  a->chunk);
+    if (a->k % a->chunk != 0)
+      return fail(DD_ERR_INVALID_ARG, "k (%d) must be a multiple of chunk (%d)", a->k, a->chunk);
+    if (!a->landmarks) return fail(DD_ERR_INVALID_ARG, "chunk > 1 needs landmarks");
+    for (int l = 0; l < a->L; ++l)
+      if (!a->landmarks[l] || !aligned16(a->landmarks[l]))
+        return fail(DD_ERR_INVALID_ARG, "landmarks of layer %d missing or not 16-byte aligned", l);
+  } else if (a->chunk < 0) {
+    return fail(DD_ERR_INVALID_ARG, "chunk must be >= 0");
+  }
   const int B = a->B, H = a->H, D = a->D, k = a->k, BH = B * H;
+  const int ks = k >> cs;                                      // entries selected per query
+  const int64_t n_sel = (a->n_max + (1 << cs) - 1) >> cs;      // rows of the scored matrix
   const size_t sbytes = slot_bytes(B, H, D, k, a->dtype);
   const size_t ring_need = (size_t)c->ring_slots * sbytes;
   if (!a->ring || a->ring_bytes < ring_need || !aligned16(a->ring))
@@ -359,15 +430,16 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     const bool kdev = c->k_rows == DD_KROWS_DEVICE;
     const void* khost = kdev ? nullptr : a->k_host[l];
     const dd::GatherJob pf{static_cast<const uint8_t*>(khost),
-                           static_cast<const uint8_t*>(a->v_host[l]), a->n_max, P, k, nullptr,
-                           (int64_t)BH * k, reinterpret_cast<uint8_t*>(kslot),
-                           reinterpret_cast<uint8_t*>(vslot), 2 * (int64_t)k, 0};
+                           static_cast<const uint8_t*>(a->v_host[l]), a->n_max, P, ks, nullptr,
+                           (int64_t)BH * ks, reinterpret_cast<uint8_t*>(kslot),
+                           reinterpret_cast<uint8_t*>(vslot), 2 * (int64_t)k, 0, cs, rowb};
 
     if (P && use_side) {
       if (l >= R) DD_CHECK_HIP(hipStreamWaitEvent(side, c->ev_free[slot], 0), "side waits slot");
       if (tev(l, 5)) DD_CHECK_HIP(hipEventRecord(tev(l, 5), side), "timing");
-      hipError_t e = dd::launch_gather(khost, a->v_host[l], a->n_max, rowb, P, k, nullptr,
-                                       BH, kslot, vslot, 2 * (int64_t)k, 0, c->prefetch_wgs, side);
+      hipError_t e = dd::launch_gather(khost, a->v_host[l], a->n_max, rowb, P, ks, nullptr,
+                                       BH, kslot, vslot, 2 * (int64_t)k, 0, c->prefetch_wgs, side,
+                                       cs);
       if (e != hipSuccess) return hip_fail(e, "prefetch gather launch");
       if (tev(l, 6)) DD_CHECK_HIP(hipEventRecord(tev(l, 6), side), "timing");
       DD_CHECK_HIP(hipEventRecord(c->ev_gathered[slot], side), "record gathered");
@@ -379,10 +451,11 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     int64_t* st = a->stats ? a->stats + 3 * (size_t)l : nullptr;
     const bool score_ev = tev(l, 0) && tev(l, 1);
     if (tev(l, 0) && !score_ev) DD_CHECK_HIP(hipEventRecord(tev(l, 0), ms), "timing");
-    hipError_t e = dd::launch_score(a->q[l], a->k_dev[l], a->lens, B, H, 2, D, a->n_max, a->dtype,
+    hipError_t e = dd::launch_score(a->q[l], cs ? static_cast<const void*>(a->landmarks[l]) : a->k_dev[l],
+                                    a->lens, B, H, 2, D, n_sel, cs ? DD_F32 : a->dtype,
                                     sc, false, scores, (P && fused) ? &pf : nullptr,
                                     c->prefetch_wgs, ms, score_ev ? tev(l, 0) : nullptr,
-                                    score_ev ? tev(l, 1) : nullptr, st);
+                                    score_ev ? tev(l, 1) : nullptr, st, cs);
     if (e != hipSuccess) return hip_fail(e, "score kernel launch");
     if (tev(l, 1) && !score_ev) DD_CHECK_HIP(hipEventRecord(tev(l, 1), ms), "timing");
     if (P && use_side) DD_CHECK_HIP(hipStreamWaitEvent(ms, c->ev_gathered[slot], 0), "main waits prefetch");
@@ -393,10 +466,10 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     // scoring copy when kdev.
     const dd::TopkBook book{P, nullptr, nullptr, nullptr};
     const dd::FusedAttn fa{a->q[l], kslot, vslot, a->k_host[l], a->v_host[l],
-                           kdev ? a->k_dev[l] : nullptr, D, a->dtype, sc,
+                           kdev ? a->k_dev[l] : nullptr, a->n_max, cs, D, a->dtype, sc,
                            a->out[l], a->lse ? a->lse[l] : nullptr, st};
-    e = dd::launch_topk(scores, a->lens, B, H, 2, a->n_max, k, a->cur_idx[l], a->spec_idx[l], k,
-                        &book, &fa, ms);
+    e = dd::launch_topk(scores, a->lens, B, H, 2, n_sel, ks, a->cur_idx[l], a->spec_idx[l], ks,
+                        &book, &fa, ms, cs);
     if (e != hipSuccess) return hip_fail(e, "top-k and attention kernel launch");
     for (int ev = 2; ev <= 4; ++ev)
       if (tev(l, ev)) DD_CHECK_HIP(hipEventRecord(tev(l, ev), ms), "timing");

@@ -264,4 +264,11 @@ __device__ __forceinline__ int64_t clamp_len(int32_t len, int64_t n_max) {
   return n < 0 ? 0 : (n > n_max ? n_max : n);
 }
 
+// Chunks of 2^shift rows that cover the first len rows (len for shift 0),
+// at most n_max of them.
+__device__ __forceinline__ int64_t chunk_len(int32_t len, int shift, int64_t n_max) {
+  const int64_t n = len < 0 ? 0 : (((int64_t)len + (1 << shift) - 1) >> shift);
+  return n > n_max ? n_max : n;
+}
+
 }  // namespace dd

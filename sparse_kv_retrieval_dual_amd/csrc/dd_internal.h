@@ -30,12 +30,14 @@ struct GatherJob;
 // set, pf_wgs extra workgroups (dispatched first) run that row gather
 // alongside the scoring (row_bytes = D * element size).  When both events
 // are given they are recorded at the kernel's own start and end.  zero3
-// (or null): three int64 counters the kernel sets to zero.
+// (or null): three int64 counters the kernel sets to zero.  len_shift > 0:
+// the rows are chunk landmarks, 2^len_shift keys each, and request b has
+// ceil(lens[b] / 2^len_shift) of them.
 hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, int B, int H,
                         int Q, int D, int64_t n_max, int dtype, float scale, bool fill_pad,
                         float* scores, const GatherJob* pf, int pf_wgs, hipStream_t s,
                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
-                        int64_t* zero3 = nullptr);
+                        int64_t* zero3 = nullptr, int len_shift = 0);
 
 // In-place softmax of each score row over its valid keys; 0 past lens[b].
 hipError_t launch_softmax_rows(float* scores, const int32_t* lens, int B, int H, int Q,
@@ -59,8 +61,10 @@ struct FusedAttn {
   const void* vslot;
   const void* k_host;    // pinned [BH][n_max][D] (unused when k_dev is set)
   const void* v_host;
-  const void* k_dev;     // device keys [BH][n_max][D]: K rows read from here
+  const void* k_dev;     // device keys [BH][n_rows][D]: K rows read from here
                          // (only V rows travel from the host), or null
+  int64_t n_rows;        // rows per slab of the K/V copies
+  int chunk_shift;       // entries are chunks of 2^chunk_shift rows (0: rows)
   int D, dtype;
   float scale;
   float* out;            // [BH][D]
@@ -72,20 +76,22 @@ struct FusedAttn {
 // Top-k of each score row.  Plane j of slab bh is written at
 // (j == 0 ? out0 : out1) + bh * out_stride_bh.  book: bookkeeping of the
 // plane-0 rows (its pos / miss / counts outputs may each be null); attn:
-// the fused attention (needs book).
+// the fused attention (needs book).  len_shift > 0: the scores are of chunk
+// landmarks of 2^len_shift rows, ceil(lens[b] / 2^len_shift) per request.
 hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, int Q,
                        int64_t n_max, int k, int32_t* out0, int32_t* out1,
                        int64_t out_stride_bh, const TopkBook* book, const FusedAttn* attn,
-                       hipStream_t s);
+                       hipStream_t s, int len_shift = 0);
 
 // Row gather from pinned host memory.  Entry j < cnt[bh] (m if cnt is null)
-// of slab bh copies host row idx[bh*m + j] (zero row if out of range) to
-// destination row bh*dst_rows_per_bh + dst_row0 + j.  At most max_wgs
-// workgroups (0: a default for a standalone copy) keep rows in flight.
+// of slab bh copies the run of R = 2^run_shift host rows from row
+// R * idx[bh*m + j] (zero rows where out of range) to destination rows
+// bh*dst_rows_per_bh + dst_row0 + R*j onwards.  At most max_wgs workgroups
+// (0: a default for a standalone copy) keep rows in flight.
 hipError_t launch_gather(const void* k_host, const void* v_host, int64_t n_max, int row_bytes,
                          const int32_t* idx, int m, const int32_t* cnt, int BH, void* k_dst,
                          void* v_dst, int64_t dst_rows_per_bh, int dst_row0, int max_wgs,
-                         hipStream_t s);
+                         hipStream_t s, int run_shift = 0);
 
 size_t attn_workspace(int B, int H, int k, int D);
 
@@ -109,5 +115,11 @@ hipError_t launch_attn(const float* q, int64_t q_stride_bh, const void* k_rows,
                        hipStream_t s);
 
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+// Chunk landmarks: out[bh][e] (fp32, D wide, ceil(n_max / 2^chunk_shift)
+// rows per slab) = the mean of keys[bh][i] over the rows i of chunk e below
+// lens[b]; zero for a chunk with no such row.
+hipError_t launch_landmarks(const void* keys, const int32_t* lens, int B, int H, int D,
+                            int64_t n_max, int chunk_shift, int dtype, float* out, hipStream_t s);
 
 }  // namespace dd

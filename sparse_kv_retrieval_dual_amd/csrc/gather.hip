@@ -32,17 +32,19 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(GatherJob g) {
 hipError_t launch_gather(const void* k_host, const void* v_host, int64_t n_max, int row_bytes,
                          const int32_t* idx, int m, const int32_t* cnt, int BH, void* k_dst,
                          void* v_dst, int64_t dst_rows_per_bh, int dst_row0, int max_wgs,
-                         hipStream_t s) {
+                         hipStream_t s, int run_shift) {
   const int64_t total = (int64_t)BH * m;
   if (total == 0) return hipSuccess;
+  if ((total << run_shift) > kGatherMaxRows) return hipErrorInvalidValue;
   const int rpi = 64 / (row_bytes / 16);
   const int64_t rows_per_wg = (int64_t)rpi * kGatherUnroll * (kGatherThreads / 64);
-  int64_t grid = (total + rows_per_wg - 1) / rows_per_wg;
+  int64_t grid = ((total << run_shift) + rows_per_wg - 1) / rows_per_wg;
   const int cap = max_wgs > 0 ? max_wgs : kDefaultMaxWgs;
   if (grid > cap) grid = cap;
   const GatherJob g{static_cast<const uint8_t*>(k_host), static_cast<const uint8_t*>(v_host),
                     n_max, idx, m, cnt, total, static_cast<uint8_t*>(k_dst),
-                    static_cast<uint8_t*>(v_dst), dst_rows_per_bh, dst_row0};
+                    static_cast<uint8_t*>(v_dst), dst_rows_per_bh, dst_row0, run_shift,
+                    row_bytes};
   switch (row_bytes) {
     case 128:
       hipLaunchKernelGGL(k_gather<128>, dim3((unsigned)grid), dim3(kGatherThreads), 0, s, g);

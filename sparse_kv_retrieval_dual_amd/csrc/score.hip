@@ -47,20 +47,30 @@ template <typename T, int D, int Q>
 __global__ __launch_bounds__(kScoreWaves * 64) void k_score(
     const float* __restrict__ q, const T* __restrict__ keys, const int32_t* __restrict__ lens,
     int BH, int H, int64_t n_max, int tiles, float scale, float* __restrict__ scores,
-    int fill_pad, GatherJob pf, int pf_wgs, int64_t* __restrict__ zero3) {
+    int fill_pad, GatherJob pf, int pf_wgs, int64_t* __restrict__ zero3, int len_shift) {
   using S = ScoreShape<T, D, Q>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   if (zero3 != nullptr && (int)blockIdx.x == pf_wgs && threadIdx.x < 3) zero3[threadIdx.x] = 0;
   if (tiles == 0) return;
   if ((int)blockIdx.x < pf_wgs) {
-    gather_rows<D * (int)sizeof(T)>(pf, (int64_t)blockIdx.x * kScoreWaves + wave,
-                                    (int64_t)pf_wgs * kScoreWaves);
+    // The gathered rows are K/V rows: the scored rows' size, or half of it
+    // when fp32 chunk landmarks are scored for bf16 K/V rows.
+    constexpr int RB = D * (int)sizeof(T);
+    const int64_t gw = (int64_t)blockIdx.x * kScoreWaves + wave;
+    const int64_t nw = (int64_t)pf_wgs * kScoreWaves;
+    if constexpr (sizeof(T) == 4) {
+      if (pf.row_bytes == RB / 2) {
+        gather_rows<RB / 2>(pf, gw, nw);
+        return;
+      }
+    }
+    gather_rows<RB>(pf, gw, nw);
     return;
   }
   int bh, tile;
   xcd_tile_map((int)blockIdx.x - pf_wgs, tiles, BH, bh, tile);
-  const int64_t n = clamp_len(lens[bh / H], n_max);
+  const int64_t n = chunk_len(lens[bh / H], len_shift, n_max);
   const int64_t tile0 = (int64_t)tile * S::TILE;
   if (tile0 >= n && !fill_pad) return;
 
@@ -167,6 +177,7 @@ struct ScoreLaunch {
   hipStream_t s;
   hipEvent_t ev_start, ev_stop;
   int64_t* zero3;
+  int len_shift;
 };
 
 template <typename T, int D, int Q>
@@ -182,11 +193,12 @@ hipError_t launch_score_t(const ScoreLaunch& a) {
     hipExtLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), 0,
                           a.s, a.ev_start, a.ev_stop, 0, a.q, static_cast<const T*>(a.keys),
                           a.lens, BH, a.H, a.n_max, (int)tiles, a.scale, a.scores,
-                          a.fill_pad ? 1 : 0, a.pf, a.pf_wgs, a.zero3);
+                          a.fill_pad ? 1 : 0, a.pf, a.pf_wgs, a.zero3, a.len_shift);
   } else {
     hipLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), 0, a.s,
                        a.q, static_cast<const T*>(a.keys), a.lens, BH, a.H, a.n_max, (int)tiles,
-                       a.scale, a.scores, a.fill_pad ? 1 : 0, a.pf, a.pf_wgs, a.zero3);
+                       a.scale, a.scores, a.fill_pad ? 1 : 0, a.pf, a.pf_wgs, a.zero3,
+                       a.len_shift);
   }
   return hipGetLastError();
 }
@@ -202,10 +214,17 @@ hipError_t launch_score_q(int Q, const ScoreLaunch& a) {
 hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, int B, int H,
                         int Q, int D, int64_t n_max, int dtype, float scale, bool fill_pad,
                         float* scores, const GatherJob* pf, int pf_wgs, hipStream_t s,
-                        hipEvent_t ev_start, hipEvent_t ev_stop, int64_t* zero3) {
+                        hipEvent_t ev_start, hipEvent_t ev_stop, int64_t* zero3,
+                        int len_shift) {
   ScoreLaunch a{q, keys, lens, B, H, n_max, scale, fill_pad, scores, GatherJob{}, 0, s,
-                ev_start, ev_stop, zero3};
+                ev_start, ev_stop, zero3, len_shift};
   if (pf != nullptr && pf->total > 0 && pf_wgs > 0) {
+    // The prefetched K/V rows are the scored rows' size, or (fp32 landmarks
+    // of bf16 rows) half of it.
+    const int rb = D * (dtype == kBF16 ? 2 : 4);
+    if (pf->row_bytes != rb && !(dtype == kF32 && pf->row_bytes == rb / 2))
+      return hipErrorInvalidValue;
+    if ((pf->total << pf->run_shift) > kGatherMaxRows) return hipErrorInvalidValue;
     a.pf = *pf;
     a.pf_wgs = (pf_wgs + 7) & ~7;  // keeps the scoring tiles' XCD placement
   }

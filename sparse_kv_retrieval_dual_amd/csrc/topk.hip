@@ -690,23 +690,37 @@ __device__ __forceinline__ int radix_select(const float* __restrict__ row, int n
 // Attention of the current query over its own selection (the layer step's
 // last stage), done by the workgroup of each bookkeeping row right after its
 // emit: slot rows and entry rows come from LDS, chunks of 128 entries as in
-// the attention kernel, chunk partials merged the same way.
+// the attention kernel, chunk partials merged the same way.  With selection
+// by chunk landmarks (cs > 0) each of the ks selected entries stands for the
+// 2^cs consecutive rows of its chunk, rows past the request's length left
+// out; the slot holds them at 2^cs times the entry's slot position.
 template <typename T, int D>
-__device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, int k,
-                                                  int64_t n_max, const int32_t* lpos,
+__device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, int ks,
+                                                  int32_t len, const int32_t* lpos,
                                                   const int32_t* lcur, float* scratch) {
   AttnLds<D>& lds = *reinterpret_cast<AttnLds<D>*>(scratch);
   float* part = scratch + (sizeof(AttnLds<D>) + 15) / 16 * 4;
+  const int cs = fa.chunk_shift;
+  const int k = ks << cs;  // rows attended (at most)
+  const int64_t n_rows = fa.n_rows;
+  const int64_t nv = clamp_len(len, n_rows);
   const int64_t slab = (int64_t)bh * 2 * k * D;
-  const int64_t hslab = (int64_t)bh * n_max * D;
+  const int64_t hslab = (int64_t)bh * n_rows * D;
   const bool kdev = fa.k_dev != nullptr;
   const AttnRows<T> R{static_cast<const T*>(fa.kslot) + slab, static_cast<const T*>(fa.vslot) + slab,
                       kdev ? nullptr : static_cast<const T*>(fa.k_host) + hslab,
                       static_cast<const T*>(fa.v_host) + hslab,
-                      kdev ? static_cast<const T*>(fa.k_dev) + hslab : nullptr, 2 * k, k, n_max};
+                      kdev ? static_cast<const T*>(fa.k_dev) + hslab : nullptr, 2 * k, k, n_rows};
+  const int cmask = (1 << cs) - 1;
   auto entry = [&](int j, int& r, int& c) {
-    r = lpos[j];
-    c = lcur[j];
+    const int e = j >> cs;
+    const int i = j & cmask;
+    const int pe = lpos[e];
+    const int ce = lcur[e];
+    const int64_t row = ((int64_t)ce << cs) + i;
+    const bool ok = ce >= 0 && pe >= 0 && row < nv;
+    r = ok ? (pe << cs) + i : -1;
+    c = ok ? (int)row : -1;
   };
   const int chunks = (k + kAttnChunk - 1) / kAttnChunk;
   const float* qrow = fa.q + (int64_t)bh * 2 * D;
@@ -737,15 +751,15 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
   }
 }
 
-__device__ __forceinline__ void fused_attention(const FusedAttn& fa, int bh, int k, int64_t n_max,
+__device__ __forceinline__ void fused_attention(const FusedAttn& fa, int bh, int ks, int32_t len,
                                                 const int32_t* lpos, const int32_t* lcur,
                                                 float* scratch) {
   if (fa.dtype == kBF16) {
-    if (fa.D == 128) fused_attention_t<uint16_t, 128>(fa, bh, k, n_max, lpos, lcur, scratch);
-    else fused_attention_t<uint16_t, 64>(fa, bh, k, n_max, lpos, lcur, scratch);
+    if (fa.D == 128) fused_attention_t<uint16_t, 128>(fa, bh, ks, len, lpos, lcur, scratch);
+    else fused_attention_t<uint16_t, 64>(fa, bh, ks, len, lpos, lcur, scratch);
   } else {
-    if (fa.D == 128) fused_attention_t<float, 128>(fa, bh, k, n_max, lpos, lcur, scratch);
-    else fused_attention_t<float, 64>(fa, bh, k, n_max, lpos, lcur, scratch);
+    if (fa.D == 128) fused_attention_t<float, 128>(fa, bh, ks, len, lpos, lcur, scratch);
+    else fused_attention_t<float, 64>(fa, bh, ks, len, lpos, lcur, scratch);
   }
 }
 
@@ -754,7 +768,7 @@ __global__ __launch_bounds__(kNT) void k_topk(
     const float* __restrict__ scores, const int32_t* __restrict__ lens, int H, int Q, int BH,
     int64_t n_max, int k, int32_t* __restrict__ out0, int32_t* __restrict__ out1,
     int64_t out_stride, int book_on, const int32_t* __restrict__ pred, int32_t* __restrict__ pos,
-    int32_t* __restrict__ miss, int32_t* __restrict__ counts, FusedAttn fa) {
+    int32_t* __restrict__ miss, int32_t* __restrict__ counts, FusedAttn fa, int len_shift) {
   extern __shared__ uint32_t smem[];
   const int tid = threadIdx.x;
   int bh, j;
@@ -777,7 +791,7 @@ __global__ __launch_bounds__(kNT) void k_topk(
     pv[r] = (pred_row != nullptr && p < k) ? pred_row[p] : -1;
   }
   clear(smem + kLHist, kBins);
-  const int n = (int)clamp_len(lens[bh / H], n_max);
+  const int n = (int)chunk_len(lens[bh / H], len_shift, n_max);
   int misses = 0, fetchable = 0;
 
   if (n <= k) {
@@ -837,7 +851,7 @@ __global__ __launch_bounds__(kNT) void k_topk(
               (unsigned long long)(fetchable + misses));
   }
   __syncthreads();  // every entry's slot row and row index are in LDS
-  fused_attention(fa, bh, k, n_max, sk.lpos, sk.lcur, reinterpret_cast<float*>(smem + kLIdx));
+  fused_attention(fa, bh, k, lens[bh / H], sk.lpos, sk.lcur, reinterpret_cast<float*>(smem + kLIdx));
 }
 
 template <bool CACHED>
@@ -860,7 +874,7 @@ TopkKernel<CACHED> pick_kernel(int g) {
 hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, int Q,
                        int64_t n_max, int k, int32_t* out0, int32_t* out1,
                        int64_t out_stride_bh, const TopkBook* book, const FusedAttn* attn,
-                       hipStream_t s) {
+                       hipStream_t s, int len_shift) {
   const int BH = B * H;
   if (BH == 0) return hipSuccess;
   const DeviceInfo& di = device_info();
@@ -891,11 +905,11 @@ hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, i
   if (cached) {
     hipLaunchKernelGGL(pick_kernel<true>(g), dim3(BH * Q), dim3(kNT), shmem, s, scores, lens, H, Q,
                        BH, n_max, k, out0, out1, out_stride_bh, book_on, pred, pos, miss, counts,
-                       fa);
+                       fa, len_shift);
   } else {
     hipLaunchKernelGGL(pick_kernel<false>(g), dim3(BH * Q), dim3(kNT), shmem, s, scores, lens, H,
                        Q, BH, n_max, k, out0, out1, out_stride_bh, book_on, pred, pos, miss, counts,
-                       fa);
+                       fa, len_shift);
   }
   return hipGetLastError();
 }

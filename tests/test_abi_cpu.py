@@ -52,6 +52,8 @@ def test_buffer_sizes(lib):
 @pytest.mark.parametrize("call,code", [
     ("score_bad_D", 2), ("score_bad_Q", 2), ("score_bad_dtype", 2), ("topk_k0", 2),
     ("topk_k_too_big", 2), ("gather_null_idx", 1), ("attn_stride", 1), ("gather_neg_m", 1),
+    ("landmarks_chunk3", 1), ("landmarks_chunk128", 1), ("gather_chunks_chunk0", 1),
+    ("gather_chunks_null_idx", 1),
 ])
 def test_argument_errors_are_reported(lib, call, code):
     z = ctypes.c_void_p(16)  # never dereferenced: validation fails first
@@ -69,6 +71,14 @@ def test_argument_errors_are_reported(lib, call, code):
         rc = lib.dd_gather(z, z, None, None, 1, 1, 4, 128, 10, 1, z, z, None)
     elif call == "gather_neg_m":
         rc = lib.dd_gather(z, z, z, None, 1, 1, -1, 128, 10, 1, z, z, None)
+    elif call == "landmarks_chunk3":
+        rc = lib.dd_landmarks(z, z, 1, 1, 128, 64, 3, 1, z, None)
+    elif call == "landmarks_chunk128":
+        rc = lib.dd_landmarks(z, z, 1, 1, 128, 64, 128, 1, z, None)
+    elif call == "gather_chunks_chunk0":
+        rc = lib.dd_gather_chunks(z, z, z, None, 1, 1, 4, 0, 128, 64, 1, z, z, None)
+    elif call == "gather_chunks_null_idx":
+        rc = lib.dd_gather_chunks(z, z, None, None, 1, 1, 4, 8, 128, 64, 1, z, z, None)
     else:
         rc = lib.dd_sparse_attn(z, 8, z, z, None, None, 1, 1, 4, 4, 128, 1, 0.0, z, None, None, 0, None)
     assert rc == code
@@ -80,3 +90,5 @@ def test_empty_shapes_are_no_ops(lib):
     assert lib.dd_score(z, z, z, 0, 8, 2, 128, 10, 1, 0.0, 0, z, None) == 0
     assert lib.dd_topk(z, z, 1, 0, 2, 10, 4, z, None) == 0
     assert lib.dd_gather(z, z, z, None, 1, 1, 0, 128, 10, 1, z, z, None) == 0
+    assert lib.dd_gather_chunks(z, z, z, None, 1, 1, 0, 8, 128, 10, 1, z, z, None) == 0
+    assert lib.dd_landmarks(z, z, 0, 4, 128, 10, 8, 1, z, None) == 0

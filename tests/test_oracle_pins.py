@@ -426,6 +426,96 @@ def test_planted_structure(name, kw, relation):
                 assert chosen <= planted
 
 
+# --------------------------------------------------------------------------- chunk landmarks
+def test_landmarks_of_constant_chunks_and_partial_tail():
+    """A chunk of equal keys has that key as its landmark, the last, partial
+    chunk included (its mean is over its valid rows, not over the chunk
+    size); chunks with no valid row are zero and rows past the length never
+    count (they hold +-1e30 here)."""
+    rng = np.random.default_rng(3)
+    B, H, n_max, D, c = 2, 3, 40, 8, 8
+    lens = np.array([37, 5])
+    base = rng.standard_normal((B, H, n_max // c, D)).astype(np.float32)
+    keys = np.repeat(base, c, axis=2).copy()
+    keys[0, :, 37:] = 1e30
+    keys[1, :, 5:] = -1e30
+    lm = oracle.landmarks(keys, lens, c, oracle.F32)
+    assert lm.shape == (B, H, 5, D)
+    for b in range(B):
+        nc = -(-int(lens[b]) // c)
+        np.testing.assert_array_equal(lm[b, :, :nc], base[b, :, :nc].astype(np.float64))
+        assert np.all(lm[b, :, nc:] == 0)
+
+
+def test_landmarks_with_chunk_one_are_the_keys():
+    w = gen.workload("llama7b_32k_layer").scaled(H=2, n_max=300)
+    lay, kh, _, lens = _layer(w)
+    lm = oracle.landmarks(kh, lens, 1, w.dtype)
+    n = int(lens[0])
+    np.testing.assert_array_equal(lm[0, :, :n], oracle.upcast(kh[0, :, :n], w.dtype))
+
+
+def test_landmarks_weighted_by_counts_sum_to_the_keys():
+    """sum over chunks of (valid rows) x landmark = the sum of all valid keys."""
+    w = gen.workload("hiconc_64").scaled(B=3, H=2, n_max=700, len_lo=50, len_hi=700)
+    lay, kh, _, lens = _layer(w)
+    c = 16
+    lm = oracle.landmarks(kh, lens, c, w.dtype)
+    for b in range(w.B):
+        n = int(lens[b])
+        cnt = np.array([min(c, n - e * c) for e in range(-(-n // c))], dtype=np.float64)
+        for h in range(w.H):
+            kf = oracle.upcast(kh[b, h, :n], w.dtype)
+            for d in range(0, w.D, 37):
+                want = math.fsum(kf[:, d].tolist())
+                got = math.fsum((cnt * lm[b, h, :len(cnt), d]).tolist())
+                assert abs(got - want) <= 1e-9 * (1 + math.fsum(np.abs(kf[:, d]).tolist()))
+
+
+def test_chunk_step_with_chunk_one_is_the_per_key_step():
+    for name, kw in (("tiny", {}), ("hiconc_64", dict(B=2, H=2, n_max=600, len_lo=100, len_hi=600, k=64))):
+        w = gen.workload(name).scaled(**kw)
+        lay, kh, vh, lens = _layer(w)
+        q = lay["q"].numpy()
+        a = oracle.layer_step(q, kh, kh, vh, lens, w.k, w.dtype)
+        b = oracle.layer_step(q, kh, kh, vh, lens, w.k, w.dtype, chunk=1)
+        for key in ("cur", "spec", "out", "lse", "stats"):
+            np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_chunk_selection_and_attention_closed_form():
+    """Keys are zero except the partial last chunk (rows 12 and 13 of 14,
+    chunk size 4), whose rows are 2q: its landmark scores 2|q|^2/sqrt(D) = 1
+    and every other chunk 0.  With k = 8 (two chunks) the current query takes
+    chunk 3 and, among the tied zeros, chunk 0; the speculated query -q takes
+    chunks 0 and 1.  Attention over rows 0-3 (logit 0) and 12-13 (logit 1)
+    with V row i = i in column 0 gives (0+1+2+3 + e(12+13)) / (4 + 2e)."""
+    D, c, n = 4, 4, 14
+    qv = np.array([1.0, 0.0, 0.0, 0.0], dtype=np.float32)
+    q = np.stack([qv, -qv])[None, None]                      # [1][1][2][D]
+    keys = np.zeros((1, 1, 16, D), dtype=np.float32)
+    keys[0, 0, 12:14] = 2 * qv
+    keys[0, 0, 14:] = 99.0                                   # padding
+    vals = np.zeros((1, 1, 16, D), dtype=np.float32)
+    vals[0, 0, :, 0] = np.arange(16)
+    vals[0, 0, :, 1] = 1.0
+    lens = np.array([n])
+    r = oracle.layer_step(q, keys, keys, vals, lens, 8, oracle.F32, chunk=c)
+    assert r["cur"].tolist() == [[[0, 3]]]
+    assert r["spec"].tolist() == [[[0, 1]]]
+    assert r["rows"][0, 0].tolist() == [0, 1, 2, 3, 12, 13, -1, -1]
+    e = math.e
+    assert abs(r["out"][0, 0, 0] - (6 + 25 * e) / (4 + 2 * e)) < 1e-12
+    assert abs(r["out"][0, 0, 1] - 1.0) < 1e-12
+    assert abs(r["lse"][0, 0] - math.log(4 + 2 * e)) < 1e-12
+    # prediction = chunks {0, 1}: chunk 0 hits (slot rows 0..3), chunk 3 misses
+    r2 = oracle.layer_step(q, keys, keys, vals, lens, 8, oracle.F32, chunk=c,
+                           pred=np.array([[[0, 1]]], dtype=np.int32))
+    assert r2["stats"].tolist() == [1, 1, 3]
+    assert r2["pos"].tolist() == [[[0, 2]]]
+    np.testing.assert_array_equal(r2["out"], r["out"])
+
+
 # --------------------------------------------------------------------------- comparators
 def test_tie_band_comparator_accepts_swaps_and_rejects_errors():
     logits = np.array([[5.0, 3.0, 3.0 + 5e-4, 1.0, 3.0 - 2e-3]])
