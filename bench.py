@@ -107,6 +107,8 @@ def main():
     ap.add_argument("--prefetch", default="auto", choices=["auto", "side", "fused"])
     ap.add_argument("--k-rows", default="device", choices=["device", "host"],
                     help="where attention reads the selected K rows")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="select by landmarks of chunks of this many keys (0: every key)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -141,8 +143,13 @@ def main():
 
     ctx = dd.Context(ring_slots=args.ring, gather_cus=args.gather_cus,
                      prefetch_wgs=args.prefetch_wgs, prefetch=args.prefetch, k_rows=args.k_rows)
-    cur = [torch.empty(B, H, k, dtype=torch.int32, device=dev)]
-    spec = [torch.empty(B, H, k, dtype=torch.int32, device=dev)]
+    chunk = args.chunk if args.chunk > 1 else 1
+    ks = k // chunk                                      # entries selected per query
+    # Landmarks are built once per cache (untimed here, measured below), one
+    # per key copy so that they rotate like the keys.
+    lm_copies = [dd.landmarks(kc, lens, chunk) for kc in k_copies] if chunk > 1 else None
+    cur = [torch.empty(B, H, ks, dtype=torch.int32, device=dev)]
+    spec = [torch.empty(B, H, ks, dtype=torch.int32, device=dev)]
     out = [torch.empty(B, H, D, dtype=torch.float32, device=dev)]
     lse = [torch.empty(B, H, dtype=torch.float32, device=dev)]
     stats = torch.zeros(1, 3, dtype=torch.int64, device=dev)
@@ -152,7 +159,8 @@ def main():
     def step(i, pred, timing=None):
         ctx.layer_step([q], [k_copies[i % len(k_copies)]], [kh], [vh], lens, k, pred=pred,
                        cur=cur, spec=spec, out=out, lse=lse, stats=stats, ring=ring, ws=ws,
-                       timing=timing)
+                       timing=timing, chunk=chunk if chunk > 1 else 0,
+                       landmarks=[lm_copies[i % len(lm_copies)]] if chunk > 1 else None)
 
     # Untimed first step without a prediction; its speculated set predicts the next.
     step(0, None)
@@ -236,19 +244,40 @@ def main():
     t_step_instr = avg(0, 4)
     st = stats[0].cpu().tolist()
     misses, hits, fetched = st
-    valid = int(torch.clamp(lens, max=k).sum().item()) * H
+    n_sel = int(((lens + chunk - 1) // chunk).sum().item()) * H   # rows scored: keys or landmarks
+    valid = int(torch.clamp((lens + chunk - 1) // chunk, max=ks).sum().item()) * H  # entries selected
 
-    # Algorithmic bytes of the scorer per launch: every valid key row once
-    # (both queries), plus the two fp32 logits written per key.
-    score_bytes = n_keys * D * eb + n_keys * 2 * 4
+    # Algorithmic bytes of the scorer per launch: every valid key row (or
+    # fp32 landmark row) once (both queries), plus the two fp32 logits
+    # written per row.
+    row_b = D * eb if chunk == 1 else D * 4
+    score_bytes = n_sel * row_b + n_sel * 2 * 4
     score_gbps = score_bytes / (t_score * 1e-3) / 1e9
     planes = 1 if args.k_rows == "device" else 2    # V rows only, or K and V
-    prefetch_bytes = valid * planes * D * eb         # k rows per (b, h)
+    prefetch_bytes = valid * chunk * planes * D * eb     # k rows per (b, h)
     # The prefetch runs on the side stream (own events) or inside the scoring
     # kernel (then its rate is bounded below by that kernel's duration).
     t_pf = t_prefetch if t_prefetch is not None else t_score
     prefetch_gbps = prefetch_bytes / (t_pf * 1e-3) / 1e9
-    miss_bytes = misses * planes * D * eb
+    miss_bytes = misses * chunk * planes * D * eb
+
+    # The landmark build (once per cache, not per step), over the same copies.
+    lm_info = None
+    if chunk > 1:
+        ev_lm = EventSet(2)
+        for kc, lm in zip(k_copies, lm_copies):
+            dd.landmarks(kc, lens, chunk, out=lm)
+        reps = 4 * len(k_copies)
+        ev_lm.record(0)
+        for i in range(reps):
+            dd.landmarks(k_copies[i % len(k_copies)], lens, chunk, out=lm_copies[i % len(lm_copies)])
+        ev_lm.record(1)
+        torch.cuda.synchronize()
+        t_lm = ev_lm.elapsed_ms(0, 1) / reps
+        lm_bytes = n_keys * D * eb + B * H * lm_copies[0].shape[2] * D * 4
+        lm_info = {"us": t_lm * 1e3, "algorithmic_bytes": lm_bytes,
+                   "GBps": lm_bytes / (t_lm * 1e-3) / 1e9,
+                   "frac": lm_bytes / (t_lm * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
     # Reference rates measured in the same process.
     big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -278,7 +307,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, lay, args.cpu_seconds)
 
-    traffic = _counter_traffic("score", SCORE_SOURCES, w.name)
+    traffic = _counter_traffic("score", SCORE_SOURCES, w.name) if chunk == 1 else None
     result = {
         "metric": METRIC,
         "value": n_keys / (ms_per_step * 1e-3),
@@ -295,7 +324,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": D, "context": w.n_max,
                    "top_k": k, "queries": 2, "kv_dtype": w.dtype, "accumulate": "f32",
                    "ring_slots": args.ring, "hbm_key_copies": len(k_copies),
-                   "k_rows": args.k_rows},
+                   "k_rows": args.k_rows, "chunk": chunk},
         "roofline": {"bound": "hbm", "achieved": score_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": score_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic,
@@ -317,8 +346,11 @@ def main():
         "h2d_memcpy_GBps": h2d_gbps,
         "hbm_stream_copy_GBps": hbm_copy,
         "prediction": {"misses": misses, "hits": hits, "rows_fetched": fetched,
-                       "recall": hits / max(valid, 1), "miss_bytes": miss_bytes},
+                       "recall": hits / max(valid, 1), "miss_bytes": miss_bytes,
+                       "unit": "keys" if chunk == 1 else f"chunks of {chunk} keys"},
     }
+    if lm_info is not None:
+        result["landmarks_build"] = lm_info
     ctx.close()
     print(json.dumps(result))
 
