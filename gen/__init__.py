@@ -8,6 +8,7 @@ from .workloads import (  # noqa: F401
     Workload,
     workload,
     make_layer,
+    decode_step_inputs,
     layer_seed,
     request_lens,
     tie_scores,

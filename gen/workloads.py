@@ -178,6 +178,31 @@ def make_layer(w: Workload, layer: int, device="cpu", k_out=None, v_out=None):
     }
 
 
+def decode_step_inputs(w: Workload, layer: int, step: int, q_prev: torch.Tensor, device="cpu"):
+    """Inputs of decode step `step` (1, 2, ...) of one layer after the drawn
+    layer (make_layer is step 0).
+
+    The token decoded now is the one the previous step speculated, up to the
+    same imperfection the workload gives speculation: q_cur = rho * q_spec(prev)
+    + rho_c * z, and the new speculated query is rho * q_cur + rho_c * z'
+    (arXiv page, section 1: the speculated token guides the next step's
+    retrieval).  The new token's key and value rows are N(0, 1) in the
+    storage type.  q_prev: fp32 [B][H][2][D] of the previous step.
+    Returns (q [B][H][2][D] fp32, new_k [B][H][D], new_v [B][H][D]).
+    """
+    device = torch.device(device)
+    g = torch.Generator(device=device).manual_seed(layer_seed(w, layer) * 7919 + step)
+    B, H, D = w.B, w.H, w.D
+    z = torch.randn(B, H, D, generator=g, device=device, dtype=torch.float32)
+    z2 = torch.randn(B, H, D, generator=g, device=device, dtype=torch.float32)
+    q_cur = w.rho * q_prev[:, :, 1].to(device) + w.rho_c * z
+    q_spec = w.rho * q_cur + w.rho_c * z2
+    q = torch.stack([q_cur, q_spec], dim=2).contiguous()
+    new_k = torch.randn(B, H, D, generator=g, device=device, dtype=torch.float32).to(w.torch_dtype)
+    new_v = torch.randn(B, H, D, generator=g, device=device, dtype=torch.float32).to(w.torch_dtype)
+    return q, new_k.contiguous(), new_v.contiguous()
+
+
 def tie_scores(rows: int, n: int, seed: int, nvalues: int = 5, device="cpu") -> torch.Tensor:
     """fp32 score rows drawn from a small value set, so that exact ties occur.
 

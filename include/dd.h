@@ -164,6 +164,22 @@ DD_API int dd_landmarks(const void* keys, const int32_t* lens, int B, int H, int
                         int64_t n_max, int chunk, int dtype, float* landmarks,
                         hipStream_t stream);
 
+/* KV append (arXiv page, section 2.1: each decoding step computes the new
+ * token's key and value and appends them to the cache).  For every (b, h)
+ * the new rows new_k[b][h], new_v[b][h] (device, [B][H][D], dtype) are
+ * written to row lens[b] of k_dev (the device keys that are scored), k_host
+ * and v_host (the pinned host cache), all [B][H][n_max][D].  lens_out (or
+ * NULL) receives lens[b] + 1; it must not alias lens, since every (b, h)
+ * reads lens[b].  A request with lens[b] outside [0, n_max) is left as it is
+ * (lens_out[b] = lens[b]).  landmarks (or NULL): the chunk landmarks of the
+ * cache (chunk as in dd_landmarks); the landmark of the chunk holding the new
+ * row is recomputed, with the same arithmetic as dd_landmarks, so it equals
+ * a rebuild of the grown cache bit for bit. */
+DD_API int dd_kv_append(void* k_dev, void* k_host, void* v_host, const void* new_k,
+                        const void* new_v, const int32_t* lens, int32_t* lens_out, int B, int H,
+                        int D, int64_t n_max, int dtype, int chunk, float* landmarks,
+                        hipStream_t stream);
+
 DD_API size_t dd_attn_workspace(int B, int H, int k, int D);
 
 /* Decode attention over gathered rows only (Figure 1 "Attention" on the

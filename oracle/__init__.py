@@ -7,6 +7,7 @@ from .dd_oracle import (  # noqa: F401
     BF16,
     F32,
     F64,
+    append_rows,
     attend_rows,
     attention_weights,
     bookkeeping,

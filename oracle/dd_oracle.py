@@ -27,6 +27,9 @@ What it computes, and where the pages define it:
 * Sparse attention.  Decode attention of the current query over only the
   selected rows ("Attention" box of Figure 1), written here as dense
   attention with every unselected logit masked to -inf.
+* KV append.  Each decode step appends the new token's key and value rows to
+  the cache (arXiv page, section 2.1), so a multi-step loop grows every
+  request by one row per step.
 * Chunk landmarks.  Selection may instead score compressed landmarks of
   chunks of adjacent entries and retrieve whole chunks (arXiv page, section
   2.2, on ShadowKV); a landmark is read as the mean key of its chunk.
@@ -300,6 +303,24 @@ def landmarks(keys: np.ndarray, lens: np.ndarray, chunk: int, dtype: str) -> np.
             lo, hi = e * chunk, min((e + 1) * chunk, n)
             out[b, :, e] = kf[:, lo:hi].sum(axis=1) / (hi - lo)
     return out
+
+
+def append_rows(cache: np.ndarray, lens: np.ndarray, new_rows: np.ndarray):
+    """The cache after appending one row per (b, h), and the new lengths.
+
+    cache: stored [B][H][n_max][D]; new_rows: stored [B][H][D].  Row lens[b]
+    of request b becomes new_rows[b] and its length grows by one; a request
+    whose length is outside [0, n_max) is left as it is.
+    """
+    out = np.array(cache, copy=True)
+    new_lens = np.array(lens, dtype=np.int64, copy=True)
+    n_max = cache.shape[2]
+    for b in range(cache.shape[0]):
+        n = int(lens[b])
+        if 0 <= n < n_max:
+            out[b, :, n] = new_rows[b]
+            new_lens[b] = n + 1
+    return out, new_lens
 
 
 def chunk_rows(sel: np.ndarray, lens: np.ndarray, chunk: int) -> np.ndarray:

@@ -9,10 +9,12 @@ import torch  # noqa: F401  (must precede loading libdd.so)
 from . import _lib
 from .api import (  # noqa: F401
     Context,
+    Decoder,
     attn_workspace_bytes,
     gather,
     gather_chunks,
     host_empty,
+    kv_append,
     kv_dtype,
     landmarks,
     layer_step_workspace_bytes,

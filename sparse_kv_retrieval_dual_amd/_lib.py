@@ -72,6 +72,7 @@ _SIGNATURES = {
     "dd_gather_chunks": (c_int, [P, P, P, P, c_int, c_int, c_int, c_int, c_int, c_int64, c_int,
                                  P, P, P]),
     "dd_landmarks": (c_int, [P, P, c_int, c_int, c_int, c_int64, c_int, c_int, P, P]),
+    "dd_kv_append": (c_int, [P, P, P, P, P, P, P, c_int, c_int, c_int, c_int64, c_int, c_int, P, P]),
 }
 
 _lib = None

@@ -179,6 +179,32 @@ def landmarks(keys, lens, chunk: int, out=None, stream=None):
     return out
 
 
+def kv_append(k_dev, k_host, v_host, new_k, new_v, lens, lens_out=None, chunk: int = 0,
+              landmarks=None, stream=None):
+    """dd_kv_append: the new token's K/V rows ([B][H][D], device) at row lens[b]."""
+    _dev(k_dev, "k_dev"), _dev(new_k, "new_k"), _dev(new_v, "new_v"), _dev(lens, "lens")
+    B, H, n_max, D = k_dev.shape
+    dt = kv_dtype(k_dev)
+    for t, name in ((k_host, "k_host"), (v_host, "v_host")):
+        _need(not t.is_cuda and t.is_contiguous() and t.shape == k_dev.shape
+              and t.dtype == k_dev.dtype, f"{name} must be a contiguous host tensor like k_dev")
+    for t, name in ((new_k, "new_k"), (new_v, "new_v")):
+        _need(t.shape == (B, H, D) and t.dtype == k_dev.dtype and t.is_contiguous(),
+              f"{name} must be [B][H][D] of the cache dtype")
+    _need(lens.dtype == torch.int32 and lens.numel() == B, "lens must be int32 [B]")
+    if lens_out is not None:
+        _dev(lens_out, "lens_out")
+        _need(lens_out.dtype == torch.int32 and lens_out.numel() == B, "lens_out must be int32 [B]")
+    if landmarks is not None:
+        _dev(landmarks, "landmarks")
+        _need(landmarks.shape == (B, H, (n_max + chunk - 1) // chunk, D)
+              and landmarks.dtype == torch.float32, "landmarks must be fp32 [B][H][ceil(n_max/chunk)][D]")
+    L.check(_lib().dd_kv_append(_p(k_dev), _p(k_host), _p(v_host), _p(new_k), _p(new_v), _p(lens),
+                                _p(lens_out), B, H, D, n_max, dt, int(chunk) if landmarks is not None else 0,
+                                _p(landmarks), _stream(stream)))
+    return lens_out
+
+
 def attn_workspace_bytes(B: int, H: int, k: int, D: int) -> int:
     return int(_lib().dd_attn_workspace(B, H, k, D))
 
@@ -362,3 +388,50 @@ class Context:
         )
         L.check(_lib().dd_layer_step(self._h, ctypes.byref(a)))
         return {"cur": cur, "spec": spec, "out": out, "lse": lse, "stats": stats}
+
+
+class Decoder:
+    """A steady-state decode loop over the layer step (several real steps).
+
+    Each step appends the new token's K/V rows of every layer (dd_kv_append,
+    also updating chunk landmarks), then runs dd_layer_step for all layers
+    with the previous step's speculated sets as the prediction, so the
+    prediction is carried across real steps.  The caller owns the caches:
+    per layer, device keys k_dev[l] and pinned host k_host[l] / v_host[l] of
+    [B][H][n_max][D], with room to grow; lens (int32 [B], device) is the
+    current length, and the class keeps its own copy.
+    """
+
+    def __init__(self, ctx: Context, k_dev, k_host, v_host, lens, k: int, chunk: int = 0):
+        self.ctx = ctx
+        self.k_dev, self.k_host, self.v_host = list(k_dev), list(k_host), list(v_host)
+        self.k = int(k)
+        self.chunk = int(chunk) if chunk and chunk > 1 else 0
+        self.L = len(self.k_dev)
+        self._lens = [lens.clone(), torch.empty_like(lens)]
+        self._cur = 0
+        self.landmarks = None
+        if self.chunk:
+            self.landmarks = [landmarks(kd, self._lens[0], self.chunk) for kd in self.k_dev]
+        self.pred = None
+        self.history = []  # per step: stats [L][3] (device)
+
+    @property
+    def lens(self):
+        return self._lens[self._cur]
+
+    def step(self, q, new_k, new_v, stream=None):
+        """q[l] fp32 [B][H][2][D] (current, speculated); new_k[l] / new_v[l] [B][H][D]."""
+        src, dst = self._lens[self._cur], self._lens[1 - self._cur]
+        for l in range(self.L):
+            kv_append(self.k_dev[l], self.k_host[l], self.v_host[l], new_k[l], new_v[l], src,
+                      lens_out=dst if l == self.L - 1 else None, chunk=self.chunk,
+                      landmarks=None if self.landmarks is None else self.landmarks[l],
+                      stream=stream)
+        self._cur = 1 - self._cur
+        res = self.ctx.layer_step(list(q), self.k_dev, self.k_host, self.v_host, self.lens, self.k,
+                                  pred=self.pred, stream=stream, chunk=self.chunk,
+                                  landmarks=self.landmarks)
+        self.pred = [s.clone() for s in res["spec"]]
+        self.history.append(res["stats"].clone())
+        return res

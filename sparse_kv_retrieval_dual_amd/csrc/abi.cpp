@@ -237,6 +237,30 @@ DD_API int dd_landmarks(const void* keys, const int32_t* lens, int B, int H, int
   return DD_OK;
 }
 
+DD_API int dd_kv_append(void* k_dev, void* k_host, void* v_host, const void* new_k,
+                        const void* new_v, const int32_t* lens, int32_t* lens_out, int B, int H,
+                        int D, int64_t n_max, int dtype, int chunk, float* landmarks,
+                        hipStream_t stream) {
+  int rc = check_shape(B, H, D, n_max, dtype);
+  if (rc) return rc;
+  int cs = 0;
+  if (landmarks != nullptr) {
+    rc = chunk_shift_of(chunk, &cs);
+    if (rc) return rc;
+  }
+  if ((int64_t)B * H == 0) return DD_OK;
+  if (!k_dev || !k_host || !v_host || !new_k || !new_v || !lens)
+    return fail(DD_ERR_INVALID_ARG, "null pointer argument");
+  if (lens_out == lens) return fail(DD_ERR_INVALID_ARG, "lens_out must not alias lens");
+  if (!aligned16(k_dev) || !aligned16(k_host) || !aligned16(v_host) || !aligned16(new_k) ||
+      !aligned16(new_v) || (landmarks && !aligned16(landmarks)))
+    return fail(DD_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+  hipError_t e = dd::launch_kv_append(k_dev, k_host, v_host, new_k, new_v, lens, lens_out, B, H,
+                                      D, n_max, dtype, cs, landmarks, stream);
+  if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+  return DD_OK;
+}
+
 DD_API size_t dd_attn_workspace(int B, int H, int k, int D) {
   if (B <= 0 || H <= 0 || k <= 0) return 0;
   return dd::attn_workspace(B, H, k, D);

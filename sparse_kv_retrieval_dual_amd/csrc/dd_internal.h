@@ -122,4 +122,12 @@ hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStrea
 hipError_t launch_landmarks(const void* keys, const int32_t* lens, int B, int H, int D,
                             int64_t n_max, int chunk_shift, int dtype, float* out, hipStream_t s);
 
+// Appends new_k / new_v ([BH][D]) at row lens[b] of k_dev, k_host and
+// v_host, writes lens_out[b] = lens[b] + 1 (lens_out may be null), and, with
+// landmarks, recomputes the landmark of the chunk holding the new row.
+hipError_t launch_kv_append(void* k_dev, void* k_host, void* v_host, const void* new_k,
+                            const void* new_v, const int32_t* lens, int32_t* lens_out, int B,
+                            int H, int D, int64_t n_max, int dtype, int chunk_shift,
+                            float* landmarks, hipStream_t s);
+
 }  // namespace dd

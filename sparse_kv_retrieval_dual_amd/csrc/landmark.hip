@@ -90,7 +90,99 @@ hipError_t launch_landmarks_t(const void* keys, const int32_t* lens, int BH, int
   return hipGetLastError();
 }
 
+// One wave per (b, h): the new token's K and V rows (LPR lanes, 16 B each)
+// go to row lens[b] of the device keys and of both host planes; with
+// landmarks, the landmark of the chunk holding that row is recomputed from
+// the chunk's earlier rows (device copy) and the new row, summed in the
+// same row order as k_landmarks.  A request whose length is outside
+// [0, n_max) is left as it is.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_kv_append(T* __restrict__ k_dev, T* __restrict__ k_host,
+                                                  T* __restrict__ v_host,
+                                                  const T* __restrict__ new_k,
+                                                  const T* __restrict__ new_v,
+                                                  const int32_t* __restrict__ lens,
+                                                  int32_t* __restrict__ lens_out, int H,
+                                                  int64_t n_max, int cs,
+                                                  float* __restrict__ landmarks, int64_t nc_max) {
+  constexpr int EPL = 16 / (int)sizeof(T);
+  constexpr int LPR = D / EPL;
+  const int bh = blockIdx.x;
+  const int b = bh / H;
+  const int lane = threadIdx.x;
+  const int32_t len = lens[b];
+  const bool ok = len >= 0 && (int64_t)len < n_max;
+  if (lens_out != nullptr && bh % H == 0 && lane == 0) lens_out[b] = ok ? len + 1 : len;
+  if (!ok || lane >= LPR) return;
+  const int64_t src = (int64_t)bh * D + lane * EPL;
+  const int64_t dst = ((int64_t)bh * n_max + len) * D + lane * EPL;
+  const u32x4 nk = *reinterpret_cast<const u32x4*>(new_k + src);
+  const u32x4 nv = *reinterpret_cast<const u32x4*>(new_v + src);
+  *reinterpret_cast<u32x4*>(k_dev + dst) = nk;
+  *reinterpret_cast<u32x4*>(k_host + dst) = nk;
+  *reinterpret_cast<u32x4*>(v_host + dst) = nv;
+  if (landmarks == nullptr) return;
+  const int64_t e = (int64_t)len >> cs;
+  const int64_t r0 = e << cs;
+  float acc[EPL];
+#pragma unroll
+  for (int x = 0; x < EPL; ++x) acc[x] = 0.f;
+  for (int64_t r = r0; r < len; ++r) {
+    float f[EPL];
+    Unpack<T>::run(*reinterpret_cast<const u32x4*>(k_dev + ((int64_t)bh * n_max + r) * D + lane * EPL), f);
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) acc[x] += f[x];
+  }
+  float f[EPL];
+  Unpack<T>::run(nk, f);
+#pragma unroll
+  for (int x = 0; x < EPL; ++x) acc[x] += f[x];
+  const float n = (float)(len - r0 + 1);
+  float* o = landmarks + ((int64_t)bh * nc_max + e) * D + lane * EPL;
+#pragma unroll
+  for (int x = 0; x < EPL; x += 4) {
+    f32x4_t v;
+    v.x = acc[x] / n;
+    v.y = acc[x + 1] / n;
+    v.z = acc[x + 2] / n;
+    v.w = acc[x + 3] / n;
+    *reinterpret_cast<f32x4_t*>(o + x) = v;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_kv_append_t(void* k_dev, void* k_host, void* v_host, const void* new_k,
+                              const void* new_v, const int32_t* lens, int32_t* lens_out, int BH,
+                              int H, int64_t n_max, int cs, float* landmarks, hipStream_t s) {
+  const int64_t nc_max = (n_max + ((int64_t)1 << cs) - 1) >> cs;
+  hipLaunchKernelGGL((k_kv_append<T, D>), dim3(BH), dim3(64), 0, s, static_cast<T*>(k_dev),
+                     static_cast<T*>(k_host), static_cast<T*>(v_host),
+                     static_cast<const T*>(new_k), static_cast<const T*>(new_v), lens, lens_out,
+                     H, n_max, cs, landmarks, nc_max);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_kv_append(void* k_dev, void* k_host, void* v_host, const void* new_k,
+                            const void* new_v, const int32_t* lens, int32_t* lens_out, int B,
+                            int H, int D, int64_t n_max, int dtype, int chunk_shift,
+                            float* landmarks, hipStream_t s) {
+  const int BH = B * H;
+  if (BH == 0) return hipSuccess;
+  if (dtype == kBF16) {
+    if (D == 128)
+      return launch_kv_append_t<uint16_t, 128>(k_dev, k_host, v_host, new_k, new_v, lens, lens_out,
+                                               BH, H, n_max, chunk_shift, landmarks, s);
+    return launch_kv_append_t<uint16_t, 64>(k_dev, k_host, v_host, new_k, new_v, lens, lens_out,
+                                            BH, H, n_max, chunk_shift, landmarks, s);
+  }
+  if (D == 128)
+    return launch_kv_append_t<float, 128>(k_dev, k_host, v_host, new_k, new_v, lens, lens_out, BH,
+                                          H, n_max, chunk_shift, landmarks, s);
+  return launch_kv_append_t<float, 64>(k_dev, k_host, v_host, new_k, new_v, lens, lens_out, BH, H,
+                                       n_max, chunk_shift, landmarks, s);
+}
 
 hipError_t launch_landmarks(const void* keys, const int32_t* lens, int B, int H, int D,
                             int64_t n_max, int chunk_shift, int dtype, float* out, hipStream_t s) {

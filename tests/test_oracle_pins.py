@@ -516,6 +516,68 @@ def test_chunk_selection_and_attention_closed_form():
     np.testing.assert_array_equal(r2["out"], r["out"])
 
 
+# --------------------------------------------------------------------------- decode loop
+def test_append_rows_writes_one_row_per_request():
+    cache = np.arange(2 * 3 * 5 * 4, dtype=np.float32).reshape(2, 3, 5, 4)
+    new = -np.ones((2, 3, 4), dtype=np.float32)
+    out, lens = oracle.append_rows(cache, np.array([2, 5]), new)
+    assert lens.tolist() == [3, 5]                    # request 1 is full
+    assert np.all(out[0, :, 2] == -1)
+    out[0, :, 2] = cache[0, :, 2]
+    np.testing.assert_array_equal(out, cache)
+
+
+def _loop(w, steps, new_key=None, chunk=0):
+    """The oracle decode loop: append, then the layer step with the previous
+    step's speculated set as the prediction."""
+    lay, kh, vh, lens = _layer(w)
+    q = lay["q"]
+    ref = oracle.layer_step(q.numpy(), kh, kh, vh, lens, w.k, w.dtype, chunk=chunk)
+    out = []
+    for t in range(1, steps + 1):
+        q, nk, nv = gen.decode_step_inputs(w, 0, t, q)
+        if new_key is not None:
+            nk = new_key(q).to(nk.dtype)
+        kh, _ = oracle.append_rows(kh, lens, _stored(nk))
+        vh, lens = oracle.append_rows(vh, lens, _stored(nv))
+        ref = oracle.layer_step(q.numpy(), kh, kh, vh, lens, w.k, w.dtype, pred=ref["spec"],
+                                chunk=chunk)
+        out.append((ref, lens.copy()))
+    return out
+
+
+def _stored(t):
+    t = t.contiguous()
+    return t.view(torch.int16).numpy() if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def test_decode_loop_perfect_speculation_has_full_recall():
+    """With the speculated query equal to the current one and the next token
+    equal to the speculated one, and zero new keys (below the k-th score), the
+    true set of step t+1 is the speculated set of step t: no misses."""
+    w = gen.workload("llama7b_32k_layer").scaled(B=2, H=2, n_max=3000, rho=1.0, rho_c=0.0,
+                                                 len_lo=2900, len_hi=2900)
+    for chunk in (0, 4):
+        for t, (ref, lens) in enumerate(_loop(w, 3, new_key=lambda q: 0.0 * q[:, :, 0],
+                                              chunk=chunk), start=1):
+            st = ref["stats"]
+            assert st[0] == 0 and st[1] == w.B * w.H * (w.k // max(chunk, 1)), (chunk, st)
+            assert lens.tolist() == [2900 + t] * w.B
+
+
+def test_decode_loop_new_dominant_key_is_exactly_one_miss():
+    """A new key of 8 q_cur scores 8|q|^2/sqrt(D), above every planted key, so it
+    joins each true set without being in the prediction (made before it
+    existed): exactly one miss per (b, h) at every step."""
+    w = gen.workload("llama7b_32k_layer").scaled(B=2, H=2, n_max=3000, rho=1.0, rho_c=0.0,
+                                                 len_lo=2900, len_hi=2900)
+    for ref, lens in _loop(w, 3, new_key=lambda q: 8.0 * q[:, :, 0]):
+        st = ref["stats"]
+        assert st[0] == w.B * w.H and st[1] == w.B * w.H * (w.k - 1), st
+        n = int(lens[0])
+        assert np.all(ref["cur"][:, :, -1] == n - 1)    # the new row, last in ascending order
+
+
 # --------------------------------------------------------------------------- comparators
 def test_tie_band_comparator_accepts_swaps_and_rejects_errors():
     logits = np.array([[5.0, 3.0, 3.0 + 5e-4, 1.0, 3.0 - 2e-3]])
