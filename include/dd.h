@@ -300,6 +300,15 @@ typedef struct dd_layer_step_args {
   int chunk;
   const float* const* landmarks; /* chunk > 1: per layer device fp32
                                     [B][H][ceil(n_max / chunk)][D] (dd_landmarks) */
+  /* Dual-token attention (arXiv page, section 1: the dual-token pipeline runs
+   * the normal token and the retrieval-guiding token through the same
+   * decoding flow).  NULL, or per layer (entries may be NULL) device fp32
+   * [B][H][D]: the speculated query (plane 1 of q) attends over the same
+   * selected rows as the current one, each K/V row read once for both; its
+   * log-sum-exp goes to lse_spec (NULL, or per layer [B][H], entries may be
+   * NULL).  out is unchanged bit for bit. */
+  float* const* out_spec;
+  float* const* lse_spec;
 } dd_layer_step_args;
 
 /* Runs the layer step for layers 0..L-1.  Per layer, on the main stream:

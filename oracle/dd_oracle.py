@@ -342,7 +342,7 @@ def chunk_rows(sel: np.ndarray, lens: np.ndarray, chunk: int) -> np.ndarray:
 def layer_step(q: np.ndarray, keys_dev: np.ndarray, keys_host: np.ndarray,
                values_host: np.ndarray, lens: np.ndarray, k: int, dtype: str,
                pred: np.ndarray | None = None, scale: float | None = None,
-               chunk: int = 0):
+               chunk: int = 0, dual: bool = False):
     """One layer of the predictive decode step, end to end.
 
     Score both queries against every cached key, select each query's top-k,
@@ -356,6 +356,12 @@ def layer_step(q: np.ndarray, keys_dev: np.ndarray, keys_host: np.ndarray,
     the lower chunk), the prediction and the bookkeeping are in chunks, and
     the current query attends over the rows of its chunks (those below
     lens[b]).  chunk = 1 is the per-key step computed through landmarks.
+
+    dual: the speculated query also attends, over the same rows as the
+    current one (out_spec, lse_spec).  Reading: the dual-token pipeline runs
+    the normal and the retrieval-guiding token through the same decoding flow
+    (arXiv page, section 1); the rows in the layer buffer are the current
+    token's, so those are the rows both attend.
     """
     if chunk >= 1:
         D = keys_dev.shape[3]
@@ -372,8 +378,12 @@ def layer_step(q: np.ndarray, keys_dev: np.ndarray, keys_host: np.ndarray,
         misses = int(bk["miss_cnt"].sum())
         stats = np.array([misses, int(bk["hits"].sum()),
                           int(bk["prefetched"].sum()) + misses], dtype=np.int64)
+        extra = {}
+        if dual:
+            extra["out_spec"], extra["lse_spec"] = masked_attention(
+                q[:, :, 1], keys_host, values_host, lens, rows, dtype, sc)
         return {"scores": s, "cur": cur, "spec": spec, "out": out, "lse": lse,
-                "stats": stats, "landmarks": lm, "rows": rows, **bk}
+                "stats": stats, "landmarks": lm, "rows": rows, **extra, **bk}
     s = scaled_logits(q, keys_dev, lens, dtype, scale)
     sel = select_topk(s, lens, k)
     cur = np.ascontiguousarray(sel[:, :, 0])
@@ -383,5 +393,9 @@ def layer_step(q: np.ndarray, keys_dev: np.ndarray, keys_host: np.ndarray,
     misses = int(bk["miss_cnt"].sum())
     stats = np.array([misses, int(bk["hits"].sum()),
                       int(bk["prefetched"].sum()) + misses], dtype=np.int64)
+    extra = {}
+    if dual:
+        extra["out_spec"], extra["lse_spec"] = masked_attention(
+            q[:, :, 1], keys_host, values_host, lens, cur, dtype, scale)
     return {"scores": s, "cur": cur, "spec": spec, "out": out, "lse": lse,
-            "stats": stats, **bk}
+            "stats": stats, **extra, **bk}

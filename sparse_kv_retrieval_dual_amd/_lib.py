@@ -49,6 +49,7 @@ class LayerStepArgs(ctypes.Structure):
         ("stream", P),
         ("timing", P),
         ("chunk", c_int), ("landmarks", P),
+        ("out_spec", P), ("lse_spec", P),
     ]
 
 

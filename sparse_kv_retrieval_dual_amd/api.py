@@ -306,7 +306,8 @@ class Context:
 
     def layer_step(self, q, k_dev, k_host, v_host, lens, k: int, pred=None, scale: float = 0.0,
                    cur=None, spec=None, out=None, lse=None, stats=None, ring=None, ws=None,
-                   timing=None, stream=None, chunk: int = 0, landmarks=None):
+                   timing=None, stream=None, chunk: int = 0, landmarks=None,
+                   dual: bool = False, out_spec=None, lse_spec=None):
         """dd_layer_step over the layers given as lists (one tensor per layer).
 
         q[l] fp32 [B][H][2][D]; k_dev[l] device [B][H][n_max][D]; k_host[l], v_host[l]
@@ -314,6 +315,8 @@ class Context:
         None or int32 [B][H][k].  Returns dict(cur, spec, out, lse, stats).
         chunk > 1: landmarks[l] fp32 [B][H][ceil(n_max/chunk)][D] are scored and
         pred / cur / spec hold k // chunk chunk indices per (b, h).
+        dual: the speculated query also attends over the same rows (out_spec,
+        lse_spec in the result).
         `timing` is None or a sequence of L * DD_STAGE_EVENTS raw hipEvent_t handles.
         """
         Lyr = len(q)
@@ -353,6 +356,11 @@ class Context:
             out = [torch.empty(B, H, D, dtype=torch.float32, device=dev) for _ in range(Lyr)]
         if lse is None:
             lse = [torch.empty(B, H, dtype=torch.float32, device=dev) for _ in range(Lyr)]
+        dual = dual or out_spec is not None
+        if dual and out_spec is None:
+            out_spec = [torch.empty(B, H, D, dtype=torch.float32, device=dev) for _ in range(Lyr)]
+        if dual and lse_spec is None:
+            lse_spec = [torch.empty(B, H, dtype=torch.float32, device=dev) for _ in range(Lyr)]
         if stats is None:
             stats = torch.zeros(Lyr, 3, dtype=torch.int64, device=dev)
         rb = ring_bytes(self.ring_slots, B, H, D, k, dt)
@@ -365,7 +373,9 @@ class Context:
                 _ptr_array(pred) if pred is not None else None,
                 _ptr_array(cur), _ptr_array(spec), _ptr_array(out),
                 _ptr_array(lse) if lse is not None else None,
-                _ptr_array(landmarks) if chunk > 1 else None]
+                _ptr_array(landmarks) if chunk > 1 else None,
+                _ptr_array(out_spec) if dual else None,
+                _ptr_array(lse_spec) if dual else None]
         tarr = None
         if timing is not None:
             tarr = (ctypes.c_void_p * len(timing))(*timing)
@@ -385,9 +395,14 @@ class Context:
             timing=None if tarr is None else ctypes.cast(tarr, ctypes.c_void_p),
             chunk=chunk,
             landmarks=None if keep[9] is None else ctypes.cast(keep[9], ctypes.c_void_p),
+            out_spec=None if keep[10] is None else ctypes.cast(keep[10], ctypes.c_void_p),
+            lse_spec=None if keep[11] is None else ctypes.cast(keep[11], ctypes.c_void_p),
         )
         L.check(_lib().dd_layer_step(self._h, ctypes.byref(a)))
-        return {"cur": cur, "spec": spec, "out": out, "lse": lse, "stats": stats}
+        res = {"cur": cur, "spec": spec, "out": out, "lse": lse, "stats": stats}
+        if dual:
+            res["out_spec"], res["lse_spec"] = out_spec, lse_spec
+        return res
 
 
 class Decoder:

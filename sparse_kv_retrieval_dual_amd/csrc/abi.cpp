@@ -491,7 +491,9 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     const dd::TopkBook book{P, nullptr, nullptr, nullptr};
     const dd::FusedAttn fa{a->q[l], kslot, vslot, a->k_host[l], a->v_host[l],
                            kdev ? a->k_dev[l] : nullptr, a->n_max, cs, D, a->dtype, sc,
-                           a->out[l], a->lse ? a->lse[l] : nullptr, st};
+                           a->out[l], a->lse ? a->lse[l] : nullptr, st,
+                           a->out_spec ? a->out_spec[l] : nullptr,
+                           (a->out_spec && a->out_spec[l] && a->lse_spec) ? a->lse_spec[l] : nullptr};
     e = dd::launch_topk(scores, a->lens, B, H, 2, n_sel, ks, a->cur_idx[l], a->spec_idx[l], ks,
                         &book, &fa, ms, cs);
     if (e != hipSuccess) return hip_fail(e, "top-k and attention kernel launch");

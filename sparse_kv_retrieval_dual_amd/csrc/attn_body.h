@@ -60,23 +60,28 @@ struct AttnRows {
   int64_t n_max;
 };
 
-// LDS of one chunk merge: per-wave max, weight sum and weighted V.
-template <int D>
+// LDS of one chunk merge, per query: per-wave max, weight sum and weighted V.
+template <int D, int NQ = 1>
 struct AttnLds {
-  float m[kAttnWaves];
-  float l[kAttnWaves];
-  float o[kAttnWaves][D];
+  float m[NQ][kAttnWaves];
+  float l[NQ][kAttnWaves];
+  float o[NQ][kAttnWaves][D];
 };
 
-// Entries c0 .. c0 + 127 (those < lim) of query q (D floats).  entry(j, r,
-// c) gives entry j's slot row r (-1: skipped) and host row c.  Afterwards
-// cm and cl (all threads) are the chunk's max logit and weight sum, and
-// threads d < D hold od = the chunk's weighted V sum of column d.  The
-// caller must not touch lds until a barrier after this returns.
-template <typename T, int D, class Entry>
-__device__ __forceinline__ void attend_chunk(const float* __restrict__ q, const AttnRows<T>& R,
-                                             int c0, int lim, float scale, Entry entry,
-                                             AttnLds<D>& lds, float& cm, float& cl, float& od) {
+// Entries c0 .. c0 + 127 (those < lim) for NQ queries at once: query j is
+// q + j * D (D floats).  Every K and V row is read once and serves all NQ
+// queries.  Contraction is off: only the explicit fmaf calls fuse, so each
+// query's result is the same bits whatever NQ is.  entry(j, r, c) gives entry j's slot row r (-1: skipped) and host
+// row c.  Afterwards cm[j] and cl[j] (all threads) are query j's max logit
+// and weight sum over the chunk, and threads d < D hold od[j] = its weighted
+// V sum of column d.  The caller must not touch lds until a barrier after
+// this returns.
+template <typename T, int D, int NQ, class Entry>
+__device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, const AttnRows<T>& R,
+                                               int c0, int lim, float scale, Entry entry,
+                                               AttnLds<D, NQ>& lds, float (&cm)[NQ],
+                                               float (&cl)[NQ], float (&od)[NQ]) {
+#pragma clang fp contract(off)
   using S = AttnShape<T, D>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -139,77 +144,104 @@ __device__ __forceinline__ void attend_chunk(const float* __restrict__ q, const 
 #pragma unroll
     for (int u = 0; u < S::U; ++u) kr[u] = vr[u] = zero;
   }
-  float qr[S::EPL];
+  float qr[NQ][S::EPL];
 #pragma unroll
-  for (int e = 0; e < S::EPL; ++e) qr[e] = q[col * S::EPL + e];
+  for (int qi = 0; qi < NQ; ++qi)
+#pragma unroll
+    for (int e = 0; e < S::EPL; ++e) qr[qi][e] = q[qi * D + col * S::EPL + e];
 
-  float s[S::U];
+  float s[NQ * S::U];  // s[qi * U + u]
 #pragma unroll
   for (int u = 0; u < S::U; ++u) {
     float f[S::EPL];
     Unpack<T>::run(kr[u], f);
-    float a = 0.f;
 #pragma unroll
-    for (int e = 0; e < S::EPL; ++e) a = fmaf(f[e], qr[e], a);
-    s[u] = a;
+    for (int qi = 0; qi < NQ; ++qi) {
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < S::EPL; ++e) a = fmaf(f[e], qr[qi][e], a);
+      s[qi * S::U + u] = a;
+    }
   }
-  group_allreduce<S::LPR, S::U>(s);
+  group_allreduce<S::LPR, NQ * S::U>(s);
 
-  // Wave-local softmax over its 32 entries (RPI row groups x U).
-  float mx = -INFINITY;
 #pragma unroll
-  for (int u = 0; u < S::U; ++u) {
-    s[u] = (rows[u] >= 0) ? s[u] * scale : -INFINITY;
-    mx = fmaxf(mx, s[u]);
-  }
+  for (int qi = 0; qi < NQ; ++qi) {
+    // Wave-local softmax of query qi over its 32 entries (RPI row groups x U).
+    float mx = -INFINITY;
 #pragma unroll
-  for (int off = S::LPR; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  float l = 0.f;
-  float o[S::EPL];
+    for (int u = 0; u < S::U; ++u) {
+      float& x = s[qi * S::U + u];
+      x = (rows[u] >= 0) ? x * scale : -INFINITY;
+      mx = fmaxf(mx, x);
+    }
 #pragma unroll
-  for (int e = 0; e < S::EPL; ++e) o[e] = 0.f;
+    for (int off = S::LPR; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float l = 0.f;
+    float o[S::EPL];
 #pragma unroll
-  for (int u = 0; u < S::U; ++u) {
-    const float w = (rows[u] >= 0) ? exp2f((s[u] - mx) * kLog2e) : 0.f;
-    l += w;
-    float f[S::EPL];
-    Unpack<T>::run(rows[u] >= 0 ? vr[u] : zero, f);
+    for (int e = 0; e < S::EPL; ++e) o[e] = 0.f;
 #pragma unroll
-    for (int e = 0; e < S::EPL; ++e) o[e] = fmaf(w, f[e], o[e]);
-  }
+    for (int u = 0; u < S::U; ++u) {
+      const float w = (rows[u] >= 0) ? exp2f((s[qi * S::U + u] - mx) * kLog2e) : 0.f;
+      l += w;
+      float f[S::EPL];
+      Unpack<T>::run(rows[u] >= 0 ? vr[u] : zero, f);
 #pragma unroll
-  for (int off = S::LPR; off < 64; off <<= 1) {
-    l += __shfl_xor(l, off);
+      for (int e = 0; e < S::EPL; ++e) o[e] = fmaf(w, f[e], o[e]);
+    }
 #pragma unroll
-    for (int e = 0; e < S::EPL; ++e) o[e] += __shfl_xor(o[e], off);
-  }
-  if (rsub == 0) {
+    for (int off = S::LPR; off < 64; off <<= 1) {
+      l += __shfl_xor(l, off);
 #pragma unroll
-    for (int e = 0; e < S::EPL; ++e) lds.o[wave][col * S::EPL + e] = o[e];
-    if (col == 0) {
-      lds.m[wave] = mx;
-      lds.l[wave] = l;
+      for (int e = 0; e < S::EPL; ++e) o[e] += __shfl_xor(o[e], off);
+    }
+    if (rsub == 0) {
+#pragma unroll
+      for (int e = 0; e < S::EPL; ++e) lds.o[qi][wave][col * S::EPL + e] = o[e];
+      if (col == 0) {
+        lds.m[qi][wave] = mx;
+        lds.l[qi][wave] = l;
+      }
     }
   }
   __syncthreads();
 
   // Merge the waves (entry order is fixed: wave 0, 1, 2, 3).
-  cm = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kAttnWaves; ++w) cm = fmaxf(cm, lds.m[w]);
-  float f[kAttnWaves];
-  cl = 0.f;
-#pragma unroll
-  for (int w = 0; w < kAttnWaves; ++w) {
-    f[w] = (lds.l[w] > 0.f) ? exp2f((lds.m[w] - cm) * kLog2e) : 0.f;
-    cl += lds.l[w] * f[w];
-  }
-  od = 0.f;
   const int d = threadIdx.x;
-  if (d < D) {
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) od += lds.o[w][d] * f[w];
+  for (int qi = 0; qi < NQ; ++qi) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) m = fmaxf(m, lds.m[qi][w]);
+    float f[kAttnWaves];
+    float tl = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      f[w] = (lds.l[qi][w] > 0.f) ? exp2f((lds.m[qi][w] - m) * kLog2e) : 0.f;
+      tl = fmaf(lds.l[qi][w], f[w], tl);
+    }
+    float acc = 0.f;
+    if (d < D) {
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) acc = fmaf(lds.o[qi][w][d], f[w], acc);
+    }
+    cm[qi] = m;
+    cl[qi] = tl;
+    od[qi] = acc;
   }
+}
+
+// One query (see attend_chunk_n).
+template <typename T, int D, class Entry>
+__device__ __forceinline__ void attend_chunk(const float* __restrict__ q, const AttnRows<T>& R,
+                                             int c0, int lim, float scale, Entry entry,
+                                             AttnLds<D>& lds, float& cm, float& cl, float& od) {
+  float m[1], l[1], o[1];
+  attend_chunk_n<T, D, 1>(q, R, c0, lim, scale, entry, lds, m, l, o);
+  cm = m[0];
+  cl = l[0];
+  od = o[0];
 }
 
 // Merge of the chunk partials of one (b, h) by log-sum-exp, for column d:
@@ -218,6 +250,7 @@ __device__ __forceinline__ void attend_chunk(const float* __restrict__ q, const 
 template <int D>
 __device__ __forceinline__ void combine_chunks(const float* p, int chunks, int d, float& out_d,
                                                float& lse) {
+#pragma clang fp contract(off)
   float mx = -INFINITY;
   for (int c = 0; c < chunks; ++c) mx = fmaxf(mx, p[c * (D + 2) + D]);
   float tot = 0.f, od = 0.f;

@@ -71,6 +71,9 @@ struct FusedAttn {
   float* lse;            // [BH] or null
   int64_t* stats;        // {misses, hits, rows over the host link}, added to
                          // atomically (zeroed before the launch), or null
+  float* out_spec;       // [BH][D]: the speculated query (plane 1) attends over
+                         // the same rows, or null
+  float* lse_spec;       // [BH] or null
 };
 
 // Top-k of each score row.  Plane j of slab bh is written at

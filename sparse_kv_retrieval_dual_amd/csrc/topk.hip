@@ -89,6 +89,11 @@ static_assert(4 * 256 + kNT <= kBins, "walk starts fit the bound histogram");
 // attention scratch: per-wave partials and up to 32 chunk partials of D+2
 constexpr int kAttnScratchWords = 8 + 4 * 128 + 8 + 32 * (128 + 2);
 static_assert(kLIdx + kAttnScratchWords <= Lay<true>::c, "attention scratch fits");
+// both queries' (dual-token) attention scratch: the tail of region C for a
+// cached row, the candidate lists otherwise (both free once emitted)
+constexpr int kAttnScratchWords2 = 2 * (8 + 4 * 128) + 8 + 2 * 32 * (128 + 2);
+static_assert(Lay<true>::end + kAttnScratchWords2 <= Lay<true>::words, "dual scratch fits (cached)");
+static_assert(kLIdx + kAttnScratchWords2 <= Lay<false>::c, "dual scratch fits (long rows)");
 
 __device__ __forceinline__ void clear(uint32_t* p, int words) {
   for (int i = threadIdx.x; i < words; i += kNT) p[i] = 0u;
@@ -693,13 +698,16 @@ __device__ __forceinline__ int radix_select(const float* __restrict__ row, int n
 // the attention kernel, chunk partials merged the same way.  With selection
 // by chunk landmarks (cs > 0) each of the ks selected entries stands for the
 // 2^cs consecutive rows of its chunk, rows past the request's length left
-// out; the slot holds them at 2^cs times the entry's slot position.
-template <typename T, int D>
+// out; the slot holds them at 2^cs times the entry's slot position.  NQ = 2:
+// the speculated query (plane 1) attends over the same rows too, each K/V
+// row read once for both (the dual-token pipeline runs both tokens through
+// the layer).
+template <typename T, int D, int NQ>
 __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, int ks,
                                                   int32_t len, const int32_t* lpos,
                                                   const int32_t* lcur, float* scratch) {
-  AttnLds<D>& lds = *reinterpret_cast<AttnLds<D>*>(scratch);
-  float* part = scratch + (sizeof(AttnLds<D>) + 15) / 16 * 4;
+  AttnLds<D, NQ>& lds = *reinterpret_cast<AttnLds<D, NQ>*>(scratch);
+  float* part = scratch + (sizeof(AttnLds<D, NQ>) + 15) / 16 * 4;
   const int cs = fa.chunk_shift;
   const int k = ks << cs;  // rows attended (at most)
   const int64_t n_rows = fa.n_rows;
@@ -723,43 +731,64 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
     c = ok ? (int)row : -1;
   };
   const int chunks = (k + kAttnChunk - 1) / kAttnChunk;
-  const float* qrow = fa.q + (int64_t)bh * 2 * D;
+  const float* qrow = fa.q + (int64_t)bh * 2 * D;  // plane 0, then plane 1
+  float* const outs[2] = {fa.out, fa.out_spec};
+  float* const lses[2] = {fa.lse, fa.lse_spec};
   const int d = threadIdx.x;
   for (int ch = 0; ch < chunks; ++ch) {
-    float cm, cl, od;
-    attend_chunk<T, D>(qrow, R, ch * kAttnChunk, k, fa.scale, entry, lds, cm, cl, od);
+    float cm[NQ], cl[NQ], od[NQ];
+    attend_chunk_n<T, D, NQ>(qrow, R, ch * kAttnChunk, k, fa.scale, entry, lds, cm, cl, od);
     if (d < D) {
-      if (chunks == 1) {
-        fa.out[(int64_t)bh * D + d] = (cl > 0.f) ? od / cl : 0.f;
-        if (d == 0 && fa.lse != nullptr) fa.lse[bh] = (cl > 0.f) ? cm + logf(cl) : -INFINITY;
-      } else {
-        float* pc = part + ch * (D + 2);
-        pc[d] = od;
-        if (d == 0) {
-          pc[D] = cl > 0.f ? cm : -INFINITY;
-          pc[D + 1] = cl;
+#pragma unroll
+      for (int qi = 0; qi < NQ; ++qi) {
+        if (chunks == 1) {
+          outs[qi][(int64_t)bh * D + d] = (cl[qi] > 0.f) ? od[qi] / cl[qi] : 0.f;
+          if (d == 0 && lses[qi] != nullptr)
+            lses[qi][bh] = (cl[qi] > 0.f) ? cm[qi] + logf(cl[qi]) : -INFINITY;
+        } else {
+          float* pc = part + (qi * chunks + ch) * (D + 2);
+          pc[d] = od[qi];
+          if (d == 0) {
+            pc[D] = cl[qi] > 0.f ? cm[qi] : -INFINITY;
+            pc[D + 1] = cl[qi];
+          }
         }
       }
     }
     __syncthreads();  // lds is reused by the next chunk; partials complete
   }
   if (chunks > 1 && d < D) {
-    float od, l;
-    combine_chunks<D>(part, chunks, d, od, l);
-    fa.out[(int64_t)bh * D + d] = od;
-    if (d == 0 && fa.lse != nullptr) fa.lse[bh] = l;
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) {
+      float o, l;
+      combine_chunks<D>(part + qi * chunks * (D + 2), chunks, d, o, l);
+      outs[qi][(int64_t)bh * D + d] = o;
+      if (d == 0 && lses[qi] != nullptr) lses[qi][bh] = l;
+    }
   }
 }
 
+// scratch: LDS for one query's attention (kAttnScratchWords); scratch2: for
+// both queries' (kAttnScratchWords2), used when the speculated query attends.
 __device__ __forceinline__ void fused_attention(const FusedAttn& fa, int bh, int ks, int32_t len,
                                                 const int32_t* lpos, const int32_t* lcur,
-                                                float* scratch) {
+                                                float* scratch, float* scratch2) {
+  if (fa.out_spec != nullptr) {
+    if (fa.dtype == kBF16) {
+      if (fa.D == 128) fused_attention_t<uint16_t, 128, 2>(fa, bh, ks, len, lpos, lcur, scratch2);
+      else fused_attention_t<uint16_t, 64, 2>(fa, bh, ks, len, lpos, lcur, scratch2);
+    } else {
+      if (fa.D == 128) fused_attention_t<float, 128, 2>(fa, bh, ks, len, lpos, lcur, scratch2);
+      else fused_attention_t<float, 64, 2>(fa, bh, ks, len, lpos, lcur, scratch2);
+    }
+    return;
+  }
   if (fa.dtype == kBF16) {
-    if (fa.D == 128) fused_attention_t<uint16_t, 128>(fa, bh, ks, len, lpos, lcur, scratch);
-    else fused_attention_t<uint16_t, 64>(fa, bh, ks, len, lpos, lcur, scratch);
+    if (fa.D == 128) fused_attention_t<uint16_t, 128, 1>(fa, bh, ks, len, lpos, lcur, scratch);
+    else fused_attention_t<uint16_t, 64, 1>(fa, bh, ks, len, lpos, lcur, scratch);
   } else {
-    if (fa.D == 128) fused_attention_t<float, 128>(fa, bh, ks, len, lpos, lcur, scratch);
-    else fused_attention_t<float, 64>(fa, bh, ks, len, lpos, lcur, scratch);
+    if (fa.D == 128) fused_attention_t<float, 128, 1>(fa, bh, ks, len, lpos, lcur, scratch);
+    else fused_attention_t<float, 64, 1>(fa, bh, ks, len, lpos, lcur, scratch);
   }
 }
 
@@ -851,7 +880,8 @@ __global__ __launch_bounds__(kNT) void k_topk(
               (unsigned long long)(fetchable + misses));
   }
   __syncthreads();  // every entry's slot row and row index are in LDS
-  fused_attention(fa, bh, k, lens[bh / H], sk.lpos, sk.lcur, reinterpret_cast<float*>(smem + kLIdx));
+  fused_attention(fa, bh, k, lens[bh / H], sk.lpos, sk.lcur, reinterpret_cast<float*>(smem + kLIdx),
+                  reinterpret_cast<float*>(smem + (CACHED ? Lay<true>::end : kLIdx)));
 }
 
 template <bool CACHED>

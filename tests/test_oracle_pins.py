@@ -508,12 +508,31 @@ def test_chunk_selection_and_attention_closed_form():
     assert abs(r["out"][0, 0, 0] - (6 + 25 * e) / (4 + 2 * e)) < 1e-12
     assert abs(r["out"][0, 0, 1] - 1.0) < 1e-12
     assert abs(r["lse"][0, 0] - math.log(4 + 2 * e)) < 1e-12
+    # dual-token: the speculated query -q attends over the same rows {0-3, 12, 13}
+    # (logits 0 and -1), not over its own chunks {0, 1}
+    rd = oracle.layer_step(q, keys, keys, vals, lens, 8, oracle.F32, chunk=c, dual=True)
+    assert abs(rd["out_spec"][0, 0, 0] - (6 + 25 / e) / (4 + 2 / e)) < 1e-12
+    assert abs(rd["lse_spec"][0, 0] - math.log(4 + 2 / e)) < 1e-12
+    np.testing.assert_array_equal(rd["out"], r["out"])
     # prediction = chunks {0, 1}: chunk 0 hits (slot rows 0..3), chunk 3 misses
     r2 = oracle.layer_step(q, keys, keys, vals, lens, 8, oracle.F32, chunk=c,
                            pred=np.array([[[0, 1]]], dtype=np.int32))
     assert r2["stats"].tolist() == [1, 1, 3]
     assert r2["pos"].tolist() == [[[0, 2]]]
     np.testing.assert_array_equal(r2["out"], r["out"])
+
+
+def test_dual_token_attention_with_equal_queries_is_the_current_output():
+    """With the speculated query equal to the current one, both attend over the
+    same rows with the same logits: equal outputs, per key and by chunks."""
+    w = gen.workload("llama7b_32k_layer").scaled(B=2, H=2, n_max=700, rho=1.0, rho_c=0.0,
+                                                 len_lo=600, len_hi=700, k=64)
+    lay, kh, vh, lens = _layer(w)
+    for chunk in (0, 8):
+        r = oracle.layer_step(lay["q"].numpy(), kh, kh, vh, lens, w.k, w.dtype, chunk=chunk,
+                              dual=True)
+        np.testing.assert_array_equal(r["out_spec"], r["out"])
+        np.testing.assert_array_equal(r["lse_spec"], r["lse"])
 
 
 # --------------------------------------------------------------------------- decode loop
