@@ -155,6 +155,8 @@ def main():
                     help="where attention reads the selected K rows")
     ap.add_argument("--chunk", type=int, default=0,
                     help="select by landmarks of chunks of this many keys (0: every key)")
+    ap.add_argument("--dual", action="store_true",
+                    help="the speculated query also attends over the selected rows")
     ap.add_argument("--decode-steps", type=int, default=0,
                     help="also time this many real decode steps (KV append + layer step, "
                          "prediction carried), after the headline measurement")
@@ -201,6 +203,7 @@ def main():
     spec = [torch.empty(B, H, ks, dtype=torch.int32, device=dev)]
     out = [torch.empty(B, H, D, dtype=torch.float32, device=dev)]
     lse = [torch.empty(B, H, dtype=torch.float32, device=dev)]
+    out_spec = [torch.empty(B, H, D, dtype=torch.float32, device=dev)] if args.dual else None
     stats = torch.zeros(1, 3, dtype=torch.int64, device=dev)
     ring = torch.empty(dd.ring_bytes(args.ring, B, H, D, k, dd.kv_dtype(lay["k"])), dtype=torch.uint8, device=dev)
     ws = torch.empty(dd.layer_step_workspace_bytes(B, H, D, w.n_max, k), dtype=torch.uint8, device=dev)
@@ -209,7 +212,8 @@ def main():
         ctx.layer_step([q], [k_copies[i % len(k_copies)]], [kh], [vh], lens, k, pred=pred,
                        cur=cur, spec=spec, out=out, lse=lse, stats=stats, ring=ring, ws=ws,
                        timing=timing, chunk=chunk if chunk > 1 else 0,
-                       landmarks=[lm_copies[i % len(lm_copies)]] if chunk > 1 else None)
+                       landmarks=[lm_copies[i % len(lm_copies)]] if chunk > 1 else None,
+                       out_spec=out_spec)
 
     # Untimed first step without a prediction; its speculated set predicts the next.
     step(0, None)
@@ -373,7 +377,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": D, "context": w.n_max,
                    "top_k": k, "queries": 2, "kv_dtype": w.dtype, "accumulate": "f32",
                    "ring_slots": args.ring, "hbm_key_copies": len(k_copies),
-                   "k_rows": args.k_rows, "chunk": chunk},
+                   "k_rows": args.k_rows, "chunk": chunk, "dual_token": bool(args.dual)},
         "roofline": {"bound": "hbm", "achieved": score_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": score_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic,

@@ -68,10 +68,11 @@ struct AttnLds {
   float o[NQ][kAttnWaves][D];
 };
 
-// Entries c0 .. c0 + 127 (those < lim) for NQ queries at once: query j is
-// q + j * D (D floats).  Every K and V row is read once and serves all NQ
-// queries.  Contraction is off: only the explicit fmaf calls fuse, so each
-// query's result is the same bits whatever NQ is.  entry(j, r, c) gives entry j's slot row r (-1: skipped) and host
+// Entries c0 .. c0 + 127 (those < lim) for the first nq <= NQ queries at
+// once: query j is q + j * D (D floats; all NQ are read).  Every K and V row
+// is read once and serves every query.  Contraction is off: only the
+// explicit fmaf calls fuse, so a query's result is the same bits whatever
+// nq is.  entry(j, r, c) gives entry j's slot row r (-1: skipped) and host
 // row c.  Afterwards cm[j] and cl[j] (all threads) are query j's max logit
 // and weight sum over the chunk, and threads d < D hold od[j] = its weighted
 // V sum of column d.  The caller must not touch lds until a barrier after
@@ -79,7 +80,7 @@ struct AttnLds {
 template <typename T, int D, int NQ, class Entry>
 __device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, const AttnRows<T>& R,
                                                int c0, int lim, float scale, Entry entry,
-                                               AttnLds<D, NQ>& lds, float (&cm)[NQ],
+                                               AttnLds<D, NQ>& lds, int nq, float (&cm)[NQ],
                                                float (&cl)[NQ], float (&od)[NQ]) {
 #pragma clang fp contract(off)
   using S = AttnShape<T, D>;
@@ -148,25 +149,28 @@ __device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, cons
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi)
 #pragma unroll
-    for (int e = 0; e < S::EPL; ++e) qr[qi][e] = q[qi * D + col * S::EPL + e];
+    for (int e = 0; e < S::EPL; ++e) qr[qi][e] = qi < nq ? q[qi * D + col * S::EPL + e] : 0.f;
 
+  // Logits: the first query always, the others only when they attend.
   float s[NQ * S::U];  // s[qi * U + u]
 #pragma unroll
-  for (int u = 0; u < S::U; ++u) {
-    float f[S::EPL];
-    Unpack<T>::run(kr[u], f);
+  for (int qi = 0; qi < NQ; ++qi) {
+    if (qi >= nq) break;
 #pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
+    for (int u = 0; u < S::U; ++u) {
+      float f[S::EPL];
+      Unpack<T>::run(kr[u], f);
       float a = 0.f;
 #pragma unroll
       for (int e = 0; e < S::EPL; ++e) a = fmaf(f[e], qr[qi][e], a);
       s[qi * S::U + u] = a;
     }
+    group_allreduce<S::LPR, S::U>(s + qi * S::U);
   }
-  group_allreduce<S::LPR, NQ * S::U>(s);
 
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
+    if (qi >= nq) break;
     // Wave-local softmax of query qi over its 32 entries (RPI row groups x U).
     float mx = -INFINITY;
 #pragma unroll
@@ -211,6 +215,10 @@ __device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, cons
   const int d = threadIdx.x;
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
+    cm[qi] = -INFINITY;
+    cl[qi] = 0.f;
+    od[qi] = 0.f;
+    if (qi >= nq) continue;
     float m = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) m = fmaxf(m, lds.m[qi][w]);
@@ -238,7 +246,7 @@ __device__ __forceinline__ void attend_chunk(const float* __restrict__ q, const 
                                              int c0, int lim, float scale, Entry entry,
                                              AttnLds<D>& lds, float& cm, float& cl, float& od) {
   float m[1], l[1], o[1];
-  attend_chunk_n<T, D, 1>(q, R, c0, lim, scale, entry, lds, m, l, o);
+  attend_chunk_n<T, D, 1>(q, R, c0, lim, scale, entry, lds, 1, m, l, o);
   cm = m[0];
   cl = l[0];
   od = o[0];

@@ -86,14 +86,12 @@ static_assert(4 * 256 <= kBins, "selection histograms fit the bound histogram");
 // histograms, the first prediction position of each thread's words.
 constexpr int kLFirst = kLHist + 4 * 256;
 static_assert(4 * 256 + kNT <= kBins, "walk starts fit the bound histogram");
-// attention scratch: per-wave partials and up to 32 chunk partials of D+2
-constexpr int kAttnScratchWords = 8 + 4 * 128 + 8 + 32 * (128 + 2);
-static_assert(kLIdx + kAttnScratchWords <= Lay<true>::c, "attention scratch fits");
-// both queries' (dual-token) attention scratch: the tail of region C for a
-// cached row, the candidate lists otherwise (both free once emitted)
-constexpr int kAttnScratchWords2 = 2 * (8 + 4 * 128) + 8 + 2 * 32 * (128 + 2);
-static_assert(Lay<true>::end + kAttnScratchWords2 <= Lay<true>::words, "dual scratch fits (cached)");
-static_assert(kLIdx + kAttnScratchWords2 <= Lay<false>::c, "dual scratch fits (long rows)");
+// attention scratch, both queries (dual-token): per-wave partials and up to
+// 32 chunk partials of D+2 each; the tail of region C for a cached row, the
+// candidate lists otherwise (both free once the selection is emitted)
+constexpr int kAttnScratchWords = 2 * (8 + 4 * 128) + 8 + 2 * 32 * (128 + 2);
+static_assert(Lay<true>::end + kAttnScratchWords <= Lay<true>::words, "dual scratch fits (cached)");
+static_assert(kLIdx + kAttnScratchWords <= Lay<false>::c, "dual scratch fits (long rows)");
 
 __device__ __forceinline__ void clear(uint32_t* p, int words) {
   for (int i = threadIdx.x; i < words; i += kNT) p[i] = 0u;
@@ -698,14 +696,17 @@ __device__ __forceinline__ int radix_select(const float* __restrict__ row, int n
 // the attention kernel, chunk partials merged the same way.  With selection
 // by chunk landmarks (cs > 0) each of the ks selected entries stands for the
 // 2^cs consecutive rows of its chunk, rows past the request's length left
-// out; the slot holds them at 2^cs times the entry's slot position.  NQ = 2:
-// the speculated query (plane 1) attends over the same rows too, each K/V
-// row read once for both (the dual-token pipeline runs both tokens through
-// the layer).
-template <typename T, int D, int NQ>
+// out; the slot holds them at 2^cs times the entry's slot position.  With
+// out_spec set, the speculated query (plane 1) attends over the same rows
+// too, each K/V row read once for both (the dual-token pipeline runs both
+// tokens through the layer); the query count is a run-time value, so one
+// body per element type serves both cases.
+template <typename T, int D>
 __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, int ks,
                                                   int32_t len, const int32_t* lpos,
                                                   const int32_t* lcur, float* scratch) {
+  constexpr int NQ = 2;
+  const int nq = fa.out_spec != nullptr ? 2 : 1;
   AttnLds<D, NQ>& lds = *reinterpret_cast<AttnLds<D, NQ>*>(scratch);
   float* part = scratch + (sizeof(AttnLds<D, NQ>) + 15) / 16 * 4;
   const int cs = fa.chunk_shift;
@@ -721,6 +722,11 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
                       kdev ? static_cast<const T*>(fa.k_dev) + hslab : nullptr, 2 * k, k, n_rows};
   const int cmask = (1 << cs) - 1;
   auto entry = [&](int j, int& r, int& c) {
+    if (cs == 0) {  // one row per entry
+      r = lpos[j];
+      c = lcur[j];
+      return;
+    }
     const int e = j >> cs;
     const int i = j & cmask;
     const int pe = lpos[e];
@@ -737,10 +743,9 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
   const int d = threadIdx.x;
   for (int ch = 0; ch < chunks; ++ch) {
     float cm[NQ], cl[NQ], od[NQ];
-    attend_chunk_n<T, D, NQ>(qrow, R, ch * kAttnChunk, k, fa.scale, entry, lds, cm, cl, od);
+    attend_chunk_n<T, D, NQ>(qrow, R, ch * kAttnChunk, k, fa.scale, entry, lds, nq, cm, cl, od);
     if (d < D) {
-#pragma unroll
-      for (int qi = 0; qi < NQ; ++qi) {
+      for (int qi = 0; qi < nq; ++qi) {
         if (chunks == 1) {
           outs[qi][(int64_t)bh * D + d] = (cl[qi] > 0.f) ? od[qi] / cl[qi] : 0.f;
           if (d == 0 && lses[qi] != nullptr)
@@ -758,8 +763,7 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
     __syncthreads();  // lds is reused by the next chunk; partials complete
   }
   if (chunks > 1 && d < D) {
-#pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) {
+    for (int qi = 0; qi < nq; ++qi) {
       float o, l;
       combine_chunks<D>(part + qi * chunks * (D + 2), chunks, d, o, l);
       outs[qi][(int64_t)bh * D + d] = o;
@@ -768,27 +772,16 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
   }
 }
 
-// scratch: LDS for one query's attention (kAttnScratchWords); scratch2: for
-// both queries' (kAttnScratchWords2), used when the speculated query attends.
+// scratch: LDS for the attention of both queries (kAttnScratchWords).
 __device__ __forceinline__ void fused_attention(const FusedAttn& fa, int bh, int ks, int32_t len,
                                                 const int32_t* lpos, const int32_t* lcur,
-                                                float* scratch, float* scratch2) {
-  if (fa.out_spec != nullptr) {
-    if (fa.dtype == kBF16) {
-      if (fa.D == 128) fused_attention_t<uint16_t, 128, 2>(fa, bh, ks, len, lpos, lcur, scratch2);
-      else fused_attention_t<uint16_t, 64, 2>(fa, bh, ks, len, lpos, lcur, scratch2);
-    } else {
-      if (fa.D == 128) fused_attention_t<float, 128, 2>(fa, bh, ks, len, lpos, lcur, scratch2);
-      else fused_attention_t<float, 64, 2>(fa, bh, ks, len, lpos, lcur, scratch2);
-    }
-    return;
-  }
+                                                float* scratch) {
   if (fa.dtype == kBF16) {
-    if (fa.D == 128) fused_attention_t<uint16_t, 128, 1>(fa, bh, ks, len, lpos, lcur, scratch);
-    else fused_attention_t<uint16_t, 64, 1>(fa, bh, ks, len, lpos, lcur, scratch);
+    if (fa.D == 128) fused_attention_t<uint16_t, 128>(fa, bh, ks, len, lpos, lcur, scratch);
+    else fused_attention_t<uint16_t, 64>(fa, bh, ks, len, lpos, lcur, scratch);
   } else {
-    if (fa.D == 128) fused_attention_t<float, 128, 1>(fa, bh, ks, len, lpos, lcur, scratch);
-    else fused_attention_t<float, 64, 1>(fa, bh, ks, len, lpos, lcur, scratch);
+    if (fa.D == 128) fused_attention_t<float, 128>(fa, bh, ks, len, lpos, lcur, scratch);
+    else fused_attention_t<float, 64>(fa, bh, ks, len, lpos, lcur, scratch);
   }
 }
 
@@ -820,7 +813,8 @@ __global__ __launch_bounds__(kNT) void k_topk(
     pv[r] = (pred_row != nullptr && p < k) ? pred_row[p] : -1;
   }
   clear(smem + kLHist, kBins);
-  const int n = (int)chunk_len(lens[bh / H], len_shift, n_max);
+  const int32_t len_b = lens[bh / H];
+  const int n = (int)chunk_len(len_b, len_shift, n_max);
   int misses = 0, fetchable = 0;
 
   if (n <= k) {
@@ -880,7 +874,7 @@ __global__ __launch_bounds__(kNT) void k_topk(
               (unsigned long long)(fetchable + misses));
   }
   __syncthreads();  // every entry's slot row and row index are in LDS
-  fused_attention(fa, bh, k, lens[bh / H], sk.lpos, sk.lcur, reinterpret_cast<float*>(smem + kLIdx),
+  fused_attention(fa, bh, k, len_b, sk.lpos, sk.lcur,
                   reinterpret_cast<float*>(smem + (CACHED ? Lay<true>::end : kLIdx)));
 }
 
