@@ -286,7 +286,7 @@ DD_API int dd_sparse_attn(const float* q, int64_t q_stride_bh, const void* k_row
     return fail(DD_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", need, ws_bytes);
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
   hipError_t e = dd::launch_attn(q, q_stride_bh, k_rows, v_rows, pos, cnt, B, H, k, m, D, dtype,
-                                 sc, out, lse, ws, nullptr, nullptr, nullptr, stream);
+                                 sc, out, lse, ws, stream);
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   return DD_OK;
 }
@@ -488,14 +488,13 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     // right after its selection, reading misses from host memory itself
     // (and storing them into their slot rows k + t); K rows come from the
     // scoring copy when kdev.
-    const dd::TopkBook book{P, nullptr, nullptr, nullptr};
     const dd::FusedAttn fa{a->q[l], kslot, vslot, a->k_host[l], a->v_host[l],
                            kdev ? a->k_dev[l] : nullptr, a->n_max, cs, D, a->dtype, sc,
                            a->out[l], a->lse ? a->lse[l] : nullptr, st,
                            a->out_spec ? a->out_spec[l] : nullptr,
                            (a->out_spec && a->out_spec[l] && a->lse_spec) ? a->lse_spec[l] : nullptr};
     e = dd::launch_topk(scores, a->lens, B, H, 2, n_sel, ks, a->cur_idx[l], a->spec_idx[l], ks,
-                        &book, &fa, ms, cs);
+                        P, &fa, ms, cs);
     if (e != hipSuccess) return hip_fail(e, "top-k and attention kernel launch");
     for (int ev = 2; ev <= 4; ++ev)
       if (tev(l, ev)) DD_CHECK_HIP(hipEventRecord(tev(l, ev), ms), "timing");

@@ -14,39 +14,13 @@ namespace dd {
 
 namespace {
 
-// Sums the per-slab counts of the layer step (misses, hits, fetchable
-// prediction entries) into stats = {misses, hits, rows over the host link}.
-__device__ __forceinline__ void write_stats(const int32_t* __restrict__ counts, int BH,
-                                            int64_t* __restrict__ stats) {
-  __shared__ unsigned long long s_acc[3];
-  if (threadIdx.x < 3) s_acc[threadIdx.x] = 0ull;
-  __syncthreads();
-  unsigned long long a0 = 0, a1 = 0, a2 = 0;
-  for (int t = threadIdx.x; t < BH; t += blockDim.x) {
-    a0 += (unsigned long long)counts[t];
-    a1 += (unsigned long long)counts[BH + t];
-    a2 += (unsigned long long)counts[2 * BH + t];
-  }
-  atomicAdd(&s_acc[0], a0);
-  atomicAdd(&s_acc[1], a1);
-  atomicAdd(&s_acc[2], a2);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    stats[0] = (int64_t)s_acc[0];
-    stats[1] = (int64_t)s_acc[1];
-    stats[2] = (int64_t)(s_acc[2] + s_acc[0]);
-  }
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(
     const float* __restrict__ q, int64_t q_stride, const T* __restrict__ krows,
     const T* __restrict__ vrows, const int32_t* __restrict__ pos, const int32_t* __restrict__ cnt,
     int BH, int k, int m, int chunks, float scale, float* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part, const int32_t* __restrict__ counts,
-    int64_t* __restrict__ stats, AttnMiss ms) {
+    float* __restrict__ lse, float* __restrict__ part) {
   __shared__ AttnLds<D> lds;
-  if (stats != nullptr && blockIdx.x == 0) write_stats(counts, BH, stats);
   int bh, c;
   xcd_tile_map(blockIdx.x, chunks, BH, bh, c);
   int lim = k;
@@ -54,16 +28,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_partial(
     const int cc = cnt[bh];
     lim = cc < 0 ? 0 : (cc > k ? k : cc);
   }
-  const bool from_host = ms.k_host != nullptr;
-  const AttnRows<T> R{krows + (int64_t)bh * m * D, vrows + (int64_t)bh * m * D,
-                      from_host ? static_cast<const T*>(ms.k_host) + (int64_t)bh * ms.n_max * D : nullptr,
-                      from_host ? static_cast<const T*>(ms.v_host) + (int64_t)bh * ms.n_max * D : nullptr,
-                      nullptr, m, ms.first_miss_row, ms.n_max};
+  // Rows come from the gathered buffer only (no host rows).
+  const AttnRows<T> R{krows + (int64_t)bh * m * D, vrows + (int64_t)bh * m * D, nullptr, nullptr,
+                      nullptr, m, m, 0};
   const int32_t* pos_bh = pos != nullptr ? pos + (int64_t)bh * k : nullptr;
-  const int32_t* cur_bh = from_host ? ms.cur + (int64_t)bh * k : nullptr;
   auto entry = [&](int j, int& r, int& hc) {
     r = (pos_bh != nullptr) ? pos_bh[j] : j;
-    if (cur_bh != nullptr) hc = cur_bh[j];
+    hc = -1;
   };
   float cm, cl, od;
   attend_chunk<T, D>(q + (int64_t)bh * q_stride, R, c * kAttnChunk, lim, scale, entry, lds, cm,
@@ -108,9 +79,6 @@ struct AttnLaunch {
   float* out;
   float* lse;
   void* ws;
-  const int32_t* counts;
-  int64_t* stats;
-  AttnMiss miss;
   hipStream_t s;
 };
 
@@ -120,8 +88,7 @@ hipError_t launch_attn_t(const AttnLaunch& a) {
   float* part = static_cast<float*>(a.ws);
   hipLaunchKernelGGL((k_attn_partial<T, D>), dim3(a.BH * chunks), dim3(kAttnThreads), 0, a.s,
                      a.q, a.q_stride, static_cast<const T*>(a.kr), static_cast<const T*>(a.vr),
-                     a.pos, a.cnt, a.BH, a.k, a.m, chunks, a.scale, a.out, a.lse, part, a.counts,
-                     a.stats, a.miss);
+                     a.pos, a.cnt, a.BH, a.k, a.m, chunks, a.scale, a.out, a.lse, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || chunks == 1) return e;
   hipLaunchKernelGGL((k_attn_combine<D>), dim3(a.BH), dim3(D), 0, a.s, part, chunks, a.out, a.lse);
@@ -139,14 +106,10 @@ size_t attn_workspace(int B, int H, int k, int D) {
 hipError_t launch_attn(const float* q, int64_t q_stride_bh, const void* k_rows,
                        const void* v_rows, const int32_t* pos, const int32_t* cnt, int B, int H,
                        int k, int m, int D, int dtype, float scale, float* out, float* lse,
-                       void* ws, const int32_t* counts, int64_t* stats, const AttnMiss* miss,
-                       hipStream_t s) {
+                       void* ws, hipStream_t s) {
   const int BH = B * H;
   if (BH == 0) return hipSuccess;
-  AttnLaunch a{q, q_stride_bh, k_rows, v_rows, pos, cnt, BH, k, m, scale, out, lse, ws, counts,
-               stats, AttnMiss{nullptr, nullptr, nullptr, 0, 0}, s};
-  if (miss != nullptr && miss->k_host != nullptr && miss->v_host != nullptr && miss->cur != nullptr)
-    a.miss = *miss;
+  AttnLaunch a{q, q_stride_bh, k_rows, v_rows, pos, cnt, BH, k, m, scale, out, lse, ws, s};
   if (dtype == kBF16) {
     if (D == 128) return launch_attn_t<uint16_t, 128>(a);
     return launch_attn_t<uint16_t, 64>(a);

@@ -43,14 +43,6 @@ hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, i
 hipError_t launch_softmax_rows(float* scores, const int32_t* lens, int B, int H, int Q,
                                int64_t n_max, hipStream_t s);
 
-// Prediction bookkeeping fused into the top-k of query plane 0.
-struct TopkBook {
-  const int32_t* pred;  // [BH][k] or nullptr (no prediction)
-  int32_t* pos;         // [BH][k] slot row of each selected entry
-  int32_t* miss;        // [BH][k] missed entries, ascending, -1 padded
-  int32_t* counts;      // [3][BH]: misses, hits, fetchable prediction entries
-};
-
 // Attention fused into the top-k of the layer step: after its bookkeeping,
 // the workgroup of each current-query row attends that query over the
 // selection (slot rows, misses read from host memory and stored into
@@ -77,13 +69,14 @@ struct FusedAttn {
 };
 
 // Top-k of each score row.  Plane j of slab bh is written at
-// (j == 0 ? out0 : out1) + bh * out_stride_bh.  book: bookkeeping of the
-// plane-0 rows (its pos / miss / counts outputs may each be null); attn:
-// the fused attention (needs book).  len_shift > 0: the scores are of chunk
-// landmarks of 2^len_shift rows, ceil(lens[b] / 2^len_shift) per request.
+// (j == 0 ? out0 : out1) + bh * out_stride_bh.  attn (or null): the plane-0
+// rows also do the prediction bookkeeping against pred ([BH][k], or null
+// for no prediction) and then the fused attention.  len_shift > 0: the
+// scores are of chunk landmarks of 2^len_shift rows, ceil(lens[b] /
+// 2^len_shift) per request.
 hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, int Q,
                        int64_t n_max, int k, int32_t* out0, int32_t* out1,
-                       int64_t out_stride_bh, const TopkBook* book, const FusedAttn* attn,
+                       int64_t out_stride_bh, const int32_t* pred, const FusedAttn* attn,
                        hipStream_t s, int len_shift = 0);
 
 // Row gather from pinned host memory.  Entry j < cnt[bh] (m if cnt is null)
@@ -98,24 +91,11 @@ hipError_t launch_gather(const void* k_host, const void* v_host, int64_t n_max, 
 
 size_t attn_workspace(int B, int H, int k, int D);
 
-// Rows the attention kernel reads straight from host memory: an entry j
-// whose row pos[j] is >= first_miss_row is host row cur[bh*k + j]; the
-// kernel also stores it into that row of k_rows / v_rows.
-struct AttnMiss {
-  const void* k_host;  // pinned host [BH][n_max][D]
-  const void* v_host;
-  const int32_t* cur;  // [BH][k]
-  int64_t n_max;
-  int first_miss_row;
-};
-
-// Sparse attention; when stats is set, workgroup 0 also writes stats[0..2]
-// = sums over slabs of the counts planes (misses, hits, fetchable + misses).
+// Sparse attention over gathered rows (entry j is row pos[j], or j).
 hipError_t launch_attn(const float* q, int64_t q_stride_bh, const void* k_rows,
                        const void* v_rows, const int32_t* pos, const int32_t* cnt, int B, int H,
                        int k, int m, int D, int dtype, float scale, float* out, float* lse,
-                       void* ws, const int32_t* counts, int64_t* stats, const AttnMiss* miss,
-                       hipStream_t s);
+                       void* ws, hipStream_t s);
 
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 

@@ -240,15 +240,12 @@ __device__ __forceinline__ void select_kth(const uint32_t* fkey, int cnt, int k,
 }
 
 // Where the selection goes: the output row and, for bookkeeping rows, the
-// prediction (in LDS) and its length, and the slot row of every entry and
-// the miss list in global memory and / or (for the fused attention) the
-// slot row and row index of every entry in LDS; each of those may be null.
+// prediction (in LDS) and its length, and the slot row (lpos) and row index
+// (lcur) of every selected entry, in LDS for the fused attention.
 struct Sink {
   int32_t* out;
   const int32_t* s_pred;  // nullptr: no bookkeeping
   int plen;
-  int32_t* pos;
-  int32_t* miss;
   int32_t* lpos;
   int32_t* lcur;
 };
@@ -312,10 +309,9 @@ __device__ __forceinline__ int emit_words(uint32_t (&g)[MAXW], const uint32_t (&
       }
       if (j < k) {
         sk.out[j] = c;
-        if (sk.lcur != nullptr) sk.lcur[j] = c;
+        sk.lcur[j] = c;
         if (hit >= 0) {
-          if (sk.pos != nullptr) sk.pos[j] = hit;
-          if (sk.lpos != nullptr) sk.lpos[j] = hit;
+          sk.lpos[j] = hit;
         } else {
           mm[w] |= 1u << b;
           ++my_miss;
@@ -333,9 +329,7 @@ __device__ __forceinline__ int emit_words(uint32_t (&g)[MAXW], const uint32_t (&
     for (uint32_t x = mm[w]; x != 0u; x &= x - 1u) {
       const int b = __ffs(x) - 1;
       const int jj = jb + __popc(g[w] & ((1u << b) - 1u));
-      if (sk.pos != nullptr) sk.pos[jj] = k + mr;
-      if (sk.lpos != nullptr) sk.lpos[jj] = k + mr;
-      if (sk.miss != nullptr) sk.miss[mr] = (w0 + w) * 32 + b;
+      sk.lpos[jj] = k + mr;
       ++mr;
     }
     jb += __popc(g[w]);
@@ -789,22 +783,19 @@ template <int G, bool CACHED>
 __global__ __launch_bounds__(kNT) void k_topk(
     const float* __restrict__ scores, const int32_t* __restrict__ lens, int H, int Q, int BH,
     int64_t n_max, int k, int32_t* __restrict__ out0, int32_t* __restrict__ out1,
-    int64_t out_stride, int book_on, const int32_t* __restrict__ pred, int32_t* __restrict__ pos,
-    int32_t* __restrict__ miss, int32_t* __restrict__ counts, FusedAttn fa, int len_shift) {
+    int64_t out_stride, const int32_t* __restrict__ pred, FusedAttn fa, int len_shift) {
   extern __shared__ uint32_t smem[];
   const int tid = threadIdx.x;
   int bh, j;
   xcd_tile_map(blockIdx.x, Q, BH, bh, j);
   const int64_t rowid = (int64_t)bh * Q + j;
   const float* row = scores + rowid * n_max;
-  const bool do_book = book_on && j == 0;
-  const bool attend = do_book && fa.q != nullptr;
+  // Bookkeeping and attention: the current-query rows, when attention is fused.
+  const bool do_book = fa.q != nullptr && j == 0;
   const int32_t* pred_row = (do_book && pred != nullptr) ? pred + (int64_t)bh * k : nullptr;
   Sink sk{((j == 0) ? out0 : out1) + (int64_t)bh * out_stride, nullptr, 0,
-          (do_book && pos != nullptr) ? pos + (int64_t)bh * k : nullptr,
-          (do_book && miss != nullptr) ? miss + (int64_t)bh * k : nullptr,
-          attend ? reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred) + kMaxK : nullptr,
-          attend ? reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred) + 2 * kMaxK : nullptr};
+          do_book ? reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred) + kMaxK : nullptr,
+          do_book ? reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred) + 2 * kMaxK : nullptr};
   // The prediction row, loaded now and stored in LDS once it is needed.
   int32_t pv[kPR];
 #pragma unroll
@@ -835,13 +826,8 @@ __global__ __launch_bounds__(kNT) void k_topk(
       if (c < k) {
         sk.out[c] = valid ? c : -1;
         if (do_book) {
-          const int pr = !valid ? -1 : (hit >= 0 ? hit : k + mr);
-          if (sk.pos != nullptr) sk.pos[c] = pr;
-          if (sk.lpos != nullptr) {
-            sk.lpos[c] = pr;
-            sk.lcur[c] = valid ? c : -1;
-          }
-          if (valid && hit < 0 && sk.miss != nullptr) sk.miss[mr] = c;
+          sk.lpos[c] = !valid ? -1 : (hit >= 0 ? hit : k + mr);
+          sk.lcur[c] = valid ? c : -1;
         }
       }
       misses += mtot;
@@ -857,15 +843,7 @@ __global__ __launch_bounds__(kNT) void k_topk(
   }
 
   if (!do_book) return;
-  if (sk.miss != nullptr)
-    for (int tt = misses + tid; tt < k; tt += kNT) sk.miss[tt] = -1;
   const int valid = n < k ? n : k;
-  if (tid == 0 && counts != nullptr) {
-    counts[bh] = misses;
-    counts[BH + bh] = valid - misses;
-    counts[2 * BH + bh] = fetchable;
-  }
-  if (!attend) return;
   if (tid == 0 && fa.stats != nullptr) {
     atomicAdd(reinterpret_cast<unsigned long long*>(fa.stats), (unsigned long long)misses);
     atomicAdd(reinterpret_cast<unsigned long long*>(fa.stats) + 1,
@@ -897,7 +875,7 @@ TopkKernel<CACHED> pick_kernel(int g) {
 
 hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, int Q,
                        int64_t n_max, int k, int32_t* out0, int32_t* out1,
-                       int64_t out_stride_bh, const TopkBook* book, const FusedAttn* attn,
+                       int64_t out_stride_bh, const int32_t* pred, const FusedAttn* attn,
                        hipStream_t s, int len_shift) {
   const int BH = B * H;
   if (BH == 0) return hipSuccess;
@@ -919,21 +897,14 @@ hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, i
     }
     attr_set[di.device] = true;
   }
-  const int book_on = book != nullptr ? 1 : 0;
-  const int32_t* pred = book_on ? book->pred : nullptr;
-  int32_t* pos = book_on ? book->pos : nullptr;
-  int32_t* miss = book_on ? book->miss : nullptr;
-  int32_t* counts = book_on ? book->counts : nullptr;
   FusedAttn fa{};
-  if (book_on && attn != nullptr) fa = *attn;
+  if (attn != nullptr) fa = *attn;
   if (cached) {
     hipLaunchKernelGGL(pick_kernel<true>(g), dim3(BH * Q), dim3(kNT), shmem, s, scores, lens, H, Q,
-                       BH, n_max, k, out0, out1, out_stride_bh, book_on, pred, pos, miss, counts,
-                       fa, len_shift);
+                       BH, n_max, k, out0, out1, out_stride_bh, pred, fa, len_shift);
   } else {
     hipLaunchKernelGGL(pick_kernel<false>(g), dim3(BH * Q), dim3(kNT), shmem, s, scores, lens, H,
-                       Q, BH, n_max, k, out0, out1, out_stride_bh, book_on, pred, pos, miss, counts,
-                       fa, len_shift);
+                       Q, BH, n_max, k, out0, out1, out_stride_bh, pred, fa, len_shift);
   }
   return hipGetLastError();
 }
