@@ -438,7 +438,7 @@ __device__ __forceinline__ uint32_t passing(const f32x4& v, int i, int n, float 
 template <int G, bool CACHED>
 __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int n, int64_t n_max, int k,
                               uint32_t* smem, Sink& sk, bool book, const int32_t (&pv)[kPR],
-                              int& misses, int& fetchable) {
+                              const f32x4 (&v0)[CACHED ? kU : 1], int& misses, int& fetchable) {
   using L = Lay<CACHED>;
   constexpr int CAP = L::cap;
   constexpr int UPG = kU / G;  // float4s per group and tile
@@ -460,9 +460,14 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
   for (int tl = 0; tl < tiles; ++tl) {
     const int c0 = tl * kTile;
     f32x4 v[kU];
-    // A cached row is loaded over its whole storage, so that the loads need
-    // not wait for its length.
-    load_tile(row, CACHED ? (int)n_max : n, c0, vec, v);
+    // A cached row was loaded over its whole storage at kernel entry (v0),
+    // so that the loads need not wait for its length.
+    if constexpr (CACHED) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] = v0[u];
+    } else {
+      load_tile(row, n, c0, vec, v);
+    }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int q = tid + kNT * u;
@@ -796,6 +801,14 @@ __global__ __launch_bounds__(kNT) void k_topk(
   Sink sk{((j == 0) ? out0 : out1) + (int64_t)bh * out_stride, nullptr, 0,
           do_book ? reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred) + kMaxK : nullptr,
           do_book ? reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred) + 2 * kMaxK : nullptr};
+  // A row that fits one tile is loaded now, before its length is known
+  // (over its whole storage), so that the loads overlap those of the length
+  // and the prediction.
+  f32x4 v0[CACHED ? kU : 1];
+  if constexpr (CACHED) {
+    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0 && (n_max & 3) == 0;
+    load_tile(row, (int)n_max, 0, vec, v0);
+  }
   // The prediction row, loaded now and stored in LDS once it is needed.
   int32_t pv[kPR];
 #pragma unroll
@@ -835,7 +848,8 @@ __global__ __launch_bounds__(kNT) void k_topk(
   } else {
     bool done = false;
     if (n <= kFilterMaxN)
-      done = filter_select<G, CACHED>(row, n, n_max, k, smem, sk, do_book, pv, misses, fetchable);
+      done = filter_select<G, CACHED>(row, n, n_max, k, smem, sk, do_book, pv, v0, misses,
+                                      fetchable);
     if (!done) {
       sk.s_pred = nullptr;
       misses = radix_select<CACHED>(row, n, n_max, k, smem, sk, do_book, pv, fetchable);
