@@ -179,3 +179,79 @@ def test_chunk_layer_step_matches_oracle(name, kw, c, R):
     ctx.close()
     hctx.close()
     print(f"worst relative attention error {worst:.2e}")
+
+
+def test_chunk_ties_and_partial_tail_closed_form():
+    """Keys are zero except the rows of the partial last chunk (48..51 of 52,
+    chunk 8), which are 2q: that chunk's landmark scores 2|q|^2/sqrt(D) = 1
+    and every other chunk exactly 0.  With k = 16 (two chunks) the current
+    query takes chunk 6 and, among the tied zeros, chunk 0; the speculated
+    query -q takes chunks 0 and 1.  Attention over rows 0-7 (logit 0) and
+    48-51 (logit 1), V row i = i in column 0: (28 + 198 e) / (8 + 4 e).  With
+    the prediction {0, 1}, chunk 0 hits and chunk 6 misses."""
+    dd = require_gpu()
+    announce("chunk closed form (ties, partial tail)")
+    D, c, n, n_max = 64, 8, 52, 64
+    qv = torch.zeros(D)
+    qv[0] = 2.0
+    q = torch.stack([qv, -qv])[None, None].contiguous().cuda()          # [1][1][2][D]
+    keys = torch.zeros(1, 1, n_max, D)
+    keys[0, 0, 48:52] = 2 * qv
+    keys[0, 0, 52:] = 99.0                                              # padding
+    vals = torch.zeros(1, 1, n_max, D)
+    vals[0, 0, :, 0] = torch.arange(n_max, dtype=torch.float32)
+    vals[0, 0, :, 1] = 1.0
+    lens = torch.tensor([n], dtype=torch.int32).cuda()
+    k_dev = keys.cuda()
+    kh, vh = to_host(dd, keys), to_host(dd, vals)
+    lm = dd.landmarks(k_dev, lens, c)
+    ctx = dd.Context(ring_slots=1)
+    res = ctx.layer_step([q], [k_dev], [kh], [vh], lens, 16, chunk=c, landmarks=[lm], dual=True)
+    hot = ctx.layer_step([q], [k_dev], [kh], [vh], lens, 16, chunk=c, landmarks=[lm],
+                         pred=[torch.tensor([[[0, 1]]], dtype=torch.int32).cuda()])
+    torch.cuda.synchronize()
+    assert res["cur"][0].cpu().tolist() == [[[0, 6]]]
+    assert res["spec"][0].cpu().tolist() == [[[0, 1]]]
+    e = float(np.e)
+    out = res["out"][0][0, 0].cpu().numpy().astype(np.float64)
+    assert abs(out[0] - (28 + 198 * e) / (8 + 4 * e)) < 1e-5
+    assert abs(out[1] - 1.0) < 1e-6
+    assert abs(float(res["lse"][0][0, 0]) - np.log(8 + 4 * e)) < 1e-5
+    spec_out = res["out_spec"][0][0, 0].cpu().numpy().astype(np.float64)
+    assert abs(spec_out[0] - (28 + 198 / e) / (8 + 4 / e)) < 1e-5
+    assert hot["stats"][0].cpu().tolist() == [1, 1, 3]
+    assert torch.equal(hot["out"][0], res["out"][0])
+    ctx.close()
+
+
+def test_chunk_layer_step_full_size_7b():
+    """The 7B-shape layer at full size (32 heads x 32768 keys, k = 128) with
+    8-key chunks, against the oracle on every head."""
+    dd = require_gpu()
+    w = gen.workload("llama7b_32k_layer")
+    c = 8
+    announce(f"chunk layer_step full size {w.name} chunk={c}")
+    data = _stage(dd, w, c)
+    ctx = dd.Context(ring_slots=2)
+    cold = _run(ctx, w, data, c)
+    hot = _run(ctx, w, data, c, pred=[s.clone() for s in cold["spec"]])
+    for key in ("out", "lse", "cur", "spec"):
+        assert torch.equal(hot[key][0], cold[key][0]), key
+    d = data[0]
+    lens = d["lens"].numpy()
+    kst, vst = stored(d["k"]), stored(d["v"])
+    ref = oracle.layer_step(d["q"].numpy(), kst, kst, vst, lens, w.k, w.dtype, chunk=c)
+    B, H, ks = w.B, w.H, w.k // c
+    nlen = np.repeat(-(-lens // c), H)
+    cur = hot["cur"][0].cpu().numpy()
+    parity.check_index_sets(cur.reshape(B * H, ks), ref["cur"].reshape(B * H, ks),
+                            ref["scores"][:, :, 0].reshape(B * H, -1), nlen, ks)
+    parity.check_index_sets(hot["spec"][0].cpu().numpy().reshape(B * H, ks),
+                            ref["spec"].reshape(B * H, ks),
+                            ref["scores"][:, :, 1].reshape(B * H, -1), nlen, ks)
+    rows = oracle.chunk_rows(cur, lens, c)
+    want, _ = oracle.masked_attention(d["q"][:, :, 0].numpy(), kst, vst, lens, rows, w.dtype)
+    got = hot["out"][0].cpu().numpy().reshape(B * H, w.D)
+    worst = parity.check_attention(got, want.reshape(B * H, w.D), np.zeros(B * H))
+    ctx.close()
+    print(f"worst relative attention error {worst:.2e}")
