@@ -190,7 +190,9 @@ __device__ __forceinline__ void pick_bin(const uint32_t* hist, int kr, ScanBufs&
 // registers; pass p counts into its own 256-counter histogram h4 + 256 p,
 // cleared by the caller before a barrier that precedes this call.  After
 // each pass's barrier every wave scans the histogram itself, so T needs no
-// broadcast.
+// broadcast.  When the chosen digit's keys are exactly the ones still
+// needed, all of them are taken and the passes stop: T is then just below
+// the digit's lowest key and no key equal to T is taken.
 template <int CAP>
 __device__ __forceinline__ void select_kth(const uint32_t* fkey, int cnt, int k, uint32_t* h4,
                                            uint32_t& thr, int& take_eq) {
@@ -217,23 +219,32 @@ __device__ __forceinline__ void select_kth(const uint32_t* fkey, int cnt, int k,
     const int excl = incl - sum;
     const uint64_t hit = __ballot(excl < kr && incl >= kr);
     const int src = (int)__builtin_ctzll(hit);
-    int a = excl, d = 252 - 4 * lane;
+    int a = excl, d = 252 - 4 * lane, cd = (int)c.x;
     if (a + (int)c.w >= kr) {
       d += 3;
+      cd = (int)c.w;
     } else if (a + (int)(c.w + c.z) >= kr) {
       a += (int)c.w;
       d += 2;
+      cd = (int)c.z;
     } else if (a + (int)(c.w + c.z + c.y) >= kr) {
       a += (int)(c.w + c.z);
       d += 1;
+      cd = (int)c.y;
     } else {
       a += (int)(c.w + c.z + c.y);
     }
     d = __builtin_amdgcn_readlane(d, src);
     a = __builtin_amdgcn_readlane(a, src);
+    cd = __builtin_amdgcn_readlane(cd, src);
     kr -= a;
     prefix |= (uint32_t)d << shift;
     pmask |= 255u << shift;
+    if (kr == cd && prefix != 0u) {  // every key of this digit is taken
+      thr = prefix - 1u;
+      take_eq = 0;
+      return;
+    }
   }
   thr = prefix;
   take_eq = kr;
