@@ -435,6 +435,11 @@ __device__ __forceinline__ float max_valid(const f32x4& v, int i, int n) {
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
+// Component c of v, with no indexing into registers.
+__device__ __forceinline__ float f4_at(const f32x4& v, int c) {
+  return c == 0 ? v.x : (c == 1 ? v.y : (c == 2 ? v.z : v.w));
+}
+
 // Entries of float4 v (first entry i) below n and >= fb, as bits 0..3.
 __device__ __forceinline__ uint32_t passing(const f32x4& v, int i, int n, float fb) {
   return ((i < n && v.x >= fb) ? 1u : 0u) | ((i + 1 < n && v.y >= fb) ? 2u : 0u) |
@@ -517,16 +522,19 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
     }
     int off = block_scan<kNW>(my, sb, cnt);
     if (cnt > CAP) return false;
+    // Each candidate's index and key, from the float4 it sits in.
 #pragma unroll 1
     for (uint32_t x = um; x != 0u; x &= x - 1u) {
       const int q = tid + kNT * (__ffs(x) - 1);
+      const f32x4 f = reinterpret_cast<const f32x4*>(regc)[q];
 #pragma unroll 1
-      for (uint32_t m = passing(reinterpret_cast<const f32x4*>(regc)[q], 4 * q, n, fb); m != 0u;
-           m &= m - 1u)
-        fidx[off++] = 4 * q + __ffs(m) - 1;
+      for (uint32_t m = passing(f, 4 * q, n, fb); m != 0u; m &= m - 1u) {
+        const int c = __ffs(m) - 1;
+        fidx[off] = 4 * q + c;
+        fkey[off] = order_key(f4_at(f, c));
+        ++off;
+      }
     }
-    __syncthreads();
-    for (int i = tid; i < cnt; i += kNT) fkey[i] = order_key(__uint_as_float(regc[fidx[i]]));
   } else {
     cnt = 0;
     for (int tl = 0; tl < tiles; ++tl) {
