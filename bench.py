@@ -108,6 +108,90 @@ def decode_loop(dd, gen, w, lay, kh, vh, k_dev, lens, steps: int, chunk: int, de
             "recall_per_step": recall}
 
 
+def components(dd, gen, w, kh, vh, h2d_gbps: float, dev, reps: int = 6):
+    """The gather and the sparse attention measured alone at sizes where
+    their own rate shows (inside the layer step the first runs beside the
+    scorer and the second handles only k rows per head):
+
+    gather: dd_gather of 4096 distinct random rows per head of K and V from
+      the pinned host cache of this workload (row by row), and
+      dd_gather_chunks of the same number of rows as 512 chunks of 8;
+    attention: dd_sparse_attn over k = 1024 resident bf16 rows per head at
+      the 32-layer 7B step's per-layer shape (16 requests x 32 heads x 128),
+      ten calls back to back on two alternating copies of the rows (so they
+      are not served from the Infinity Cache), time per call."""
+    import numpy as np
+    import torch
+    from sparse_kv_retrieval_dual_amd.hipevents import EventSet
+
+    B, H, D = w.B, w.H, w.D
+    eb = w.elem_bytes
+    g = torch.Generator().manual_seed(7)
+    n = int(gen.request_lens(w).min().item())      # rows valid in every request
+    m = min(4096, n)
+    idx = torch.stack([torch.randperm(n, generator=g)[:m]
+                       for _ in range(B * H)]).view(B, H, m).to(torch.int32).to(dev)
+    ko = torch.empty(B, H, m, D, dtype=w.torch_dtype, device=dev)
+    vo = torch.empty_like(ko)
+    c = 8
+    cidx = torch.stack([torch.randperm(n // c, generator=g)[:m // c]
+                        for _ in range(B * H)]).view(B, H, m // c).to(torch.int32).to(dev)
+    ev = EventSet(2)
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            ev.record(0)
+            fn()
+            ev.record(1)
+            torch.cuda.synchronize()
+            ts.append(ev.elapsed_ms(0, 1))
+        return float(np.median(ts))
+
+    gbytes = 2 * B * H * m * D * eb
+    t_rows = timed(lambda: dd.gather(kh, vh, idx, k_out=ko, v_out=vo))
+    t_chunks = timed(lambda: dd.gather_chunks(kh, vh, cidx, c, k_out=ko, v_out=vo))
+    del ko, vo
+
+    sw = gen.workload("llama7b_32k_step")
+    aB, aH, ak, aD = sw.B, sw.H, sw.k, sw.D
+    rows = [(torch.randn(aB, aH, ak, aD, device=dev).to(sw.torch_dtype),
+             torch.randn(aB, aH, ak, aD, device=dev).to(sw.torch_dtype)) for _ in range(2)]
+    q = torch.randn(aB, aH, 2, aD, device=dev)
+    out = torch.empty(aB, aH, aD, dtype=torch.float32, device=dev)
+    lse = torch.empty(aB, aH, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, dd.attn_workspace_bytes(aB, aH, ak, aD)), dtype=torch.uint8, device=dev)
+    abytes = 2 * aB * aH * ak * aD * sw.elem_bytes + aB * aH * aD * 4 * 2 + aB * aH * 4
+    # Calls back to back between the events (the copies alternate), so that
+    # the host's launch time is hidden behind the GPU's work.
+    per = 10
+    ts = []
+    for i in range(reps + 2):
+        ev.record(0)
+        for j in range(per):
+            kr, vr = rows[j % 2]
+            dd.sparse_attn(q, kr, vr, k=ak, out=out, lse=lse, ws=ws)
+        ev.record(1)
+        torch.cuda.synchronize()
+        if i >= 2:
+            ts.append(ev.elapsed_ms(0, 1) / per)
+    t_attn = float(np.median(ts))
+    del rows
+    return {
+        "gather_rows": {"rows_per_head": m, "planes": 2, "bytes": gbytes, "us": t_rows * 1e3,
+                        "GBps": gbytes / (t_rows * 1e-3) / 1e9,
+                        "frac_of_h2d": gbytes / (t_rows * 1e-3) / 1e9 / h2d_gbps},
+        "gather_chunks8": {"chunks_per_head": m // c, "planes": 2, "bytes": gbytes,
+                           "us": t_chunks * 1e3, "GBps": gbytes / (t_chunks * 1e-3) / 1e9,
+                           "frac_of_h2d": gbytes / (t_chunks * 1e-3) / 1e9 / h2d_gbps},
+        "sparse_attention": {"shape": f"B={aB} H={aH} k={ak} D={aD} {sw.dtype}",
+                             "algorithmic_bytes": abytes, "us": t_attn * 1e3,
+                             "GBps": abytes / (t_attn * 1e-3) / 1e9,
+                             "frac": abytes / (t_attn * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+    }
+
+
 def cpu_baseline(w, lay, budget_s: float):
     """The oracle as it stands, single-threaded, on the same workload; it
     repeats the whole layer until about budget_s seconds have passed."""
@@ -157,6 +241,8 @@ def main():
                     help="select by landmarks of chunks of this many keys (0: every key)")
     ap.add_argument("--dual", action="store_true",
                     help="the speculated query also attends over the selected rows")
+    ap.add_argument("--no-components", action="store_true",
+                    help="skip the stand-alone gather and attention measurements")
     ap.add_argument("--decode-steps", type=int, default=0,
                     help="also time this many real decode steps (KV append + layer step, "
                          "prediction carried), after the headline measurement")
@@ -355,6 +441,7 @@ def main():
         h2d.append(big.numel() / (ev.elapsed_ms(0, 1) * 1e-3) / 1e9)
     h2d_gbps = float(np.median(h2d))
     del big, big2, hpin
+    comp = None if args.no_components else components(dd, gen, w, kh, vh, h2d_gbps, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -402,6 +489,8 @@ def main():
                        "recall": hits / max(valid, 1), "miss_bytes": miss_bytes,
                        "unit": "keys" if chunk == 1 else f"chunks of {chunk} keys"},
     }
+    if comp is not None:
+        result["components"] = comp
     if lm_info is not None:
         result["landmarks_build"] = lm_info
     if args.decode_steps > 0:

@@ -136,7 +136,6 @@ DD_API int dd_gather(const void* k_host, const void* v_host, const int32_t* idx,
                      const int32_t* cnt, int B, int H, int m, int D, int64_t n_max,
                      int dtype, void* k_rows, void* v_rows, hipStream_t stream);
 
-/* Workspace bytes dd_sparse_attn needs for these sizes (0 is possible). */
 /* Chunk gather (arXiv page, section 2.2: the GPU picks important chunks
  * and retrieves their entries from host memory).  Entry j < cnt[b][h] (m if
  * cnt is NULL) names chunk idx[b][h][j]: its `chunk` consecutive host rows
@@ -180,6 +179,8 @@ DD_API int dd_kv_append(void* k_dev, void* k_host, void* v_host, const void* new
                         int D, int64_t n_max, int dtype, int chunk, float* landmarks,
                         hipStream_t stream);
 
+/* Workspace bytes dd_sparse_attn needs for these sizes (0 when k <= 128:
+ * one chunk, nothing to merge).  It holds the chunk partials. */
 DD_API size_t dd_attn_workspace(int B, int H, int k, int D);
 
 /* Decode attention over gathered rows only (Figure 1 "Attention" on the
@@ -196,7 +197,9 @@ DD_API size_t dd_attn_workspace(int B, int H, int k, int D);
  *            when no entry takes part.
  *   lse      device fp32 [B][H] or NULL: log-sum-exp of the scaled logits
  *            (-inf when no entry takes part).
- *   ws       device workspace of at least dd_attn_workspace(B, H, k, D) bytes.
+ *   ws       device workspace of at least dd_attn_workspace(B, H, k, D) bytes
+ *            (no initial contents needed; calls that overlap on one
+ *            workspace race).
  * The reduction order depends only on j, never on pos, so the result for
  * a given list of rows is bitwise the same wherever the rows sit.
  */

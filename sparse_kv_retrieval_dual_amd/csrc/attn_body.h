@@ -68,31 +68,35 @@ struct AttnLds {
   float o[NQ][kAttnWaves][D];
 };
 
-// Entries c0 .. c0 + 127 (those < lim) for the first nq <= NQ queries at
-// once: query j is q + j * D (D floats; all NQ are read).  Every K and V row
-// is read once and serves every query.  Contraction is off: only the
-// explicit fmaf calls fuse, so a query's result is the same bits whatever
-// nq is.  entry(j, r, c) gives entry j's slot row r (-1: skipped) and host
-// row c.  Afterwards cm[j] and cl[j] (all threads) are query j's max logit
-// and weight sum over the chunk, and threads d < D hold od[j] = its weighted
-// V sum of column d.  The caller must not touch lds until a barrier after
-// this returns.
-template <typename T, int D, int NQ, class Entry>
-__device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, const AttnRows<T>& R,
-                                               int c0, int lim, float scale, Entry entry,
-                                               AttnLds<D, NQ>& lds, int nq, float (&cm)[NQ],
-                                               float (&cl)[NQ], float (&od)[NQ]) {
-#pragma clang fp contract(off)
+// The rows of one chunk in registers: entry slot rows (-1: skipped), the
+// host row of each miss (-1 otherwise) and every entry's K and V bytes.
+template <typename T, int D>
+struct AttnFetch {
   using S = AttnShape<T, D>;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  int rows[S::U];
+  int hrow[S::U];
+  u32x4 kr[S::U], vr[S::U];
+};
+
+// First half of a chunk (entries c0 .. c0 + 127 below lim, handled by the
+// 256 threads tid = 0 .. 255): resolves each
+// entry's rows through entry(j, r, c) (slot row r, -1: skipped; host row c)
+// and issues its K and V loads, all at once (slot rows and device keys from
+// HBM, missed rows over the host link); a skipped entry reads row 0 of the
+// slab (when there is one) and is masked later.  Nothing waits for the
+// loads here, so a caller can fetch the next chunk before it finishes this
+// one.
+template <typename T, int D, class Entry>
+__device__ __forceinline__ void attn_fetch(const AttnRows<T>& R, int c0, int lim, Entry entry,
+                                           AttnFetch<T, D>& f, int tid) {
+  using S = AttnShape<T, D>;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int col = lane % S::LPR;
   const int rsub = lane / S::LPR;
   const int e0 = c0 + wave * kWaveEntries;  // this wave's first entry
   const bool from_host = R.vhb != nullptr;
   const bool kdev = R.kdb != nullptr;
-  int rows[S::U];
-  int hrow[S::U];  // host row of a miss, else -1
   int krow[S::U];  // row of the device key copy (kdev), else -1
 #pragma unroll
   for (int u = 0; u < S::U; ++u) {
@@ -105,45 +109,73 @@ __device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, cons
     const bool cvalid = c >= 0 && (int64_t)c < R.n_max;
     const bool miss = r >= R.first_miss_row && from_host;
     if ((miss || kdev) && !cvalid) r = -1;
-    rows[u] = r;
-    hrow[u] = (r >= 0 && miss) ? c : -1;
+    f.rows[u] = r;
+    f.hrow[u] = (r >= 0 && miss) ? c : -1;
     krow[u] = (r >= 0 && kdev) ? c : -1;
   }
-  // K and V of every entry in flight together (slot rows and device keys
-  // from HBM, missed rows over the host link); a skipped entry reads row 0
-  // of the slab (when there is one) and is masked below.
   const T* kb = R.kb + col * S::EPL;
   const T* vb = R.vb + col * S::EPL;
   const T* khb = (from_host && !kdev) ? R.khb + col * S::EPL : kb;
   const T* vhb = from_host ? R.vhb + col * S::EPL : vb;
   const T* kdb = kdev ? R.kdb + col * S::EPL : kb;
+  // Streaming (non-temporal) loads: every row is read once.  One store per
+  // element (values selected, not addresses), so the fetch stays in
+  // registers.
+  const bool any = R.m > 0;
+#pragma unroll
+  for (int u = 0; u < S::U; ++u) {
+    u32x4 kv = u32x4{0u, 0u, 0u, 0u};
+    u32x4 vv = kv;
+    if (any) {
+      const bool h = f.hrow[u] >= 0;
+      const int64_t off = (int64_t)(h ? f.hrow[u] : (f.rows[u] >= 0 ? f.rows[u] : 0)) * D;
+      const int64_t koff = (int64_t)(krow[u] >= 0 ? krow[u] : 0) * D;
+      kv = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(kdev ? kdb + koff : (h ? khb : kb) + off));
+      vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>((h ? vhb : vb) + off));
+    }
+    f.kr[u] = kv;
+    f.vr[u] = vv;
+  }
+}
+
+// Second half of a chunk fetched by attn_fetch (tid: the thread's index in
+// the 256 that handle the chunk; every thread of the workgroup must call
+// it, since it holds a workgroup barrier), for the first nq <= NQ
+// queries at once: query j is q + j * D (D floats; all NQ are read).  Every
+// K and V row is read once and serves every query; a missed row is first
+// copied into its slot row.  Contraction is off: only the explicit fmaf
+// calls fuse, so a query's result is the same bits whatever nq is.
+// Afterwards cm[j] and cl[j] (all threads) are query j's max logit and
+// weight sum over the chunk, and threads d < D hold od[j] = its weighted V
+// sum of column d.  The caller must not touch lds until a barrier after
+// this returns.
+template <typename T, int D, int NQ>
+__device__ __forceinline__ void attn_finish(const float* __restrict__ q, const AttnRows<T>& R,
+                                            float scale, const AttnFetch<T, D>& f,
+                                            AttnLds<D, NQ>& lds, int nq, float (&cm)[NQ],
+                                            float (&cl)[NQ], float (&od)[NQ], int tid) {
+#pragma clang fp contract(off)
+  using S = AttnShape<T, D>;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane % S::LPR;
+  const int rsub = lane / S::LPR;
+  const bool from_host = R.vhb != nullptr;
+  const bool kdev = R.kdb != nullptr;
   const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-  u32x4 kr[S::U], vr[S::U];
-  if (R.m > 0) {
+  if (from_host && R.m > 0) {  // the slot keeps a copy of every fetched miss
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
-      const bool h = hrow[u] >= 0;
-      const int64_t off = (int64_t)(h ? hrow[u] : (rows[u] >= 0 ? rows[u] : 0)) * D;
-      const int64_t koff = (int64_t)(krow[u] >= 0 ? krow[u] : 0) * D;
-      kr[u] = *reinterpret_cast<const u32x4*>(kdev ? kdb + koff : (h ? khb : kb) + off);
-      vr[u] = *reinterpret_cast<const u32x4*>((h ? vhb : vb) + off);
-    }
-    if (from_host) {  // the slot keeps a copy of every fetched miss
-#pragma unroll
-      for (int u = 0; u < S::U; ++u) {
-        if (hrow[u] >= 0) {
-          T* vd = const_cast<T*>(vb) + (int64_t)rows[u] * D;
-          *reinterpret_cast<u32x4*>(vd) = vr[u];
-          if (!kdev) {
-            T* kd = const_cast<T*>(kb) + (int64_t)rows[u] * D;
-            *reinterpret_cast<u32x4*>(kd) = kr[u];
-          }
+      if (f.hrow[u] >= 0) {
+        T* vd = const_cast<T*>(R.vb) + col * S::EPL + (int64_t)f.rows[u] * D;
+        *reinterpret_cast<u32x4*>(vd) = f.vr[u];
+        if (!kdev) {
+          T* kd = const_cast<T*>(R.kb) + col * S::EPL + (int64_t)f.rows[u] * D;
+          *reinterpret_cast<u32x4*>(kd) = f.kr[u];
         }
       }
     }
-  } else {
-#pragma unroll
-    for (int u = 0; u < S::U; ++u) kr[u] = vr[u] = zero;
   }
   float qr[NQ][S::EPL];
 #pragma unroll
@@ -158,11 +190,11 @@ __device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, cons
     if (qi >= nq) break;
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
-      float f[S::EPL];
-      Unpack<T>::run(kr[u], f);
+      float fk[S::EPL];
+      Unpack<T>::run(f.kr[u], fk);
       float a = 0.f;
 #pragma unroll
-      for (int e = 0; e < S::EPL; ++e) a = fmaf(f[e], qr[qi][e], a);
+      for (int e = 0; e < S::EPL; ++e) a = fmaf(fk[e], qr[qi][e], a);
       s[qi * S::U + u] = a;
     }
     group_allreduce<S::LPR, S::U>(s + qi * S::U);
@@ -176,7 +208,7 @@ __device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, cons
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
       float& x = s[qi * S::U + u];
-      x = (rows[u] >= 0) ? x * scale : -INFINITY;
+      x = (f.rows[u] >= 0) ? x * scale : -INFINITY;
       mx = fmaxf(mx, x);
     }
 #pragma unroll
@@ -187,12 +219,14 @@ __device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, cons
     for (int e = 0; e < S::EPL; ++e) o[e] = 0.f;
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
-      const float w = (rows[u] >= 0) ? exp2f((s[qi * S::U + u] - mx) * kLog2e) : 0.f;
+      const float w = (f.rows[u] >= 0) ? exp2f((s[qi * S::U + u] - mx) * kLog2e) : 0.f;
       l += w;
-      float f[S::EPL];
-      Unpack<T>::run(rows[u] >= 0 ? vr[u] : zero, f);
+      float fv[S::EPL];
+      u32x4 vv = f.vr[u];  // a value select: selecting lvalues would put both in memory
+      if (f.rows[u] < 0) vv = zero;
+      Unpack<T>::run(vv, fv);
 #pragma unroll
-      for (int e = 0; e < S::EPL; ++e) o[e] = fmaf(w, f[e], o[e]);
+      for (int e = 0; e < S::EPL; ++e) o[e] = fmaf(w, fv[e], o[e]);
     }
 #pragma unroll
     for (int off = S::LPR; off < 64; off <<= 1) {
@@ -212,7 +246,7 @@ __device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, cons
   __syncthreads();
 
   // Merge the waves (entry order is fixed: wave 0, 1, 2, 3).
-  const int d = threadIdx.x;
+  const int d = tid;
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
     cm[qi] = -INFINITY;
@@ -222,17 +256,17 @@ __device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, cons
     float m = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) m = fmaxf(m, lds.m[qi][w]);
-    float f[kAttnWaves];
+    float fw[kAttnWaves];
     float tl = 0.f;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) {
-      f[w] = (lds.l[qi][w] > 0.f) ? exp2f((lds.m[qi][w] - m) * kLog2e) : 0.f;
-      tl = fmaf(lds.l[qi][w], f[w], tl);
+      fw[w] = (lds.l[qi][w] > 0.f) ? exp2f((lds.m[qi][w] - m) * kLog2e) : 0.f;
+      tl = fmaf(lds.l[qi][w], fw[w], tl);
     }
     float acc = 0.f;
     if (d < D) {
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) acc = fmaf(lds.o[qi][w][d], f[w], acc);
+      for (int w = 0; w < kAttnWaves; ++w) acc = fmaf(lds.o[qi][w][d], fw[w], acc);
     }
     cm[qi] = m;
     cl[qi] = tl;
@@ -240,16 +274,15 @@ __device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, cons
   }
 }
 
-// One query (see attend_chunk_n).
-template <typename T, int D, class Entry>
-__device__ __forceinline__ void attend_chunk(const float* __restrict__ q, const AttnRows<T>& R,
-                                             int c0, int lim, float scale, Entry entry,
-                                             AttnLds<D>& lds, float& cm, float& cl, float& od) {
-  float m[1], l[1], o[1];
-  attend_chunk_n<T, D, 1>(q, R, c0, lim, scale, entry, lds, 1, m, l, o);
-  cm = m[0];
-  cl = l[0];
-  od = o[0];
+// Entries c0 .. c0 + 127 (those < lim): attn_fetch, then attn_finish.
+template <typename T, int D, int NQ, class Entry>
+__device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, const AttnRows<T>& R,
+                                               int c0, int lim, float scale, Entry entry,
+                                               AttnLds<D, NQ>& lds, int nq, float (&cm)[NQ],
+                                               float (&cl)[NQ], float (&od)[NQ]) {
+  AttnFetch<T, D> f;
+  attn_fetch<T, D>(R, c0, lim, entry, f, threadIdx.x);
+  attn_finish<T, D, NQ>(q, R, scale, f, lds, nq, cm, cl, od, threadIdx.x);
 }
 
 // Merge of the chunk partials of one (b, h) by log-sum-exp, for column d:
@@ -260,9 +293,11 @@ __device__ __forceinline__ void combine_chunks(const float* p, int chunks, int d
                                                float& lse) {
 #pragma clang fp contract(off)
   float mx = -INFINITY;
+#pragma unroll 8
   for (int c = 0; c < chunks; ++c) mx = fmaxf(mx, p[c * (D + 2) + D]);
   float tot = 0.f, od = 0.f;
   if (mx > -INFINITY) {
+#pragma unroll 8
     for (int c = 0; c < chunks; ++c) {
       const float* pc = p + c * (D + 2);
       const float wsum = pc[D + 1];

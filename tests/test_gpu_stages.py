@@ -234,3 +234,60 @@ def test_attention_is_independent_of_row_placement():
     o1, l1 = dd.sparse_attn(q.cuda(), kr.cuda(), vr.cuda(), pos=pos.cuda())
     o2, l2 = dd.sparse_attn(q.cuda(), kr2.cuda(), vr2.cuda(), pos=pos2.cuda())
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_attention_workspace_reuse():
+    """One workspace, with what earlier calls of other sizes left in it,
+    serves the next call: every result equals, bit for bit, that of the same
+    call on a fresh workspace (the last case repeats the first after three
+    others), for splits of one (b, h) over several workgroups and for one
+    workgroup per (b, h)."""
+    dd = require_gpu()
+    announce("attn workspace reuse")
+    D = 128
+    cases = [(2, 3, 1024, 1100), (1, 5, 300, 300), (4, 8, 2048, 2048), (3, 2, 129, 200),
+             (2, 3, 1024, 1100), (16, 40, 640, 640)]
+    need = max(dd.attn_workspace_bytes(B, H, k, D) for B, H, k, _ in cases)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+    for i, (B, H, k, m) in enumerate(cases):
+        seed = 40 + 3 * (i % 4)
+        kr = gen.random_tensor((B, H, m, D), seed=seed, dtype=torch.bfloat16).cuda()
+        vr = gen.random_tensor((B, H, m, D), seed=seed + 1, dtype=torch.bfloat16).cuda()
+        q = gen.random_tensor((B, H, D), seed=seed + 2).cuda()
+        o1, l1 = dd.sparse_attn(q, kr, vr, k=k, ws=ws)
+        o2, l2 = dd.sparse_attn(q, kr, vr, k=k)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), (B, H, k)
+
+
+@pytest.mark.parametrize("big_b,big_h,k,m", [
+    (4, 160, 1000, 1024),   # 640 (b, h): one 256-thread workgroup each
+    (8, 160, 300, 320),     # 1280 (b, h): two groups, 3 chunks (one group idles in round 2)
+])
+def test_attention_split_does_not_change_bits(big_b, big_h, k, m):
+    """The same (b, h) rows give the same bits whether the batch around them
+    is small (its chunks spread over several workgroups, merged by a second
+    kernel) or large (one workgroup per (b, h), merged in LDS); both match
+    the oracle."""
+    dd = require_gpu()
+    announce(f"attn split invariance B={big_b} H={big_h} k={k} m={m}")
+    D = 128
+    kr = gen.random_tensor((big_b, big_h, m, D), seed=71, dtype=torch.bfloat16)
+    vr = gen.random_tensor((big_b, big_h, m, D), seed=72, dtype=torch.bfloat16)
+    q = gen.random_tensor((big_b, big_h, D), seed=73, scale=2.0)
+    pos = gen.random_positions(big_b * big_h, k, m, seed=74, invalid_frac=0.03).reshape(big_b, big_h, k)
+    o_big, l_big = dd.sparse_attn(q.cuda(), kr.cuda(), vr.cuda(), pos=pos.cuda())
+    sl = slice(0, 3)                   # 3 (b, h): split
+    o_small, l_small = dd.sparse_attn(q[:1, sl].contiguous().cuda(), kr[:1, sl].contiguous().cuda(),
+                                      vr[:1, sl].contiguous().cuda(), pos=pos[:1, sl].contiguous().cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(o_big[:1, sl], o_small) and torch.equal(l_big[:1, sl], l_small)
+    ro, _ = oracle.attend_rows(q[:1, sl].numpy(), stored(kr[:1, sl].contiguous()),
+                               stored(vr[:1, sl].contiguous()), "bf16", pos=pos[:1, sl].numpy(), k=k)
+    parity.check_attention(o_small.cpu().numpy().reshape(3, D), ro.reshape(3, D))
+    # a sample of the large batch against the oracle too
+    last = slice(big_h - 2, big_h)
+    ro2, _ = oracle.attend_rows(q[-1:, last].numpy(), stored(kr[-1:, last].contiguous()),
+                                stored(vr[-1:, last].contiguous()), "bf16", pos=pos[-1:, last].numpy(),
+                                k=k)
+    parity.check_attention(o_big[-1:, last].cpu().numpy().reshape(2, D), ro2.reshape(2, D))
