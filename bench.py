@@ -4,8 +4,9 @@ One step = one dd_layer_step over one batch of the Llama-2-7B-shape
 single-layer workload (batch 1, 32 heads x 128, 32768 cached keys, bf16 K/V,
 top-128, current + speculated query): scoring of every key for both queries,
 both top-k selections with the prediction bookkeeping, the prefetch of the
-predicted rows on the side stream, the miss fetch and the sparse attention.
-The prediction is the speculated set of an untimed first step, as in decode.
+predicted V rows (inside the scoring kernel by default), the miss fetch and
+the sparse attention.  The prediction is the speculated set of an untimed
+first step, as in decode.  --workload times one layer of another workload.
 
 Inputs are resident before the clock starts: keys in HBM, the full K/V in
 pinned host memory.  The key copy rotates over several identical HBM copies
@@ -108,6 +109,49 @@ def decode_loop(dd, gen, w, lay, kh, vh, k_dev, lens, steps: int, chunk: int, de
             "recall_per_step": recall}
 
 
+def multi_layer(dd, w, lay, kh, vh, k_dev, lens, layers: int, h2d_gbps: float, dev,
+                steps: int, prefetch: str, k_rows: str):
+    """One decode step over `layers` layers of the workload's shape (the same
+    tensors serve every layer; each layer keeps its own prediction and
+    outputs): the multi-layer schedule, where layer l+1's prefetch overlaps
+    layer l (on the side stream by default).  Eager steps, each bracketed by
+    events on the caller's stream; the link floor is the host-link bytes the
+    step moved (prefetched and missed rows) at the measured pinned-copy rate."""
+    import numpy as np
+    import torch
+    from sparse_kv_retrieval_dual_amd.hipevents import EventSet
+
+    N = layers
+    ctx = dd.Context(ring_slots=2, prefetch=prefetch, k_rows=k_rows)
+    q = lay["q"]
+    lists = ([q] * N, [k_dev] * N, [kh] * N, [vh] * N)
+    res = ctx.layer_step(*lists, lens, w.k)
+    pred = [s.clone() for s in res["spec"]]
+    stats = torch.zeros(N, 3, dtype=torch.int64, device=dev)
+    ev = EventSet(2)
+    times = []
+    for i in range(steps + 2):
+        ev.record(0)
+        ctx.layer_step(*lists, lens, w.k, pred=pred, cur=res["cur"], spec=res["spec"],
+                       out=res["out"], lse=res["lse"], stats=stats)
+        ev.record(1)
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(ev.elapsed_ms(0, 1) * 1e3)
+    st = stats.cpu().numpy()
+    ctx.close()
+    t = float(np.median(times))
+    planes = 1 if k_rows == "device" else 2
+    link_bytes = int(st[:, 2].sum()) * w.D * w.elem_bytes * planes
+    floor_us = link_bytes / (h2d_gbps * 1e9) * 1e6
+    return {"layers": N, "prefetch": prefetch, "step_us_median": t, "per_layer_us": t / N,
+            "timing": "eager, events around each whole step",
+            "link_bytes_per_step": link_bytes, "link_floor_us": floor_us,
+            "frac_of_link_floor": floor_us / t,
+            "misses": int(st[:, 0].sum()), "hits": int(st[:, 1].sum()),
+            "recall": float(st[:, 1].sum() / max(st[:, 0].sum() + st[:, 1].sum(), 1))}
+
+
 def components(dd, gen, w, kh, vh, h2d_gbps: float, dev, reps: int = 6):
     """The gather and the sparse attention measured alone at sizes where
     their own rate shows (inside the layer step the first runs beside the
@@ -202,10 +246,13 @@ def cpu_baseline(w, lay, budget_s: float):
         limiter = threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
         limiter = None
-    q = lay["q"].cpu().numpy()
-    k16 = lay["k"].cpu().view(__import__("torch").int16).numpy()
-    v16 = lay["v"].cpu().view(__import__("torch").int16).numpy()
-    lens = lay["lens"].cpu().numpy()
+    # A batch of several requests is sampled down to its first request (the
+    # oracle's fp64 copy of a whole batch would not fit in host memory).
+    nb = 1 if w.B > 1 else w.B
+    q = lay["q"][:nb].cpu().numpy()
+    k16 = lay["k"][:nb].cpu().view(__import__("torch").int16).numpy()
+    v16 = lay["v"][:nb].cpu().view(__import__("torch").int16).numpy()
+    lens = lay["lens"][:nb].cpu().numpy()
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.layer_step(q, k16, k16, v16, lens, w.k, w.dtype)
@@ -217,7 +264,7 @@ def cpu_baseline(w, lay, budget_s: float):
         limiter.unregister()
     keys = int(np.sum(lens)) * w.H * reps
     return {"value": keys / el, "unit": "keys/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full oracle layer steps of {w.name} (B={w.B} H={w.H} n={w.n_max} "
+            "sample": f"{reps} full oracle layer steps of {w.name} (B={nb} H={w.H} n={w.n_max} "
                       f"k={w.k}; fp64 scoring, full sort, dense-masked attention) in {el:.1f} s"}
 
 
@@ -243,6 +290,8 @@ def main():
                     help="the speculated query also attends over the selected rows")
     ap.add_argument("--no-components", action="store_true",
                     help="skip the stand-alone gather and attention measurements")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="also time one step over this many layers of the workload's shape")
     ap.add_argument("--decode-steps", type=int, default=0,
                     help="also time this many real decode steps (KV append + layer step, "
                          "prediction carried), after the headline measurement")
@@ -264,7 +313,8 @@ def main():
     dd.load()
     dev = torch.device("cuda:0")
     w = gen.workload(args.workload)
-    assert w.L == 1, "the timed workload is a single layer step"
+    # A step is one layer step; a workload of L layers is timed on its first
+    # layer (every layer has the same shapes and work).
     lay = gen.make_layer(w, 0, dev)
     lens = lay["lens"]
     kh = dd.host_empty(lay["k"].shape, lay["k"].dtype)
@@ -461,7 +511,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": D, "context": w.n_max,
+        "config": {"workload": w.name, "layers_timed": f"1 of {w.L}", "batch": B, "heads": H,
+                   "head_dim": D, "context": w.n_max,
                    "top_k": k, "queries": 2, "kv_dtype": w.dtype, "accumulate": "f32",
                    "ring_slots": args.ring, "hbm_key_copies": len(k_copies),
                    "k_rows": args.k_rows, "chunk": chunk, "dual_token": bool(args.dual)},
@@ -493,6 +544,11 @@ def main():
         result["components"] = comp
     if lm_info is not None:
         result["landmarks_build"] = lm_info
+    if args.layers > 1:
+        result["multi_layer"] = multi_layer(dd, w, lay, kh, vh, k_copies[0], lens, args.layers,
+                                            h2d_gbps, dev, max(3, min(args.steps, 10)),
+                                            "auto" if args.prefetch == "auto" else args.prefetch,
+                                            args.k_rows)
     if args.decode_steps > 0:
         result["decode_loop"] = decode_loop(dd, gen, w, lay, kh, vh, k_copies[0], lens,
                                             args.decode_steps, chunk if chunk > 1 else 0, dev)
