@@ -312,7 +312,30 @@ typedef struct dd_layer_step_args {
    * NULL).  out is unchanged bit for bit. */
   float* const* out_spec;
   float* const* lse_spec;
+  /* Rows kept across steps (arXiv page, section 1: the prefetched entries of
+   * a layer are those its next step is predicted to need).  NULL: the ring
+   * of ring_slots slots is shared by the layers and every step fetches the
+   * whole prediction over the host link.  Otherwise device memory of at
+   * least dd_resident_bytes(L, B, H, D, n_max, k, dtype) bytes that gives
+   * every layer two slots of its own, used in turn (ring and ring_bytes are
+   * then unused): a predicted or missed row that the layer's previous step
+   * already brought in is copied from there in HBM instead of crossing the
+   * host link again.  Outputs are bitwise those of the ring; stats count as
+   * rows fetched only the rows read over the link.  Needs chunk 0 or 1 and
+   * DD_KROWS_DEVICE; the prefetch runs on the side stream.  The host rows
+   * must not change while they may be held, except by dd_kv_append (an
+   * appended row was never selected before).  The state belongs to one
+   * sequence of steps over the same layers and shapes. */
+  void* resident;
+  size_t resident_bytes;
+  int parity;  /* 0 or 1, flipped by the caller from one step to the next */
+  int reset;   /* non-zero: the state is cleared first (the first step, or
+                  after the host cache was rewritten); nothing is read from it */
 } dd_layer_step_args;
+
+/* Bytes of the state of rows kept across steps for L layers (see
+ * dd_layer_step_args.resident). */
+DD_API size_t dd_resident_bytes(int L, int B, int H, int D, int64_t n_max, int k, int dtype);
 
 /* Runs the layer step for layers 0..L-1.  Per layer, on the main stream:
  * score both queries, select both top-k sets, compare the true set with the

@@ -17,6 +17,7 @@ from .dd_oracle import (  # noqa: F401
     landmarks,
     layer_step,
     masked_attention,
+    resident_fetches,
     scaled_logits,
     select_topk,
     upcast,

@@ -33,6 +33,11 @@ What it computes, and where the pages define it:
 * Chunk landmarks.  Selection may instead score compressed landmarks of
   chunks of adjacent entries and retrieve whole chunks (arXiv page, section
   2.2, on ShadowKV); a landmark is read as the mean key of its chunk.
+* Rows kept across steps.  The host-link rows of a step whose layer still
+  holds what its previous step brought in (that step's prediction and
+  misses): the prediction and misses not among them (arXiv page, section 1:
+  the predicted entries are prefetched so the step need not wait for them;
+  reading: a row already on the GPU is not fetched again).
 
 Arithmetic is float64 on exact upcasts of the stored fp32 or bf16 values.
 Where the pages leave a point open, the reading used is stated next to the
@@ -283,6 +288,37 @@ def bookkeeping(cur: np.ndarray, pred: np.ndarray | None, n_max: int):
             miss_cnt[b, h] = t
     return {"miss": miss, "miss_cnt": miss_cnt, "pos": pos, "hits": hits,
             "prefetched": prefetched}
+
+
+def resident_fetches(prev_pred, prev_miss, pred, miss, n_max: int) -> np.ndarray:
+    """Rows a step reads over the host link when its layer keeps the rows of
+    its previous step, int64 [B][H].
+
+    The previous step's slot holds the keys of its prediction prev_pred
+    (entries in [0, n_max)) and of its misses prev_miss (entries >= 0);
+    either may be None (nothing held: the first step).  This step fetches
+    every entry of its prediction pred (in [0, n_max); None: no prediction)
+    and of its misses miss (>= 0) whose key that slot does not hold; the
+    others are copied on the GPU.  All arrays are [B][H][k], -1 padded.
+    Reading: a key held by the previous step is not fetched again (arXiv
+    page, section 1, prefetch of the predicted entries; the pages do not
+    discuss keeping rows across steps).
+    """
+    B, H, _ = miss.shape
+    out = np.zeros((B, H), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            held = set()
+            if prev_pred is not None:
+                held.update(int(x) for x in prev_pred[b, h] if 0 <= x < n_max)
+            if prev_miss is not None:
+                held.update(int(x) for x in prev_miss[b, h] if x >= 0)
+            n = 0
+            if pred is not None:
+                n += sum(1 for x in pred[b, h] if 0 <= x < n_max and int(x) not in held)
+            n += sum(1 for x in miss[b, h] if x >= 0 and int(x) not in held)
+            out[b, h] = n
+    return out
 
 
 def landmarks(keys: np.ndarray, lens: np.ndarray, chunk: int, dtype: str) -> np.ndarray:

@@ -18,6 +18,7 @@ from .api import (  # noqa: F401
     kv_dtype,
     landmarks,
     layer_step_workspace_bytes,
+    resident_bytes,
     ring_bytes,
     score,
     sparse_attn,

@@ -50,6 +50,7 @@ class LayerStepArgs(ctypes.Structure):
         ("timing", P),
         ("chunk", c_int), ("landmarks", P),
         ("out_spec", P), ("lse_spec", P),
+        ("resident", P), ("resident_bytes", c_size_t), ("parity", c_int), ("reset", c_int),
     ]
 
 
@@ -68,6 +69,7 @@ _SIGNATURES = {
     "dd_ctx_destroy": (c_int, [P]),
     "dd_ring_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "dd_layer_step_workspace": (c_size_t, [c_int, c_int, c_int, c_int64, c_int]),
+    "dd_resident_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int64, c_int, c_int]),
     "dd_layer_step": (c_int, [P, ctypes.POINTER(LayerStepArgs)]),
     "dd_stream_copy": (c_int, [P, P, c_size_t, P]),
     "dd_gather_chunks": (c_int, [P, P, P, P, c_int, c_int, c_int, c_int, c_int, c_int64, c_int,

@@ -261,6 +261,11 @@ def ring_bytes(ring_slots: int, B: int, H: int, D: int, k: int, dtype: int) -> i
     return int(_lib().dd_ring_bytes(ring_slots, B, H, D, k, dtype))
 
 
+def resident_bytes(L: int, B: int, H: int, D: int, n_max: int, k: int, dtype: int) -> int:
+    """dd_resident_bytes: state of rows kept across steps for L layers."""
+    return int(_lib().dd_resident_bytes(L, B, H, D, n_max, k, dtype))
+
+
 def layer_step_workspace_bytes(B: int, H: int, D: int, n_max: int, k: int) -> int:
     return int(_lib().dd_layer_step_workspace(B, H, D, n_max, k))
 
@@ -307,7 +312,8 @@ class Context:
     def layer_step(self, q, k_dev, k_host, v_host, lens, k: int, pred=None, scale: float = 0.0,
                    cur=None, spec=None, out=None, lse=None, stats=None, ring=None, ws=None,
                    timing=None, stream=None, chunk: int = 0, landmarks=None,
-                   dual: bool = False, out_spec=None, lse_spec=None):
+                   dual: bool = False, out_spec=None, lse_spec=None, resident=None,
+                   parity: int = 0, reset: bool = False):
         """dd_layer_step over the layers given as lists (one tensor per layer).
 
         q[l] fp32 [B][H][2][D]; k_dev[l] device [B][H][n_max][D]; k_host[l], v_host[l]
@@ -317,6 +323,9 @@ class Context:
         pred / cur / spec hold k // chunk chunk indices per (b, h).
         dual: the speculated query also attends over the same rows (out_spec,
         lse_spec in the result).
+        resident: None, or a device uint8 tensor of resident_bytes(...) bytes: rows
+        kept across steps (each layer's own two slots, used in turn by parity 0 / 1;
+        reset clears it first, for the first step of a sequence).
         `timing` is None or a sequence of L * DD_STAGE_EVENTS raw hipEvent_t handles.
         """
         Lyr = len(q)
@@ -365,7 +374,11 @@ class Context:
             stats = torch.zeros(Lyr, 3, dtype=torch.int64, device=dev)
         rb = ring_bytes(self.ring_slots, B, H, D, k, dt)
         wb = layer_step_workspace_bytes(B, H, D, n_max, k)
-        if ring is None:
+        if resident is not None:
+            _dev(resident, "resident")
+            _need(resident.numel() * resident.element_size() >= resident_bytes(Lyr, B, H, D, n_max, k, dt),
+                  "resident state too small (resident_bytes)")
+        if ring is None and resident is None:
             ring = self._buffer("_ring", rb, dev)
         if ws is None:
             ws = self._buffer("_ws", wb, dev)
@@ -389,7 +402,8 @@ class Context:
             out=ctypes.cast(keep[7], ctypes.c_void_p),
             lse=None if keep[8] is None else ctypes.cast(keep[8], ctypes.c_void_p),
             stats=stats.data_ptr(),
-            ring=ring.data_ptr(), ring_bytes=ring.numel() * ring.element_size(),
+            ring=None if ring is None else ring.data_ptr(),
+            ring_bytes=0 if ring is None else ring.numel() * ring.element_size(),
             ws=ws.data_ptr(), ws_bytes=ws.numel() * ws.element_size(),
             stream=_stream(stream).value,
             timing=None if tarr is None else ctypes.cast(tarr, ctypes.c_void_p),
@@ -397,6 +411,9 @@ class Context:
             landmarks=None if keep[9] is None else ctypes.cast(keep[9], ctypes.c_void_p),
             out_spec=None if keep[10] is None else ctypes.cast(keep[10], ctypes.c_void_p),
             lse_spec=None if keep[11] is None else ctypes.cast(keep[11], ctypes.c_void_p),
+            resident=None if resident is None else resident.data_ptr(),
+            resident_bytes=0 if resident is None else resident.numel() * resident.element_size(),
+            parity=int(parity), reset=1 if reset else 0,
         )
         L.check(_lib().dd_layer_step(self._h, ctypes.byref(a)))
         res = {"cur": cur, "spec": spec, "out": out, "lse": lse, "stats": stats}
@@ -414,10 +431,14 @@ class Decoder:
     prediction is carried across real steps.  The caller owns the caches:
     per layer, device keys k_dev[l] and pinned host k_host[l] / v_host[l] of
     [B][H][n_max][D], with room to grow; lens (int32 [B], device) is the
-    current length, and the class keeps its own copy.
+    current length, and the class keeps its own copy.  resident: each layer
+    keeps its selected rows across steps (dd_layer_step_args.resident), so a
+    step fetches over the host link only rows its previous step did not
+    bring in; the state is cleared on the first step.
     """
 
-    def __init__(self, ctx: Context, k_dev, k_host, v_host, lens, k: int, chunk: int = 0):
+    def __init__(self, ctx: Context, k_dev, k_host, v_host, lens, k: int, chunk: int = 0,
+                 resident: bool = False):
         self.ctx = ctx
         self.k_dev, self.k_host, self.v_host = list(k_dev), list(k_host), list(v_host)
         self.k = int(k)
@@ -430,6 +451,13 @@ class Decoder:
             self.landmarks = [landmarks(kd, self._lens[0], self.chunk) for kd in self.k_dev]
         self.pred = None
         self.history = []  # per step: stats [L][3] (device)
+        self.state = None
+        self._parity, self._reset = 0, True
+        if resident:
+            kd = self.k_dev[0]
+            B, H, n_max, D = kd.shape
+            nb = resident_bytes(self.L, B, H, D, n_max, self.k, kv_dtype(kd))
+            self.state = torch.empty(nb, dtype=torch.uint8, device=kd.device)
 
     @property
     def lens(self):
@@ -446,7 +474,10 @@ class Decoder:
         self._cur = 1 - self._cur
         res = self.ctx.layer_step(list(q), self.k_dev, self.k_host, self.v_host, self.lens, self.k,
                                   pred=self.pred, stream=stream, chunk=self.chunk,
-                                  landmarks=self.landmarks)
+                                  landmarks=self.landmarks, resident=self.state,
+                                  parity=self._parity, reset=self._reset)
+        if self.state is not None:
+            self._parity, self._reset = 1 - self._parity, False
         self.pred = [s.clone() for s in res["spec"]]
         self.history.append(res["stats"].clone())
         return res

@@ -94,6 +94,29 @@ size_t slot_bytes(int B, int H, int D, int k, int dtype) {
   return 2 * (size_t)B * H * 2 * k * D * dd::elem_bytes(dtype);
 }
 
+// Rows kept across steps, per layer (byte offsets, 256-byte aligned): two
+// slots of V rows ([BH][2k][D] each), their key lists ([BH][2k] int32
+// each), the key -> row map ([BH][n_max] int32) and the prefetch's host-row
+// counter; `layer` is the stride between layers.
+struct ResidentLayout {
+  size_t vbytes, ibytes;  // one slot's V rows, one slot's key list
+  size_t vslot, idx, where, counter, layer;
+};
+
+ResidentLayout resident_layout(int B, int H, int D, int64_t n_max, int k, int dtype) {
+  const size_t BH = (size_t)B * H;
+  const size_t rows = 2 * (size_t)k;
+  ResidentLayout r{};
+  r.vbytes = align_up(BH * rows * D * dd::elem_bytes(dtype));
+  r.ibytes = align_up(BH * rows * sizeof(int32_t));
+  r.vslot = 0;
+  r.idx = 2 * r.vbytes;
+  r.where = r.idx + 2 * r.ibytes;
+  r.counter = r.where + align_up(BH * (size_t)n_max * sizeof(int32_t));
+  r.layer = r.counter + 256;
+  return r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -296,6 +319,11 @@ DD_API size_t dd_ring_bytes(int ring_slots, int B, int H, int D, int k, int dtyp
   return (size_t)ring_slots * slot_bytes(B, H, D, k, dtype);
 }
 
+DD_API size_t dd_resident_bytes(int L, int B, int H, int D, int64_t n_max, int k, int dtype) {
+  if (L <= 0 || B <= 0 || H <= 0 || k <= 0 || n_max <= 0 || D <= 0) return 0;
+  return (size_t)L * resident_layout(B, H, D, n_max, k, dtype).layer;
+}
+
 DD_API size_t dd_layer_step_workspace(int B, int H, int D, int64_t n_max, int k) {
   if (B <= 0 || H <= 0 || k <= 0 || n_max < 0) return 0;
   return step_layout(B, H, D, n_max, k).total;
@@ -409,9 +437,26 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
   const int ks = k >> cs;                                      // entries selected per query
   const int64_t n_sel = (a->n_max + (1 << cs) - 1) >> cs;      // rows of the scored matrix
   const size_t sbytes = slot_bytes(B, H, D, k, a->dtype);
-  const size_t ring_need = (size_t)c->ring_slots * sbytes;
-  if (!a->ring || a->ring_bytes < ring_need || !aligned16(a->ring))
-    return fail(DD_ERR_WORKSPACE, "ring too small: need %zu bytes, got %zu", ring_need, a->ring_bytes);
+  // Rows kept across steps: each layer's own pair of slots replaces the ring.
+  const bool resident = a->resident != nullptr;
+  const ResidentLayout RL = resident_layout(B, H, D, a->n_max, k, a->dtype);
+  if (resident) {
+    if (cs != 0) return fail(DD_ERR_UNSUPPORTED, "rows kept across steps need chunk 0 or 1");
+    if (c->k_rows != DD_KROWS_DEVICE)
+      return fail(DD_ERR_UNSUPPORTED, "rows kept across steps need K rows from k_dev "
+                                      "(DD_KROWS_DEVICE)");
+    if (a->parity != 0 && a->parity != 1)
+      return fail(DD_ERR_INVALID_ARG, "parity must be 0 or 1 (got %d)", a->parity);
+    const size_t need = (size_t)a->L * RL.layer;
+    if (a->resident_bytes < need || !aligned16(a->resident))
+      return fail(DD_ERR_WORKSPACE, "resident state too small: need %zu bytes, got %zu", need,
+                  a->resident_bytes);
+  } else {
+    const size_t ring_need = (size_t)c->ring_slots * sbytes;
+    if (!a->ring || a->ring_bytes < ring_need || !aligned16(a->ring))
+      return fail(DD_ERR_WORKSPACE, "ring too small: need %zu bytes, got %zu", ring_need,
+                  a->ring_bytes);
+  }
   const StepLayout lay = step_layout(B, H, D, a->n_max, k);
   if (!a->ws || a->ws_bytes < lay.total)
     return fail(DD_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", lay.total, a->ws_bytes);
@@ -432,10 +477,22 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
   // (it can then overlap the previous layer's work), or by extra workgroups
   // of the layer's own scoring kernel (no second stream, no cross-stream
   // wait; the transfer overlaps that layer's key scan only).
-  const bool fused = c->prefetch_mode == DD_PREFETCH_FUSED ||
-                     (c->prefetch_mode == DD_PREFETCH_AUTO && a->L == 1);
+  // Rows kept across steps are always prefetched on the side stream (the
+  // layer's own slots free it from waiting for other layers).
+  const bool fused = !resident && (c->prefetch_mode == DD_PREFETCH_FUSED ||
+                                   (c->prefetch_mode == DD_PREFETCH_AUTO && a->L == 1));
   const bool use_side = any_pred && !fused;
 
+  if (resident && a->reset) {  // both slots hold nothing; counters at zero
+    for (int l = 0; l < a->L; ++l) {
+      char* base = static_cast<char*>(a->resident) + (size_t)l * RL.layer;
+      hipError_t e = dd::launch_fill_i32(reinterpret_cast<int32_t*>(base + RL.idx), -1,
+                                         (int64_t)(2 * RL.ibytes / sizeof(int32_t)), caller);
+      if (e == hipSuccess)
+        e = dd::launch_fill_i32(reinterpret_cast<int32_t*>(base + RL.counter), 0, 2, caller);
+      if (e != hipSuccess) return hip_fail(e, "resident state reset");
+    }
+  }
   DD_CHECK_HIP(hipEventRecord(c->ev_start, caller), "record start");
   if (ms != caller) DD_CHECK_HIP(hipStreamWaitEvent(ms, c->ev_start, 0), "main waits start");
   if (use_side) DD_CHECK_HIP(hipStreamWaitEvent(side, c->ev_start, 0), "side waits start");
@@ -446,8 +503,24 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
 
   for (int l = 0; l < a->L; ++l) {
     const int slot = l % R;
-    char* kslot = static_cast<char*>(a->ring) + (size_t)slot * sbytes;
-    char* vslot = kslot + sbytes / 2;
+    char* kslot = resident ? nullptr : static_cast<char*>(a->ring) + (size_t)slot * sbytes;
+    char* vslot = resident ? nullptr : kslot + sbytes / 2;
+    // Rows kept across steps: this step fills slot `parity` of the layer and
+    // reads rows the previous step left in the other one.
+    dd::GatherRes res{};
+    const void* old_v = nullptr;
+    if (resident) {
+      char* base = static_cast<char*>(a->resident) + (size_t)l * RL.layer;
+      const int p = a->parity;
+      vslot = base + RL.vslot + (size_t)p * RL.vbytes;
+      kslot = vslot;  // unused: K rows come from k_dev
+      old_v = base + RL.vslot + (size_t)(1 - p) * RL.vbytes;
+      res = dd::GatherRes{reinterpret_cast<int32_t*>(base + RL.where),
+                          reinterpret_cast<const int32_t*>(base + RL.idx + (size_t)(1 - p) * RL.ibytes),
+                          reinterpret_cast<int32_t*>(base + RL.idx + (size_t)p * RL.ibytes),
+                          static_cast<const uint8_t*>(old_v),
+                          reinterpret_cast<unsigned long long*>(base + RL.counter)};
+    }
     const int32_t* P = a->pred ? a->pred[l] : nullptr;
     // With K rows read from the scoring copy, only V rows cross the host
     // link (the slot's K plane stays unused).
@@ -459,11 +532,14 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
                            reinterpret_cast<uint8_t*>(vslot), 2 * (int64_t)k, 0, cs, rowb};
 
     if (P && use_side) {
-      if (l >= R) DD_CHECK_HIP(hipStreamWaitEvent(side, c->ev_free[slot], 0), "side waits slot");
+      if (l >= R && !resident)
+        DD_CHECK_HIP(hipStreamWaitEvent(side, c->ev_free[slot], 0), "side waits slot");
       if (tev(l, 5)) DD_CHECK_HIP(hipEventRecord(tev(l, 5), side), "timing");
-      hipError_t e = dd::launch_gather(khost, a->v_host[l], a->n_max, rowb, P, ks, nullptr,
-                                       BH, kslot, vslot, 2 * (int64_t)k, 0, c->prefetch_wgs, side,
-                                       cs);
+      hipError_t e =
+          resident ? dd::launch_gather_resident(a->v_host[l], a->n_max, rowb, P, ks, BH, vslot,
+                                                2 * (int64_t)k, res, c->prefetch_wgs, side)
+                   : dd::launch_gather(khost, a->v_host[l], a->n_max, rowb, P, ks, nullptr, BH,
+                                       kslot, vslot, 2 * (int64_t)k, 0, c->prefetch_wgs, side, cs);
       if (e != hipSuccess) return hip_fail(e, "prefetch gather launch");
       if (tev(l, 6)) DD_CHECK_HIP(hipEventRecord(tev(l, 6), side), "timing");
       DD_CHECK_HIP(hipEventRecord(c->ev_gathered[slot], side), "record gathered");
@@ -492,7 +568,8 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
                            kdev ? a->k_dev[l] : nullptr, a->n_max, cs, D, a->dtype, sc,
                            a->out[l], a->lse ? a->lse[l] : nullptr, st,
                            a->out_spec ? a->out_spec[l] : nullptr,
-                           (a->out_spec && a->out_spec[l] && a->lse_spec) ? a->lse_spec[l] : nullptr};
+                           (a->out_spec && a->out_spec[l] && a->lse_spec) ? a->lse_spec[l] : nullptr,
+                           res.where, res.old_idx, res.new_idx, old_v, res.host_rows};
     e = dd::launch_topk(scores, a->lens, B, H, 2, n_sel, ks, a->cur_idx[l], a->spec_idx[l], ks,
                         P, &fa, ms, cs);
     if (e != hipSuccess) return hip_fail(e, "top-k and attention kernel launch");

@@ -47,9 +47,10 @@ __global__ __launch_bounds__(G * kAttnThreads) void k_attn(
   const AttnRows<T> R{krows + (int64_t)bh * m * D, vrows + (int64_t)bh * m * D, nullptr, nullptr,
                       nullptr, m, m, 0};
   const int32_t* pos_bh = pos != nullptr ? pos + (int64_t)bh * k : nullptr;
-  auto entry = [&](int j, int& r, int& hc) {
+  auto entry = [&](int j, int& r, int& hc, int& o) {
     r = (pos_bh != nullptr) ? pos_bh[j] : j;
     hc = -1;
+    o = -1;
   };
   const float* qb = q + (int64_t)bh * q_stride;
   const int g = threadIdx.x / kAttnThreads;

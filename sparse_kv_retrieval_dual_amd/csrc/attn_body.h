@@ -47,7 +47,9 @@ __device__ __forceinline__ void group_allreduce(float* x) {
 // are read from (and copied into their slot row); vhb null: no host rows.
 // kdb (or null): the device copy of the keys ([n_max][D]); when set, every
 // entry's K row is read from it by row index and only V rows come from the
-// slot or the host (khb is then unused).
+// slot or the host (khb is then unused).  vob (or null, with kdb set): the
+// previous step's slot ([m][D] V rows); a miss it holds is read from there
+// instead of the host.
 template <typename T>
 struct AttnRows {
   const T* kb;
@@ -58,6 +60,7 @@ struct AttnRows {
   int m;
   int first_miss_row;
   int64_t n_max;
+  const T* vob = nullptr;
 };
 
 // LDS of one chunk merge, per query: per-wave max, weight sum and weighted V.
@@ -79,9 +82,9 @@ struct AttnFetch {
 };
 
 // First half of a chunk (entries c0 .. c0 + 127 below lim, handled by the
-// 256 threads tid = 0 .. 255): resolves each
-// entry's rows through entry(j, r, c) (slot row r, -1: skipped; host row c)
-// and issues its K and V loads, all at once (slot rows and device keys from
+// 256 threads tid = 0 .. 255): resolves each entry's rows through
+// entry(j, r, c, o) (slot row r, -1: skipped; host row c; row o of the
+// previous step's slot holding a miss, else -1) and issues its K and V loads, all at once (slot rows and device keys from
 // HBM, missed rows over the host link); a skipped entry reads row 0 of the
 // slab (when there is one) and is masked later.  Nothing waits for the
 // loads here, so a caller can fetch the next chunk before it finishes this
@@ -98,12 +101,13 @@ __device__ __forceinline__ void attn_fetch(const AttnRows<T>& R, int c0, int lim
   const bool from_host = R.vhb != nullptr;
   const bool kdev = R.kdb != nullptr;
   int krow[S::U];  // row of the device key copy (kdev), else -1
+  int orow[S::U];  // row of the previous step's slot holding a miss, else -1
 #pragma unroll
   for (int u = 0; u < S::U; ++u) {
     const int j = e0 + u * S::RPI + rsub;
-    int r = -1, c = -1;
+    int r = -1, c = -1, o = -1;
     if (j < lim && R.m > 0) {
-      entry(j, r, c);
+      entry(j, r, c, o);
       if (r < 0 || r >= R.m) r = -1;
     }
     const bool cvalid = c >= 0 && (int64_t)c < R.n_max;
@@ -112,6 +116,7 @@ __device__ __forceinline__ void attn_fetch(const AttnRows<T>& R, int c0, int lim
     f.rows[u] = r;
     f.hrow[u] = (r >= 0 && miss) ? c : -1;
     krow[u] = (r >= 0 && kdev) ? c : -1;
+    orow[u] = (r >= 0 && miss && R.vob != nullptr && o >= 0 && o < R.m) ? o : -1;
   }
   const T* kb = R.kb + col * S::EPL;
   const T* vb = R.vb + col * S::EPL;
@@ -132,7 +137,9 @@ __device__ __forceinline__ void attn_fetch(const AttnRows<T>& R, int c0, int lim
       const int64_t koff = (int64_t)(krow[u] >= 0 ? krow[u] : 0) * D;
       kv = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4*>(kdev ? kdb + koff : (h ? khb : kb) + off));
-      vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>((h ? vhb : vb) + off));
+      const T* vsrc = (h ? vhb : vb) + off;
+      if (orow[u] >= 0) vsrc = R.vob + col * S::EPL + (int64_t)orow[u] * D;
+      vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vsrc));
     }
     f.kr[u] = kv;
     f.vr[u] = vv;

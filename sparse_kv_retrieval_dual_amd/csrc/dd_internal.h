@@ -24,6 +24,7 @@ const DeviceInfo& device_info();
 inline int elem_bytes(int dtype) { return dtype == kF32 ? 4 : 2; }
 
 struct GatherJob;
+struct GatherRes;
 
 // Scaled logits of Q queries against every key; rows past lens[b] become
 // -inf when fill_pad is set and are left untouched otherwise.  When pf is
@@ -66,6 +67,17 @@ struct FusedAttn {
   float* out_spec;       // [BH][D]: the speculated query (plane 1) attends over
                          // the same rows, or null
   float* lse_spec;       // [BH] or null
+  // Rows kept across steps (null where: every miss comes from the host).
+  // vslot is this step's slot; old_vslot / old_idx the previous step's, whose
+  // rows serve a miss they hold instead of the host; new_idx ([BH][2k]) and
+  // where ([BH][n_rows]) record every row this step's slot holds; pf_host
+  // holds the prefetch's count of rows read over the link (read and cleared
+  // here).  One row per entry (chunk_shift 0), K rows from k_dev.
+  int32_t* where;
+  const int32_t* old_idx;
+  int32_t* new_idx;
+  const void* old_vslot;
+  unsigned long long* pf_host;
 };
 
 // Top-k of each score row.  Plane j of slab bh is written at
@@ -88,6 +100,17 @@ hipError_t launch_gather(const void* k_host, const void* v_host, int64_t n_max, 
                          const int32_t* idx, int m, const int32_t* cnt, int BH, void* k_dst,
                          void* v_dst, int64_t dst_rows_per_bh, int dst_row0, int max_wgs,
                          hipStream_t s, int run_shift = 0);
+
+// The prefetch of a layer whose rows are kept across steps: entry j of
+// slab bh (key idx[bh*m + j]) goes to V row j of the new slot, from the old
+// slot when it holds the key, else over the host link (see GatherRes).
+hipError_t launch_gather_resident(const void* v_host, int64_t n_max, int row_bytes,
+                                  const int32_t* idx, int m, int BH, void* v_dst,
+                                  int64_t dst_rows_per_bh, const GatherRes& r, int max_wgs,
+                                  hipStream_t s);
+
+// Sets n 32-bit words at p to v.
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 
 size_t attn_workspace(int B, int H, int k, int D);
 

@@ -27,6 +27,15 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(GatherJob g) {
   gather_rows<ROWB>(g, gw, nw);
 }
 
+// The prefetch of a layer whose rows are kept across steps (V plane, one
+// row per entry).
+template <int ROWB>
+__global__ __launch_bounds__(kGatherThreads) void k_gather_resident(GatherJob g, GatherRes r) {
+  const int64_t gw = (int64_t)blockIdx.x * (kGatherThreads / 64) + (threadIdx.x >> 6);
+  const int64_t nw = (int64_t)gridDim.x * (kGatherThreads / 64);
+  gather_rows<ROWB, true>(g, gw, nw, r);
+}
+
 }  // namespace
 
 hipError_t launch_gather(const void* k_host, const void* v_host, int64_t n_max, int row_bytes,
@@ -54,6 +63,37 @@ hipError_t launch_gather(const void* k_host, const void* v_host, int64_t n_max, 
       break;
     default:
       hipLaunchKernelGGL(k_gather<512>, dim3((unsigned)grid), dim3(kGatherThreads), 0, s, g);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_resident(const void* v_host, int64_t n_max, int row_bytes,
+                                  const int32_t* idx, int m, int BH, void* v_dst,
+                                  int64_t dst_rows_per_bh, const GatherRes& r, int max_wgs,
+                                  hipStream_t s) {
+  const int64_t total = (int64_t)BH * m;
+  if (total == 0) return hipSuccess;
+  if (total > kGatherMaxRows || m > dst_rows_per_bh) return hipErrorInvalidValue;
+  const int rpi = 64 / (row_bytes / 16);
+  const int64_t rows_per_wg = (int64_t)rpi * kGatherUnroll * (kGatherThreads / 64);
+  int64_t grid = (total + rows_per_wg - 1) / rows_per_wg;
+  const int cap = max_wgs > 0 ? max_wgs : kDefaultMaxWgs;
+  if (grid > cap) grid = cap;
+  const GatherJob g{nullptr, static_cast<const uint8_t*>(v_host), n_max, idx, m, nullptr, total,
+                    nullptr, static_cast<uint8_t*>(v_dst), dst_rows_per_bh, 0, 0, row_bytes};
+  switch (row_bytes) {
+    case 128:
+      hipLaunchKernelGGL(k_gather_resident<128>, dim3((unsigned)grid), dim3(kGatherThreads), 0, s,
+                         g, r);
+      break;
+    case 256:
+      hipLaunchKernelGGL(k_gather_resident<256>, dim3((unsigned)grid), dim3(kGatherThreads), 0, s,
+                         g, r);
+      break;
+    default:
+      hipLaunchKernelGGL(k_gather_resident<512>, dim3((unsigned)grid), dim3(kGatherThreads), 0, s,
+                         g, r);
       break;
   }
   return hipGetLastError();

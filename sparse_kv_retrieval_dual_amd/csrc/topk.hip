@@ -40,6 +40,7 @@
 #include "attn_body.h"
 #include "dd_device.h"
 #include "dd_internal.h"
+#include "gather_body.h"
 
 namespace dd {
 
@@ -92,6 +93,13 @@ static_assert(4 * 256 + kNT <= kBins, "walk starts fit the bound histogram");
 constexpr int kAttnScratchWords = 2 * (8 + 4 * 128) + 8 + 2 * 32 * (128 + 2);
 static_assert(Lay<true>::end + kAttnScratchWords <= Lay<true>::words, "dual scratch fits (cached)");
 static_assert(kLIdx + kAttnScratchWords <= Lay<false>::c, "dual scratch fits (long rows)");
+// Rows kept across steps: each entry's row in the previous step's slot (or
+// -1), in the candidate lists (free once the selection is emitted), beside
+// the attention scratch.
+template <bool CACHED>
+constexpr int kLOld = CACHED ? kLIdx : kLIdx + kAttnScratchWords;
+static_assert(kLOld<true> + kMaxK <= Lay<true>::c, "old rows fit (cached)");
+static_assert(kLOld<false> + kMaxK <= Lay<false>::c, "old rows fit (long rows)");
 
 __device__ __forceinline__ void clear(uint32_t* p, int words) {
   for (int i = threadIdx.x; i < words; i += kNT) p[i] = 0u;
@@ -722,7 +730,8 @@ __device__ __forceinline__ int radix_select(const float* __restrict__ row, int n
 template <typename T, int D>
 __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, int ks,
                                                   int32_t len, const int32_t* lpos,
-                                                  const int32_t* lcur, float* scratch) {
+                                                  const int32_t* lcur, const int32_t* lold,
+                                                  float* scratch) {
   constexpr int NQ = 2;
   const int nq = fa.out_spec != nullptr ? 2 : 1;
   AttnLds<D, NQ>& lds = *reinterpret_cast<AttnLds<D, NQ>*>(scratch);
@@ -737,12 +746,15 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
   const AttnRows<T> R{static_cast<const T*>(fa.kslot) + slab, static_cast<const T*>(fa.vslot) + slab,
                       kdev ? nullptr : static_cast<const T*>(fa.k_host) + hslab,
                       static_cast<const T*>(fa.v_host) + hslab,
-                      kdev ? static_cast<const T*>(fa.k_dev) + hslab : nullptr, 2 * k, k, n_rows};
+                      kdev ? static_cast<const T*>(fa.k_dev) + hslab : nullptr, 2 * k, k, n_rows,
+                      lold != nullptr ? static_cast<const T*>(fa.old_vslot) + slab : nullptr};
   const int cmask = (1 << cs) - 1;
-  auto entry = [&](int j, int& r, int& c) {
+  auto entry = [&](int j, int& r, int& c, int& o) {
+    o = -1;
     if (cs == 0) {  // one row per entry
       r = lpos[j];
       c = lcur[j];
+      if (lold != nullptr) o = lold[j];
       return;
     }
     const int e = j >> cs;
@@ -790,16 +802,53 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
   }
 }
 
+// Bookkeeping of a layer whose rows are kept across steps, by the
+// workgroup of a current-query row after its emit: every miss (slot row
+// r >= k, key c) is looked up in the previous step's slot (lold[j]: its row
+// there, or -1 when it must come over the host link), and the new slot's
+// key list and the key -> row map are brought up to date: the misses' rows,
+// then -1 on the rows no miss fills (and on the prediction's rows when
+// there was no prediction, so no prefetch wrote them).  Returns the
+// workgroup's count of misses read over the link (all threads).
+__device__ __forceinline__ int resident_bookkeeping(const FusedAttn& fa, int bh, int k,
+                                                    int misses, bool has_pred,
+                                                    const int32_t* lpos, const int32_t* lcur,
+                                                    int32_t* lold, ScanBufs sb) {
+  const int tid = threadIdx.x;
+  const int64_t rows = 2 * (int64_t)k;
+  const int64_t ib = (int64_t)bh * rows;
+  const int64_t wb = (int64_t)bh * fa.n_rows;
+  int host = 0;
+  for (int j = tid; j < k; j += kNT) {
+    const int r = lpos[j];
+    const int c = lcur[j];
+    int o = -1;
+    if (r >= k && r < rows && c >= 0 && (int64_t)c < fa.n_rows) {
+      o = resident_row(fa.where, fa.old_idx, fa.n_rows, rows, bh, c);
+      host += o < 0 ? 1 : 0;
+      fa.new_idx[ib + r] = c;
+      fa.where[wb + c] = r;
+    }
+    lold[j] = o;
+  }
+  const int64_t m = misses < k ? misses : k;
+  for (int64_t r = (has_pred ? k + m : 0) + tid; r < rows; r += kNT)
+    if (r < k || r >= k + m) fa.new_idx[ib + r] = -1;
+  int total = 0;
+  block_scan<kNW>(host, sb, total);
+  return total;
+}
+
 // scratch: LDS for the attention of both queries (kAttnScratchWords).
 __device__ __forceinline__ void fused_attention(const FusedAttn& fa, int bh, int ks, int32_t len,
                                                 const int32_t* lpos, const int32_t* lcur,
-                                                float* scratch) {
+                                                const int32_t* lold, float* scratch) {
   if (fa.dtype == kBF16) {
-    if (fa.D == 128) fused_attention_t<uint16_t, 128>(fa, bh, ks, len, lpos, lcur, scratch);
-    else fused_attention_t<uint16_t, 64>(fa, bh, ks, len, lpos, lcur, scratch);
+    if (fa.D == 128) fused_attention_t<uint16_t, 128>(fa, bh, ks, len, lpos, lcur, lold, scratch);
+    else fused_attention_t<uint16_t, 64>(fa, bh, ks, len, lpos, lcur, lold, scratch);
   } else {
-    if (fa.D == 128) fused_attention_t<float, 128>(fa, bh, ks, len, lpos, lcur, scratch);
-    else fused_attention_t<float, 64>(fa, bh, ks, len, lpos, lcur, scratch);
+    if (fa.D == 128) fused_attention_t<float, 128>(fa, bh, ks, len, lpos, lcur, lold, scratch);
+    else fused_attention_t<float, 64>(fa, bh, ks, len, lpos, lcur, lold, scratch);
   }
 }
 
@@ -877,15 +926,35 @@ __global__ __launch_bounds__(kNT) void k_topk(
 
   if (!do_book) return;
   const int valid = n < k ? n : k;
+  const bool resident = fa.where != nullptr;
   if (tid == 0 && fa.stats != nullptr) {
     atomicAdd(reinterpret_cast<unsigned long long*>(fa.stats), (unsigned long long)misses);
     atomicAdd(reinterpret_cast<unsigned long long*>(fa.stats) + 1,
               (unsigned long long)(valid - misses));
-    atomicAdd(reinterpret_cast<unsigned long long*>(fa.stats) + 2,
-              (unsigned long long)(fetchable + misses));
+    if (!resident)
+      atomicAdd(reinterpret_cast<unsigned long long*>(fa.stats) + 2,
+                (unsigned long long)(fetchable + misses));
   }
   __syncthreads();  // every entry's slot row and row index are in LDS
-  fused_attention(fa, bh, k, len_b, sk.lpos, sk.lcur,
+  int32_t* lold = nullptr;
+  if (resident) {
+    lold = reinterpret_cast<int32_t*>(smem + kLOld<CACHED>);
+    const int host = resident_bookkeeping(fa, bh, k, misses, pred_row != nullptr, sk.lpos,
+                                          sk.lcur, lold,
+                                          ScanBufs{reinterpret_cast<int*>(smem + kLScr), 0});
+    if (tid == 0) {
+      unsigned long long pf = 0;
+      if (bh == 0) {  // the layer's prefetch count, taken once and cleared
+        pf = *fa.pf_host;
+        *fa.pf_host = 0ull;
+      }
+      if (fa.stats != nullptr)
+        atomicAdd(reinterpret_cast<unsigned long long*>(fa.stats) + 2,
+                  (unsigned long long)host + pf);
+    }
+    __syncthreads();  // lold complete
+  }
+  fused_attention(fa, bh, k, len_b, sk.lpos, sk.lcur, lold,
                   reinterpret_cast<float*>(smem + (CACHED ? Lay<true>::end : kLIdx)));
 }
 

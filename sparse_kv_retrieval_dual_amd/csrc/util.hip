@@ -1,4 +1,4 @@
-// Device properties and the streaming-copy measurement kernel.
+// Device properties, the streaming-copy measurement kernel and a fill.
 #include <mutex>
 
 #include "dd_device.h"
@@ -30,7 +30,21 @@ __global__ __launch_bounds__(256) void k_stream_copy(const u32x4* __restrict__ s
   for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// Grid-stride fill of n 32-bit words with v.
+__global__ __launch_bounds__(256) void k_fill_i32(int32_t* __restrict__ p, int32_t v, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
 }  // namespace
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t grid = (n + 255) / 256;
+  if (grid > 2048) grid = 2048;
+  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)grid), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
 
 const DeviceInfo& device_info() {
   int dev = 0;

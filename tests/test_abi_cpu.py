@@ -43,6 +43,11 @@ def test_buffer_sizes(lib):
     # attention partials: one (D + 2)-float record per (b, h, 128-entry chunk), none for one chunk
     assert lib.dd_attn_workspace(1, 32, 128, 128) == 0
     assert lib.dd_attn_workspace(16, 32, 1024, 128) == 16 * 32 * 8 * 130 * 4
+    # rows kept across steps, per layer: 2 slots of V rows (B*H x 2k x D x elem), 2 key lists
+    # (B*H x 2k int32), the key -> row map (B*H x n_max int32), a 256-byte counter
+    per_layer = 2 * 32 * 256 * 128 * 2 + 2 * 32 * 256 * 4 + 32 * 32768 * 4 + 256
+    assert lib.dd_resident_bytes(2, 1, 32, 128, 32768, 128, 1) == 2 * per_layer
+    assert lib.dd_resident_bytes(0, 1, 32, 128, 32768, 128, 1) == 0
     # layer-step workspace holds the two score planes of a layer
     ws = lib.dd_layer_step_workspace(1, 32, 128, 32768, 128)
     assert ws >= 32 * 2 * 32768 * 4

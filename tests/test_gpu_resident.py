@@ -1,0 +1,106 @@
+"""Rows kept across decode steps (dd_layer_step_args.resident): a decode
+loop where every layer keeps its own two slots gives, bit for bit, the sets,
+outputs and hit / miss counts of the shared ring, and reads over the host
+link exactly the rows the oracle's resident_fetches counts (whenever the
+GPU's sets are the oracle's)."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from tests.gpu_util import announce, require_gpu, stored, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000)),
+    ("llama7b_32k_step", dict(L=2, B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000, k=256)),
+    ("tiny", dict(n_max=2048, len_lo=1500, len_hi=1500)),
+])
+def test_resident_decode_loop(name, kw):
+    dd = require_gpu()
+    w = gen.workload(name).scaled(**kw)
+    L = w.L
+    announce(f"resident decode loop {name} {kw}")
+    layers = [gen.make_layer(w, l, "cpu") for l in range(L)]
+
+    def caches():
+        return ([lay["k"].cuda() for lay in layers], [to_host(dd, lay["k"]) for lay in layers],
+                [to_host(dd, lay["v"]) for lay in layers])
+
+    ctx = dd.Context(ring_slots=2)
+    lens = layers[0]["lens"].cuda()
+    plain = dd.Decoder(ctx, *caches(), lens, w.k)
+    keep = dd.Decoder(ctx, *caches(), lens, w.k, resident=True)
+    q = [lay["q"] for lay in layers]
+    kst = [stored(lay["k"]) for lay in layers]
+    vst = [stored(lay["v"]) for lay in layers]
+    lens_np = layers[0]["lens"].numpy().astype(np.int64)
+    pred_ref = [None] * L       # the oracle's prediction of each layer
+    held = [None] * L           # the oracle's (prediction, misses) of the previous step
+    agree = True                # the GPU's sets have been the oracle's at every step
+    for t in range(1, 6):
+        if t == 4:              # a reset mid-sequence: nothing is held any more
+            keep._reset = True
+            held = [None] * L
+        new = [gen.decode_step_inputs(w, l, t, q[l]) for l in range(L)]
+        q = [x[0] for x in new]
+        args = ([x.cuda() for x in q], [x[1].cuda() for x in new], [x[2].cuda() for x in new])
+        a = plain.step(*args)
+        b = keep.step(*args)
+        torch.cuda.synchronize()
+        for l in range(L):
+            for key in ("cur", "spec", "out", "lse"):
+                assert torch.equal(a[key][l], b[key][l]), (t, l, key)
+        sa, sb = a["stats"].cpu().numpy(), b["stats"].cpu().numpy()
+        assert np.array_equal(sa[:, :2], sb[:, :2]), t
+        assert sb[:, 2].sum() <= sa[:, 2].sum(), t
+        # the oracle's loop: append, then the step with the previous spec set
+        for l in range(L):
+            kst[l], _ = oracle.append_rows(kst[l], lens_np, stored(new[l][1]))
+            vst[l], grown = oracle.append_rows(vst[l], lens_np, stored(new[l][2]))
+        lens_np = grown
+        want = np.zeros(L, dtype=np.int64)
+        for l in range(L):
+            ref = oracle.layer_step(q[l].numpy(), kst[l], kst[l], vst[l], lens_np, w.k, w.dtype,
+                                    pred=pred_ref[l])
+            agree = agree and np.array_equal(b["cur"][l].cpu().numpy(), ref["cur"]) \
+                and np.array_equal(b["spec"][l].cpu().numpy(), ref["spec"])
+            pp, pm = held[l] if held[l] is not None else (None, None)
+            want[l] = oracle.resident_fetches(pp, pm, pred_ref[l], ref["miss"], w.n_max).sum()
+            held[l] = (pred_ref[l], ref["miss"])
+            pred_ref[l] = ref["spec"]
+        if agree:
+            assert sb[:, 2].tolist() == want.tolist(), (t, sb[:, 2].tolist(), want.tolist())
+        print(f"step {t}: host rows {int(sb[:, 2].sum())} kept-rows mode, "
+              f"{int(sa[:, 2].sum())} ring; sets agree with the oracle: {agree}")
+    ctx.close()
+
+
+def test_resident_argument_errors():
+    dd = require_gpu()
+    announce("resident argument errors")
+    w = gen.workload("tiny").scaled(n_max=512, len_lo=400, len_hi=400)
+    lay = gen.make_layer(w, 0, "cpu")
+    q, kd = lay["q"].cuda(), lay["k"].cuda()
+    kh, vh = to_host(dd, lay["k"]), to_host(dd, lay["v"])
+    lens = lay["lens"].cuda()
+    B, H, n_max, D = kd.shape
+    nb = dd.resident_bytes(1, B, H, D, n_max, w.k, dd.kv_dtype(kd))
+    state = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ctx = dd.Context(ring_slots=2)
+    with pytest.raises(Exception, match="parity"):
+        ctx.layer_step([q], [kd], [kh], [vh], lens, w.k, resident=state, parity=2, reset=True)
+    lm = dd.landmarks(kd, lens, 8)
+    with pytest.raises(Exception, match="chunk"):
+        ctx.layer_step([q], [kd], [kh], [vh], lens, w.k, chunk=8, landmarks=[lm], resident=state,
+                       reset=True)
+    with pytest.raises(Exception, match="too small"):
+        ctx.layer_step([q], [kd], [kh], [vh], lens, w.k, resident=state[:nb // 2], reset=True)
+    hctx = dd.Context(ring_slots=2, k_rows="host")
+    with pytest.raises(Exception, match="k_dev|DD_KROWS_DEVICE"):
+        hctx.layer_step([q], [kd], [kh], [vh], lens, w.k, resident=state, reset=True)
+    ctx.close()
+    hctx.close()

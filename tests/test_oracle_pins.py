@@ -608,3 +608,60 @@ def test_tie_band_comparator_accepts_swaps_and_rejects_errors():
         parity.check_index_sets(np.array([[0, 4]]), ref, logits, lens, 2)
     with pytest.raises(AssertionError):
         parity.check_index_sets(np.array([[2, 0]]), ref, logits, lens, 2)
+
+
+def test_resident_fetches_hand_example():
+    """Previous slot holds prediction {1, 2, 3} (the -1 and the out-of-range
+    9 hold nothing) and miss {7}; this step's prediction {2, 3, 4, 5} brings
+    4 and 5 over the link, its misses {7, 8} bring 8: three rows."""
+    n_max = 9
+    prev_pred = np.array([[[1, 2, 3, -1, 9]]], dtype=np.int32)
+    prev_miss = np.array([[[7, -1, -1, -1, -1]]], dtype=np.int32)
+    pred = np.array([[[2, 3, 4, 5, -1]]], dtype=np.int32)
+    miss = np.array([[[7, 8, -1, -1, -1]]], dtype=np.int32)
+    assert oracle.resident_fetches(prev_pred, prev_miss, pred, miss, n_max).tolist() == [[3]]
+    # nothing held before: every valid prediction entry and every miss
+    assert oracle.resident_fetches(None, None, pred, miss, n_max).tolist() == [[6]]
+    # no prediction this step: only the misses not held
+    assert oracle.resident_fetches(prev_pred, prev_miss, None, miss, n_max).tolist() == [[1]]
+    # the same prediction and misses again: nothing crosses the link
+    assert oracle.resident_fetches(prev_pred, prev_miss, prev_pred, prev_miss, n_max).tolist() == [[0]]
+
+
+def test_resident_fetches_cold_step_is_the_ring_count():
+    """Without a previous step, the rows fetched are the prediction's valid
+    entries plus the misses: the bookkeeping's prefetched + miss_cnt."""
+    rng = np.random.default_rng(5)
+    B, H, k, n_max = 2, 3, 16, 64
+    cur = np.sort(np.stack([[rng.choice(n_max, k, replace=False) for _ in range(H)]
+                            for _ in range(B)]), axis=2).astype(np.int32)
+    pred = np.sort(np.stack([[rng.choice(n_max, k, replace=False) for _ in range(H)]
+                             for _ in range(B)]), axis=2).astype(np.int32)
+    bk = oracle.bookkeeping(cur, pred, n_max)
+    got = oracle.resident_fetches(None, None, pred, bk["miss"], n_max)
+    assert np.array_equal(got, bk["prefetched"] + bk["miss_cnt"])
+
+
+def test_resident_fetches_match_a_brute_force_count():
+    """Against a count by membership masks over all n_max keys."""
+    rng = np.random.default_rng(6)
+    B, H, k, n_max = 2, 2, 8, 24
+    def draw():
+        a = np.full((B, H, k), -1, dtype=np.int32)
+        for b in range(B):
+            for h in range(H):
+                m = rng.integers(0, k + 1)
+                a[b, h, :m] = np.sort(rng.choice(n_max, m, replace=False))
+        return a
+    for _ in range(20):
+        pp, pm, p, m = draw(), draw(), draw(), draw()
+        got = oracle.resident_fetches(pp, pm, p, m, n_max)
+        for b in range(B):
+            for h in range(H):
+                held = np.zeros(n_max, dtype=bool)
+                for x in list(pp[b, h]) + list(pm[b, h]):
+                    if x >= 0:
+                        held[x] = True
+                want = sum(1 for x in p[b, h] if x >= 0 and not held[x]) + \
+                    sum(1 for x in m[b, h] if x >= 0 and not held[x])
+                assert got[b, h] == want
