@@ -63,29 +63,43 @@ def _counter_traffic(kernel: str, sources, workload: str):
         return None
 
 
-def decode_loop(dd, gen, w, lay, kh, vh, k_dev, lens, steps: int, chunk: int, dev):
+def decode_loop(dd, gen, w, lay, kh, vh, k_dev, lens, steps: int, chunk: int, dev,
+                layers: int = 1, resident: bool = False, h2d_gbps: float = 0.0,
+                prefetch_wgs: int = 0):
     """Real decode steps on the same cache: each appends the new token's K/V
     rows (dd_kv_append) and runs the layer step with the previous step's
     speculated set as the prediction.  The loop starts `steps` rows short of
     the workload's context (rows past the length are filler) and grows back
     to it.  Each step is timed alone (eager, events around it on the
     caller's stream), after a 1 GiB streaming copy that clears the keys from
-    the 256 MB Infinity Cache."""
+    the 256 MB Infinity Cache.
+
+    layers > 1: every step runs that many layers of the workload's shape.
+    The layers share the cache tensors (their appends land on the same rows,
+    which changes no amount of work) but each has its own query sequence,
+    prediction and outputs.  resident: each layer keeps its selected rows
+    across steps, so only rows its previous step did not bring in cross the
+    host link.  prefetch_wgs caps the workgroups of a side-stream prefetch
+    (0: the library's default)."""
     import numpy as np
     import torch
     from sparse_kv_retrieval_dual_amd.hipevents import EventSet
 
+    N = layers
     start = torch.clamp(lens - steps, min=0).to(torch.int32)
-    ctx = dd.Context(ring_slots=2)
-    dec = dd.Decoder(ctx, [k_dev], [kh], [vh], start, w.k, chunk=chunk)
-    q = lay["q"].cpu()
-    res = ctx.layer_step([q.to(dev)], [k_dev], [kh], [vh], dec.lens, w.k, chunk=chunk,
-                         landmarks=dec.landmarks)
+    ctx = dd.Context(ring_slots=2, prefetch_wgs=prefetch_wgs)
+    dec = dd.Decoder(ctx, [k_dev] * N, [kh] * N, [vh] * N, start, w.k, chunk=chunk,
+                     resident=resident)
+    q0 = lay["q"].cpu()
+    res = ctx.layer_step([q0.to(dev)] * N, [k_dev] * N, [kh] * N, [vh] * N, dec.lens, w.k,
+                         chunk=chunk, landmarks=dec.landmarks)
     dec.pred = [s.clone() for s in res["spec"]]
     inputs = []
+    qs = [q0] * N
     for t in range(1, steps + 1):
-        q, nk, nv = gen.decode_step_inputs(w, 0, t, q)
-        inputs.append((q.to(dev), nk.to(dev), nv.to(dev)))
+        new = [gen.decode_step_inputs(w, l, t, qs[l]) for l in range(N)]
+        qs = [x[0] for x in new]
+        inputs.append(tuple([x[i].to(dev) for x in new] for i in range(3)))
     big = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
     big2 = torch.empty_like(big)
     ev = EventSet(2)
@@ -93,20 +107,33 @@ def decode_loop(dd, gen, w, lay, kh, vh, k_dev, lens, steps: int, chunk: int, de
     for qd, nk, nv in inputs:
         dd.stream_copy(big, big2)
         ev.record(0)
-        dec.step([qd], [nk], [nv])
+        dec.step(qd, nk, nv)
         ev.record(1)
         torch.cuda.synchronize()
         times.append(ev.elapsed_ms(0, 1) * 1e3)
     del big, big2
     c = max(chunk, 1)
-    recall = []
-    for st, n in zip(dec.history, range(1, steps + 1)):
-        m, h, _ = st[0].cpu().tolist()
+    recall, link_rows = [], []
+    for st in dec.history:
+        a = st.cpu().numpy()
+        m, h = int(a[:, 0].sum()), int(a[:, 1].sum())
         recall.append(h / max(m + h, 1))
+        link_rows.append(int(a[:, 2].sum()))
     ctx.close()
-    return {"steps": steps, "chunk": c, "us_per_step_mean": float(np.mean(times)),
-            "us_per_step_median": float(np.median(times)), "timing": "eager, one step at a time",
-            "recall_per_step": recall}
+    out = {"steps": steps, "layers": N, "resident": bool(resident), "chunk": c,
+           "us_per_step_mean": float(np.mean(times)),
+           "us_per_step_median": float(np.median(times)),
+           "us_per_layer_median": float(np.median(times)) / N,
+           "timing": "eager, one step at a time", "recall_per_step": recall,
+           "host_rows_per_step": link_rows}
+    if h2d_gbps > 0:
+        # V rows only cross the link (K rows come from the scoring copy).
+        row_b = w.D * w.elem_bytes * c
+        tail = link_rows[len(link_rows) // 2:]
+        out["host_bytes_per_step_late_half"] = float(np.mean(tail)) * row_b
+        out["link_floor_us_late_half"] = float(np.mean(tail)) * row_b / (h2d_gbps * 1e9) * 1e6
+        out["us_per_step_median_late_half"] = float(np.median(times[len(times) // 2:]))
+    return out
 
 
 def multi_layer(dd, w, lay, kh, vh, k_dev, lens, layers: int, h2d_gbps: float, dev,
@@ -294,7 +321,11 @@ def main():
                     help="also time one step over this many layers of the workload's shape")
     ap.add_argument("--decode-steps", type=int, default=0,
                     help="also time this many real decode steps (KV append + layer step, "
-                         "prediction carried), after the headline measurement")
+                         "prediction carried), after the headline measurement; with "
+                         "--layers, each step runs that many layers")
+    ap.add_argument("--resident", action="store_true",
+                    help="in the decode loop, also time it with each layer keeping its "
+                         "selected rows across steps")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -550,8 +581,15 @@ def main():
                                             "auto" if args.prefetch == "auto" else args.prefetch,
                                             args.k_rows)
     if args.decode_steps > 0:
+        c0 = chunk if chunk > 1 else 0
         result["decode_loop"] = decode_loop(dd, gen, w, lay, kh, vh, k_copies[0], lens,
-                                            args.decode_steps, chunk if chunk > 1 else 0, dev)
+                                            args.decode_steps, c0, dev, layers=args.layers,
+                                            h2d_gbps=h2d_gbps, prefetch_wgs=args.prefetch_wgs)
+        if args.resident:
+            result["decode_loop_resident"] = decode_loop(
+                dd, gen, w, lay, kh, vh, k_copies[0], lens, args.decode_steps, c0, dev,
+                layers=args.layers, resident=True, h2d_gbps=h2d_gbps,
+                prefetch_wgs=args.prefetch_wgs)
     ctx.close()
     print(json.dumps(result))
 

@@ -13,6 +13,7 @@
 #include "dd.h"
 #include "dd_internal.h"
 #include "gather_body.h"
+#include "gather_res.h"
 
 struct dd_ctx {
   int device = -1;

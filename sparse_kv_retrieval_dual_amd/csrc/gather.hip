@@ -12,6 +12,7 @@
 // ran 50% slower, with 16 about 25%).
 #include "dd_internal.h"
 #include "gather_body.h"
+#include "gather_res.h"
 
 namespace dd {
 
@@ -28,12 +29,15 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(GatherJob g) {
 }
 
 // The prefetch of a layer whose rows are kept across steps (V plane, one
-// row per entry).
+// row per entry); each wave keeps its two copy queues in LDS.
 template <int ROWB>
 __global__ __launch_bounds__(kGatherThreads) void k_gather_resident(GatherJob g, GatherRes r) {
-  const int64_t gw = (int64_t)blockIdx.x * (kGatherThreads / 64) + (threadIdx.x >> 6);
+  __shared__ ResQueue qh[kGatherThreads / 64];
+  __shared__ ResQueue qd[kGatherThreads / 64];
+  const int w = threadIdx.x >> 6;
+  const int64_t gw = (int64_t)blockIdx.x * (kGatherThreads / 64) + w;
   const int64_t nw = (int64_t)gridDim.x * (kGatherThreads / 64);
-  gather_rows<ROWB, true>(g, gw, nw, r);
+  gather_rows_res<ROWB>(g, gw, nw, r, qh[w], qd[w]);
 }
 
 }  // namespace
@@ -75,8 +79,8 @@ hipError_t launch_gather_resident(const void* v_host, int64_t n_max, int row_byt
   const int64_t total = (int64_t)BH * m;
   if (total == 0) return hipSuccess;
   if (total > kGatherMaxRows || m > dst_rows_per_bh) return hipErrorInvalidValue;
-  const int rpi = 64 / (row_bytes / 16);
-  const int64_t rows_per_wg = (int64_t)rpi * kGatherUnroll * (kGatherThreads / 64);
+  // A wave classifies 64 entries at a time.
+  const int64_t rows_per_wg = 64 * (kGatherThreads / 64);
   int64_t grid = (total + rows_per_wg - 1) / rows_per_wg;
   const int cap = max_wgs > 0 ? max_wgs : kDefaultMaxWgs;
   if (grid > cap) grid = cap;

@@ -22,27 +22,6 @@ struct GatherJob {
   int row_bytes;         // bytes of one K/V row: 128, 256 or 512
 };
 
-// Rows kept across decode steps: each layer owns two slots, the one the
-// previous step filled ("old") and the one this step fills ("new"), each
-// with the key index held by every row (-1: none).  where[bh][x] is the row
-// that key x was last written to; it is trusted only when the old slot's
-// index list confirms it (old_idx[row] == x), so it never needs clearing.
-struct GatherRes {
-  int32_t* where;                  // [BH][n_max]
-  const int32_t* old_idx;          // [BH][dst_rows_per_bh]
-  int32_t* new_idx;                // [BH][dst_rows_per_bh]
-  const uint8_t* old_v;            // [BH][dst_rows_per_bh][row]: the old slot's V plane
-  unsigned long long* host_rows;   // rows read over the host link are added here
-};
-
-// Row of the old slot that holds key x of slab bh, or -1.
-__device__ __forceinline__ int resident_row(const int32_t* where, const int32_t* old_idx,
-                                            int64_t n_max, int64_t rows, int bh, int64_t x) {
-  const int w = where[(int64_t)bh * n_max + x];
-  if (w < 0 || w >= rows) return -1;
-  return old_idx[(int64_t)bh * rows + w] == (int32_t)x ? w : -1;
-}
-
 constexpr int kGatherUnroll = 4;
 constexpr int64_t kGatherMaxRows = 0x7fffffff - 1024;  // rows of one job (32-bit row numbers)
 
@@ -56,13 +35,8 @@ constexpr int64_t kGatherMaxRows = 0x7fffffff - 1024;  // rows of one job (32-bi
 // that all of them are in flight at once; a lane without a host row to
 // fetch reads a stand-in address in device memory (its own destination
 // slot) and its data is discarded.
-//
-// RES (one row per entry, V plane only): a row the old slot already holds is
-// copied from there instead of over the host link; every written row's key
-// goes to new_idx and where, and the rows read over the link are counted.
-template <int ROWB, bool RES = false>
-__device__ __forceinline__ void gather_rows(const GatherJob& g, int64_t gw, int64_t nw,
-                                            const GatherRes& res = GatherRes{}) {
+template <int ROWB>
+__device__ __forceinline__ void gather_rows(const GatherJob& g, int64_t gw, int64_t nw) {
   constexpr int LPR = ROWB / 16;
   constexpr int RPI = 64 / LPR;
   constexpr int U = kGatherUnroll;
@@ -76,13 +50,11 @@ __device__ __forceinline__ void gather_rows(const GatherJob& g, int64_t gw, int6
   // below 2^31); byte offsets are 64-bit.
   const int rs = g.run_shift;
   const int rows = (int)(g.total << rs);
-  int host_cnt = 0;  // RES: rows this lane's row group read over the link
   for (int64_t base = gw * (RPI * U); base < rows; base += nw * (RPI * U)) {
     const uint8_t* kp[U];
     const uint8_t* vp[U];
     int64_t doff[U];
     bool wr[U], fetch[U];
-    int key[U], drow[U], bhs[U], orow[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       int row = (int)base + u * RPI + rsub;
@@ -105,15 +77,6 @@ __device__ __forceinline__ void gather_rows(const GatherJob& g, int64_t gw, int6
       const int64_t soff = ((int64_t)bh * g.n_max + (fetch[u] ? hr : 0)) * ROWB + col * 16;
       kp[u] = (fetch[u] && has_k) ? g.ksrc + soff : g.kdst + (has_k ? doff[u] : 0);
       vp[u] = (fetch[u] && has_v) ? g.vsrc + soff : g.vdst + (has_v ? doff[u] : 0);
-      if constexpr (RES) {
-        key[u] = fetch[u] ? (int)hr : -1;
-        drow[u] = g.dst_row0 + j;
-        bhs[u] = bh;
-        orow[u] = fetch[u] ? resident_row(res.where, res.old_idx, g.n_max, g.dst_rows_per_bh, bh, hr)
-                           : -1;
-        if (orow[u] >= 0)
-          vp[u] = res.old_v + ((int64_t)bh * g.dst_rows_per_bh + orow[u]) * ROWB + col * 16;
-      }
     }
     u32x4 kv[U], vv[U];
 #pragma unroll
@@ -126,19 +89,8 @@ __device__ __forceinline__ void gather_rows(const GatherJob& g, int64_t gw, int6
       if (wr[u]) {
         if (has_k) *reinterpret_cast<u32x4*>(g.kdst + doff[u]) = fetch[u] ? kv[u] : zero;
         if (has_v) *reinterpret_cast<u32x4*>(g.vdst + doff[u]) = fetch[u] ? vv[u] : zero;
-        if constexpr (RES) {
-          if (col == 0) {  // one lane per row: its key and where it now lives
-            res.new_idx[(int64_t)bhs[u] * g.dst_rows_per_bh + drow[u]] = key[u];
-            if (key[u] >= 0) res.where[(int64_t)bhs[u] * g.n_max + key[u]] = drow[u];
-            host_cnt += (key[u] >= 0 && orow[u] < 0) ? 1 : 0;
-          }
-        }
       }
     }
-  }
-  if constexpr (RES) {
-    for (int off = 32; off >= 1; off >>= 1) host_cnt += __shfl_xor(host_cnt, off);
-    if (lane == 0 && host_cnt > 0) atomicAdd(res.host_rows, (unsigned long long)host_cnt);
   }
 }
 

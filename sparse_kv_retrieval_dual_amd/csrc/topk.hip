@@ -41,6 +41,7 @@
 #include "dd_device.h"
 #include "dd_internal.h"
 #include "gather_body.h"
+#include "gather_res.h"
 
 namespace dd {
 
