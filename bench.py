@@ -35,6 +35,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 SCORE_SOURCES = ("score.hip", "dd_device.h", "gather_body.h")
 
 
+def _progress(msg: str) -> None:
+    """A line on stderr as each phase of the run ends (stdout holds only the
+    JSON result)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
 def _source_hash(files) -> str:
     h = hashlib.sha256()
     for name in files:
@@ -276,16 +282,22 @@ def cpu_baseline(w, lay, budget_s: float):
     # A batch of several requests is sampled down to its first request (the
     # oracle's fp64 copy of a whole batch would not fit in host memory).
     nb = 1 if w.B > 1 else w.B
+    import torch
+
+    def stored(t):  # the oracle's view of stored elements: bf16 as int16 bit patterns
+        t = t[:nb].cpu().contiguous()
+        return t.view(torch.int16).numpy() if t.dtype == torch.bfloat16 else t.numpy()
+
     q = lay["q"][:nb].cpu().numpy()
-    k16 = lay["k"][:nb].cpu().view(__import__("torch").int16).numpy()
-    v16 = lay["v"][:nb].cpu().view(__import__("torch").int16).numpy()
+    k16 = stored(lay["k"])
+    v16 = stored(lay["v"])
     lens = lay["lens"][:nb].cpu().numpy()
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.layer_step(q, k16, k16, v16, lens, w.k, w.dtype)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 50:
+        if el >= budget_s:
             break
     if limiter is not None:
         limiter.unregister()
@@ -358,6 +370,7 @@ def main():
     n_keys = int(lens.sum().item()) * H
     eb = w.elem_bytes
     torch.cuda.synchronize()
+    _progress(f"{w.name}: inputs resident ({n_keys} keys)")
 
     ctx = dd.Context(ring_slots=args.ring, gather_cus=args.gather_cus,
                      prefetch_wgs=args.prefetch_wgs, prefetch=args.prefetch, k_rows=args.k_rows)
@@ -446,6 +459,7 @@ def main():
     eager_ms = bounds.elapsed_ms(0, 1) / K
     ms_per_step = graph_ms if graph is not None else eager_ms
     t_score = float(np.mean([score_ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)]))
+    _progress(f"timed {K} steps: {ms_per_step * 1e3:.1f} us per step")
 
     # Breakdown: the same steps again with every stage bracketed (the extra
     # event records make these steps slightly longer; not the headline).
@@ -523,10 +537,12 @@ def main():
     h2d_gbps = float(np.median(h2d))
     del big, big2, hpin
     comp = None if args.no_components else components(dd, gen, w, kh, vh, h2d_gbps, dev)
+    _progress("reference rates and components done")
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, lay, args.cpu_seconds)
+        _progress("cpu baseline done")
 
     traffic = _counter_traffic("score", SCORE_SOURCES, w.name) if chunk == 1 else None
     result = {
