@@ -32,7 +32,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 # The scoring kernel's source: its file and the headers it includes.
-SCORE_SOURCES = ("score.hip", "dd_device.h", "gather_body.h")
+SCORE_SOURCES = ("score.hip", "dd_device.h", "gather_body.h", "gather_res.h")
 
 
 def _progress(msg: str) -> None:
@@ -71,7 +71,7 @@ def _counter_traffic(kernel: str, sources, workload: str):
 
 def decode_loop(dd, gen, w, lay, kh, vh, k_dev, lens, steps: int, chunk: int, dev,
                 layers: int = 1, resident: bool = False, h2d_gbps: float = 0.0,
-                prefetch_wgs: int = 0):
+                prefetch_wgs: int = 0, prefetch: str = "auto"):
     """Real decode steps on the same cache: each appends the new token's K/V
     rows (dd_kv_append) and runs the layer step with the previous step's
     speculated set as the prediction.  The loop starts `steps` rows short of
@@ -85,15 +85,15 @@ def decode_loop(dd, gen, w, lay, kh, vh, k_dev, lens, steps: int, chunk: int, de
     which changes no amount of work) but each has its own query sequence,
     prediction and outputs.  resident: each layer keeps its selected rows
     across steps, so only rows its previous step did not bring in cross the
-    host link.  prefetch_wgs caps the workgroups of a side-stream prefetch
-    (0: the library's default)."""
+    host link.  prefetch / prefetch_wgs: the context's prefetch mode and
+    workgroup count (0: the library's default)."""
     import numpy as np
     import torch
     from sparse_kv_retrieval_dual_amd.hipevents import EventSet
 
     N = layers
     start = torch.clamp(lens - steps, min=0).to(torch.int32)
-    ctx = dd.Context(ring_slots=2, prefetch_wgs=prefetch_wgs)
+    ctx = dd.Context(ring_slots=2, prefetch_wgs=prefetch_wgs, prefetch=prefetch)
     dec = dd.Decoder(ctx, [k_dev] * N, [kh] * N, [vh] * N, start, w.k, chunk=chunk,
                      resident=resident)
     q0 = lay["q"].cpu()
@@ -614,12 +614,13 @@ def main():
         c0 = chunk if chunk > 1 else 0
         result["decode_loop"] = decode_loop(dd, gen, w, lay, kh, vh, k_copies[0], lens,
                                             args.decode_steps, c0, dev, layers=args.layers,
-                                            h2d_gbps=h2d_gbps, prefetch_wgs=args.prefetch_wgs)
+                                            h2d_gbps=h2d_gbps, prefetch_wgs=args.prefetch_wgs,
+                                            prefetch=args.prefetch)
         if args.resident:
             result["decode_loop_resident"] = decode_loop(
                 dd, gen, w, lay, kh, vh, k_copies[0], lens, args.decode_steps, c0, dev,
                 layers=args.layers, resident=True, h2d_gbps=h2d_gbps,
-                prefetch_wgs=args.prefetch_wgs)
+                prefetch_wgs=args.prefetch_wgs, prefetch=args.prefetch)
     ctx.close()
     print(json.dumps(result))
 

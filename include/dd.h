@@ -224,12 +224,14 @@ typedef struct dd_ctx_config {
   int gather_cus;  /* 0: side stream without a CU mask.  > 0: the side stream
                       is restricted to this many CUs and the layer step's own
                       main stream to the others */
-  int prefetch_wgs; /* workgroups of the prefetch gather (0: 32).  Fewer keep
+  int prefetch_wgs; /* workgroups of the prefetch gather (0: 32; four times
+                      as many when rows are kept across steps).  Fewer keep
                       fewer host reads outstanding, which disturbs the
                       concurrent HBM-bound scoring less; enough of them
                       still saturate the host link */
-  int prefetch_mode; /* DD_PREFETCH_AUTO (fused for L == 1, side stream
-                      otherwise), DD_PREFETCH_SIDE or DD_PREFETCH_FUSED */
+  int prefetch_mode; /* DD_PREFETCH_AUTO (fused for L == 1 or when rows are
+                      kept across steps, side stream otherwise),
+                      DD_PREFETCH_SIDE or DD_PREFETCH_FUSED */
   int k_rows;       /* DD_KROWS_DEVICE (0) or DD_KROWS_HOST: where attention
                       reads the K rows of the selected entries */
 } dd_ctx_config;
@@ -322,7 +324,7 @@ typedef struct dd_layer_step_args {
    * already brought in is copied from there in HBM instead of crossing the
    * host link again.  Outputs are bitwise those of the ring; stats count as
    * rows fetched only the rows read over the link.  Needs chunk 0 or 1 and
-   * DD_KROWS_DEVICE; the prefetch runs on the side stream.  The host rows
+   * DD_KROWS_DEVICE.  The host rows
    * must not change while they may be held, except by dd_kv_append (an
    * appended row was never selected before).  The state belongs to one
    * sequence of steps over the same layers and shapes. */

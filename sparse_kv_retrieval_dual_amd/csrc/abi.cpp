@@ -32,6 +32,11 @@ struct dd_ctx {
 
 namespace {
 
+// Workgroups of a kept-rows prefetch per prefetch_wgs: 4 (128 at the default
+// 32) was the fastest of 1 to 8, on the side stream and inside the scoring
+// kernel alike, for a 4-layer decode step at batch 16, k = 1024 on MI355X.
+constexpr int kResidentWgsScale = 4;
+
 thread_local std::string g_err;
 
 int fail(int code, const char* fmt, ...) {
@@ -478,10 +483,12 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
   // (it can then overlap the previous layer's work), or by extra workgroups
   // of the layer's own scoring kernel (no second stream, no cross-stream
   // wait; the transfer overlaps that layer's key scan only).
-  // Rows kept across steps are always prefetched on the side stream (the
-  // layer's own slots free it from waiting for other layers).
-  const bool fused = !resident && (c->prefetch_mode == DD_PREFETCH_FUSED ||
-                                   (c->prefetch_mode == DD_PREFETCH_AUTO && a->L == 1));
+  // With rows kept across steps, a layer's prefetch has its own slot to
+  // fill and no slot to wait for; inside the layer's scoring kernel it
+  // disturbed the main stream least (a 4-layer step at batch 16, k = 1024:
+  // 5.96 ms against 6.70 ms on the side stream).
+  const bool fused = c->prefetch_mode == DD_PREFETCH_FUSED ||
+                     (c->prefetch_mode == DD_PREFETCH_AUTO && (a->L == 1 || resident));
   const bool use_side = any_pred && !fused;
 
   if (resident && a->reset) {  // both slots hold nothing; counters at zero
@@ -536,9 +543,13 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
       if (l >= R && !resident)
         DD_CHECK_HIP(hipStreamWaitEvent(side, c->ev_free[slot], 0), "side waits slot");
       if (tev(l, 5)) DD_CHECK_HIP(hipEventRecord(tev(l, 5), side), "timing");
+      // A kept-rows prefetch runs on more workgroups: each wave's
+      // lookups (index, then the old slot's row) leave its host loads idle
+      // for a while, and its own layer's slots free it from waiting.
       hipError_t e =
           resident ? dd::launch_gather_resident(a->v_host[l], a->n_max, rowb, P, ks, BH, vslot,
-                                                2 * (int64_t)k, res, c->prefetch_wgs, side)
+                                                2 * (int64_t)k, res, kResidentWgsScale * c->prefetch_wgs,
+                                                side)
                    : dd::launch_gather(khost, a->v_host[l], a->n_max, rowb, P, ks, nullptr, BH,
                                        kslot, vslot, 2 * (int64_t)k, 0, c->prefetch_wgs, side, cs);
       if (e != hipSuccess) return hip_fail(e, "prefetch gather launch");
@@ -555,8 +566,10 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     hipError_t e = dd::launch_score(a->q[l], cs ? static_cast<const void*>(a->landmarks[l]) : a->k_dev[l],
                                     a->lens, B, H, 2, D, n_sel, cs ? DD_F32 : a->dtype,
                                     sc, false, scores, (P && fused) ? &pf : nullptr,
-                                    c->prefetch_wgs, ms, score_ev ? tev(l, 0) : nullptr,
-                                    score_ev ? tev(l, 1) : nullptr, st, cs);
+                                    (resident ? kResidentWgsScale : 1) * c->prefetch_wgs, ms,
+                                    score_ev ? tev(l, 0) : nullptr,
+                                    score_ev ? tev(l, 1) : nullptr, st, cs,
+                                    (P && fused && resident) ? &res : nullptr);
     if (e != hipSuccess) return hip_fail(e, "score kernel launch");
     if (tev(l, 1) && !score_ev) DD_CHECK_HIP(hipEventRecord(tev(l, 1), ms), "timing");
     if (P && use_side) DD_CHECK_HIP(hipStreamWaitEvent(ms, c->ev_gathered[slot], 0), "main waits prefetch");

@@ -33,12 +33,14 @@ struct GatherRes;
 // are given they are recorded at the kernel's own start and end.  zero3
 // (or null): three int64 counters the kernel sets to zero.  len_shift > 0:
 // the rows are chunk landmarks, 2^len_shift keys each, and request b has
-// ceil(lens[b] / 2^len_shift) of them.
+// ceil(lens[b] / 2^len_shift) of them.  pres (with pf): the prefetch of a
+// layer whose rows are kept across steps (see launch_gather_resident).
 hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, int B, int H,
                         int Q, int D, int64_t n_max, int dtype, float scale, bool fill_pad,
                         float* scores, const GatherJob* pf, int pf_wgs, hipStream_t s,
                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
-                        int64_t* zero3 = nullptr, int len_shift = 0);
+                        int64_t* zero3 = nullptr, int len_shift = 0,
+                        const GatherRes* pres = nullptr);
 
 // In-place softmax of each score row over its valid keys; 0 past lens[b].
 hipError_t launch_softmax_rows(float* scores, const int32_t* lens, int B, int H, int Q,

@@ -20,6 +20,7 @@
 #include "dd_device.h"
 #include "dd_internal.h"
 #include "gather_body.h"
+#include "gather_res.h"
 
 namespace dd {
 
@@ -47,7 +48,8 @@ template <typename T, int D, int Q>
 __global__ __launch_bounds__(kScoreWaves * 64) void k_score(
     const float* __restrict__ q, const T* __restrict__ keys, const int32_t* __restrict__ lens,
     int BH, int H, int64_t n_max, int tiles, float scale, float* __restrict__ scores,
-    int fill_pad, GatherJob pf, int pf_wgs, int64_t* __restrict__ zero3, int len_shift) {
+    int fill_pad, GatherJob pf, int pf_wgs, int64_t* __restrict__ zero3, int len_shift,
+    GatherRes pres) {
   using S = ScoreShape<T, D, Q>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -59,6 +61,11 @@ __global__ __launch_bounds__(kScoreWaves * 64) void k_score(
     constexpr int RB = D * (int)sizeof(T);
     const int64_t gw = (int64_t)blockIdx.x * kScoreWaves + wave;
     const int64_t nw = (int64_t)pf_wgs * kScoreWaves;
+    if (pres.where != nullptr) {  // rows kept across steps: V rows, one per entry
+      extern __shared__ ResQueue s_queues[];  // [2][kScoreWaves], launched with them
+      gather_rows_res<RB>(pf, gw, nw, pres, s_queues[wave], s_queues[kScoreWaves + wave]);
+      return;
+    }
     if constexpr (sizeof(T) == 4) {
       if (pf.row_bytes == RB / 2) {
         gather_rows<RB / 2>(pf, gw, nw);
@@ -178,6 +185,7 @@ struct ScoreLaunch {
   hipEvent_t ev_start, ev_stop;
   int64_t* zero3;
   int len_shift;
+  GatherRes pres;
 };
 
 template <typename T, int D, int Q>
@@ -188,17 +196,19 @@ hipError_t launch_score_t(const ScoreLaunch& a) {
   if (BH == 0 || (tiles == 0 && a.pf_wgs == 0 && a.zero3 == nullptr)) return hipSuccess;
   const int64_t grid = (tiles > 0 ? tiles * BH : 1) + a.pf_wgs;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  // The copy queues of a kept-rows prefetch (dynamic LDS, only then).
+  const unsigned lds = a.pres.where != nullptr ? 2 * kScoreWaves * sizeof(ResQueue) : 0;
   if (a.ev_start != nullptr && a.ev_stop != nullptr) {
     // Events taken by the dispatch itself: the kernel's own duration.
-    hipExtLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), 0,
+    hipExtLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), lds,
                           a.s, a.ev_start, a.ev_stop, 0, a.q, static_cast<const T*>(a.keys),
                           a.lens, BH, a.H, a.n_max, (int)tiles, a.scale, a.scores,
-                          a.fill_pad ? 1 : 0, a.pf, a.pf_wgs, a.zero3, a.len_shift);
+                          a.fill_pad ? 1 : 0, a.pf, a.pf_wgs, a.zero3, a.len_shift, a.pres);
   } else {
-    hipLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), 0, a.s,
+    hipLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), lds, a.s,
                        a.q, static_cast<const T*>(a.keys), a.lens, BH, a.H, a.n_max, (int)tiles,
                        a.scale, a.scores, a.fill_pad ? 1 : 0, a.pf, a.pf_wgs, a.zero3,
-                       a.len_shift);
+                       a.len_shift, a.pres);
   }
   return hipGetLastError();
 }
@@ -215,9 +225,9 @@ hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, i
                         int Q, int D, int64_t n_max, int dtype, float scale, bool fill_pad,
                         float* scores, const GatherJob* pf, int pf_wgs, hipStream_t s,
                         hipEvent_t ev_start, hipEvent_t ev_stop, int64_t* zero3,
-                        int len_shift) {
+                        int len_shift, const GatherRes* pres) {
   ScoreLaunch a{q, keys, lens, B, H, n_max, scale, fill_pad, scores, GatherJob{}, 0, s,
-                ev_start, ev_stop, zero3, len_shift};
+                ev_start, ev_stop, zero3, len_shift, GatherRes{}};
   if (pf != nullptr && pf->total > 0 && pf_wgs > 0) {
     // The prefetched K/V rows are the scored rows' size, or (fp32 landmarks
     // of bf16 rows) half of it.
@@ -227,6 +237,13 @@ hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, i
     if ((pf->total << pf->run_shift) > kGatherMaxRows) return hipErrorInvalidValue;
     a.pf = *pf;
     a.pf_wgs = (pf_wgs + 7) & ~7;  // keeps the scoring tiles' XCD placement
+    if (pres != nullptr) {
+      // Kept rows: V plane only, one row per entry, the scored rows' size.
+      if (pf->ksrc != nullptr || pf->run_shift != 0 || pf->row_bytes != rb ||
+          pf->m > pf->dst_rows_per_bh || pf->total > kGatherMaxRows)
+        return hipErrorInvalidValue;
+      a.pres = *pres;
+    }
   }
   if (dtype == kBF16) {
     if (D == 128) return launch_score_q<uint16_t, 128>(Q, a);

@@ -14,23 +14,26 @@ from tests.gpu_util import announce, require_gpu, stored, to_host
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("prefetch", ["auto", "side"])
 @pytest.mark.parametrize("name,kw", [
     ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000)),
     ("llama7b_32k_step", dict(L=2, B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000, k=256)),
     ("tiny", dict(n_max=2048, len_lo=1500, len_hi=1500)),
 ])
-def test_resident_decode_loop(name, kw):
+def test_resident_decode_loop(name, kw, prefetch):
     dd = require_gpu()
     w = gen.workload(name).scaled(**kw)
     L = w.L
-    announce(f"resident decode loop {name} {kw}")
+    announce(f"resident decode loop {name} {kw} prefetch={prefetch}")
     layers = [gen.make_layer(w, l, "cpu") for l in range(L)]
 
     def caches():
         return ([lay["k"].cuda() for lay in layers], [to_host(dd, lay["k"]) for lay in layers],
                 [to_host(dd, lay["v"]) for lay in layers])
 
-    ctx = dd.Context(ring_slots=2)
+    # auto: the kept-rows prefetch rides in each layer's scoring kernel;
+    # side: it runs on the context's side stream.
+    ctx = dd.Context(ring_slots=2, prefetch=prefetch)
     lens = layers[0]["lens"].cuda()
     plain = dd.Decoder(ctx, *caches(), lens, w.k)
     keep = dd.Decoder(ctx, *caches(), lens, w.k, resident=True)
