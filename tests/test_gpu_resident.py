@@ -15,17 +15,22 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("prefetch", ["auto", "side"])
-@pytest.mark.parametrize("name,kw", [
-    ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000)),
-    ("llama7b_32k_step", dict(L=2, B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000, k=256)),
-    ("tiny", dict(n_max=2048, len_lo=1500, len_hi=1500)),
+@pytest.mark.parametrize("name,kw,short", [
+    ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000), None),
+    ("llama7b_32k_step", dict(L=2, B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000, k=256), None),
+    ("tiny", dict(n_max=2048, len_lo=1500, len_hi=1500), None),
+    # request 0 shorter than k: its sets and predictions carry -1 padding
+    ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000), 60),
 ])
-def test_resident_decode_loop(name, kw, prefetch):
+def test_resident_decode_loop(name, kw, short, prefetch):
     dd = require_gpu()
     w = gen.workload(name).scaled(**kw)
     L = w.L
-    announce(f"resident decode loop {name} {kw} prefetch={prefetch}")
+    announce(f"resident decode loop {name} {kw} short={short} prefetch={prefetch}")
     layers = [gen.make_layer(w, l, "cpu") for l in range(L)]
+    if short is not None:  # rows past the new length are filler
+        for lay in layers:
+            lay["lens"][0] = short
 
     def caches():
         return ([lay["k"].cuda() for lay in layers], [to_host(dd, lay["k"]) for lay in layers],
