@@ -19,7 +19,7 @@ struct dd_ctx {
   int device = -1;
   int ring_slots = 1;
   int gather_cus = 0;
-  int prefetch_wgs = 32;
+  int prefetch_wgs = 0;             // 0: sized per layer (prefetch_wgs_for)
   int prefetch_mode = DD_PREFETCH_AUTO;
   int k_rows = DD_KROWS_DEVICE;
   hipStream_t side = nullptr;       // prefetch gathers
@@ -36,6 +36,16 @@ namespace {
 // 32) was the fastest of 1 to 8, on the side stream and inside the scoring
 // kernel alike, for a 4-layer decode step at batch 16, k = 1024 on MI355X.
 constexpr int kResidentWgsScale = 4;
+
+// Workgroups of one layer's prefetch when the context leaves it open: 32 for
+// a small prefetch (1 MiB at batch 1, k = 128: 16 to 32 were equal, 8 too
+// few), 64 from 16 MiB up (84 MiB at batch 4 x 40 heads, k = 2048: 2.06 ms
+// per layer against 2.14 ms with 32), times kResidentWgsScale for kept rows.
+int prefetch_wgs_for(const dd_ctx* c, int64_t rows, int row_bytes, bool resident) {
+  int w = c->prefetch_wgs;
+  if (w == 0) w = rows * row_bytes >= (int64_t(16) << 20) && !resident ? 64 : 32;
+  return resident ? kResidentWgsScale * w : w;
+}
 
 thread_local std::string g_err;
 
@@ -349,7 +359,7 @@ DD_API int dd_ctx_create(const dd_ctx_config* cfg, dd_ctx** ctx) {
   dd_ctx* c = new dd_ctx();
   c->ring_slots = cfg->ring_slots;
   c->gather_cus = cfg->gather_cus;
-  c->prefetch_wgs = cfg->prefetch_wgs > 0 ? cfg->prefetch_wgs : 32;
+  c->prefetch_wgs = cfg->prefetch_wgs;
   c->prefetch_mode = cfg->prefetch_mode;
   c->k_rows = cfg->k_rows;
   hipError_t e = hipGetDevice(&c->device);
@@ -538,6 +548,9 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
                            static_cast<const uint8_t*>(a->v_host[l]), a->n_max, P, ks, nullptr,
                            (int64_t)BH * ks, reinterpret_cast<uint8_t*>(kslot),
                            reinterpret_cast<uint8_t*>(vslot), 2 * (int64_t)k, 0, cs, rowb};
+    // Bytes the prefetch moves: V rows (and K rows from the host).
+    const int pf_wgs = prefetch_wgs_for(c, ((int64_t)BH * ks) << cs, rowb * (kdev ? 1 : 2),
+                                        resident);
 
     if (P && use_side) {
       if (l >= R && !resident)
@@ -548,10 +561,10 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
       // for a while, and its own layer's slots free it from waiting.
       hipError_t e =
           resident ? dd::launch_gather_resident(a->v_host[l], a->n_max, rowb, P, ks, BH, vslot,
-                                                2 * (int64_t)k, res, kResidentWgsScale * c->prefetch_wgs,
+                                                2 * (int64_t)k, res, pf_wgs,
                                                 side)
                    : dd::launch_gather(khost, a->v_host[l], a->n_max, rowb, P, ks, nullptr, BH,
-                                       kslot, vslot, 2 * (int64_t)k, 0, c->prefetch_wgs, side, cs);
+                                       kslot, vslot, 2 * (int64_t)k, 0, pf_wgs, side, cs);
       if (e != hipSuccess) return hip_fail(e, "prefetch gather launch");
       if (tev(l, 6)) DD_CHECK_HIP(hipEventRecord(tev(l, 6), side), "timing");
       DD_CHECK_HIP(hipEventRecord(c->ev_gathered[slot], side), "record gathered");
@@ -566,7 +579,7 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     hipError_t e = dd::launch_score(a->q[l], cs ? static_cast<const void*>(a->landmarks[l]) : a->k_dev[l],
                                     a->lens, B, H, 2, D, n_sel, cs ? DD_F32 : a->dtype,
                                     sc, false, scores, (P && fused) ? &pf : nullptr,
-                                    (resident ? kResidentWgsScale : 1) * c->prefetch_wgs, ms,
+                                    pf_wgs, ms,
                                     score_ev ? tev(l, 0) : nullptr,
                                     score_ev ? tev(l, 1) : nullptr, st, cs,
                                     (P && fused && resident) ? &res : nullptr);
