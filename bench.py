@@ -490,6 +490,7 @@ def main():
     t_select_attn = avg(1, 4)
     t_prefetch = avg(5, 6) if args.prefetch == "side" else None
     t_step_instr = avg(0, 4)
+    steps_instr = np.array([stage.elapsed_ms(i * E, i * E + 4) for i in range(K)]) * 1e3
     st = stats[0].cpu().tolist()
     misses, hits, fetched = st
     n_sel = int(((lens + chunk - 1) // chunk).sum().item()) * H   # rows scored: keys or landmarks
@@ -508,6 +509,20 @@ def main():
     t_pf = t_prefetch if t_prefetch is not None else t_score
     prefetch_gbps = prefetch_bytes / (t_pf * 1e-3) / 1e9
     miss_bytes = misses * chunk * planes * D * eb
+
+    # A cold step: the same step with no prediction, so every selected row
+    # is fetched over the host link on the critical path (eager, events
+    # around each step on the caller's stream).
+    cold_ev = EventSet(2)
+    cold = []
+    for i in range(max(3, min(K, 20))):
+        cold_ev.record(0)
+        step(i, None)
+        cold_ev.record(1)
+        torch.cuda.synchronize()
+        cold.append(cold_ev.elapsed_ms(0, 1) * 1e3)
+    step(0, pred)  # leaves the stats and outputs of a predicted step
+    torch.cuda.synchronize()
 
     # The landmark build (once per cache, not per step), over the same copies.
     lm_info = None
@@ -590,7 +605,12 @@ def main():
         "stages_us": {"score": t_score * 1e3,
                       "select_bookkeeping_attention": t_select_attn * 1e3,
                       "prefetch_side_stream": None if t_prefetch is None else t_prefetch * 1e3,
-                      "instrumented_step": t_step_instr * 1e3},
+                      "instrumented_step": t_step_instr * 1e3,
+                      "instrumented_step_p10_p50_p90": [float(np.percentile(steps_instr, p))
+                                                        for p in (10, 50, 90)]},
+        "cold_layer_step_us": {"median": float(np.median(cold)),
+                               "note": "eager, no prediction: every selected row over the "
+                                       "host link on the critical path"},
         "score_keys_per_s": n_keys / (t_score * 1e-3),
         "score_frac_of_measured_hbm_copy": score_gbps / hbm_copy,
         "gather_GBps": prefetch_gbps,
