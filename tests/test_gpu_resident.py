@@ -112,3 +112,66 @@ def test_resident_argument_errors():
         hctx.layer_step([q], [kd], [kh], [vh], lens, w.k, resident=state, reset=True)
     ctx.close()
     hctx.close()
+
+
+def test_resident_step_graph_replays_match_eager():
+    """A kept-rows step captured in a HIP graph (the prefetch rides in the
+    scoring kernel): every replay, with eager work in between, reproduces the
+    eager step's sets, outputs and host-row counts bitwise.  The state of the
+    kept rows is restored before each run of the step (eagerly, between
+    replays), so every run starts from the state the previous step left."""
+    dd = require_gpu()
+    announce("resident layer step graph capture and replay")
+    w = gen.workload("llama7b_32k_step").scaled(L=2, B=2, H=4, n_max=8192, len_lo=6000,
+                                                len_hi=8000, k=256)
+    layers = [gen.make_layer(w, l, "cpu") for l in range(w.L)]
+    kd = [d["k"].cuda() for d in layers]
+    kh = [to_host(dd, d["k"]) for d in layers]
+    vh = [to_host(dd, d["v"]) for d in layers]
+    lens = layers[0]["lens"].cuda()
+    B, H, D, k, n_max = w.B, w.H, w.D, w.k, w.n_max
+    ctx = dd.Context(ring_slots=2)
+    state = torch.empty(dd.resident_bytes(w.L, B, H, D, n_max, k, dd.kv_dtype(kd[0])),
+                        dtype=torch.uint8, device="cuda")
+    qs = [[d["q"].cuda() for d in layers]]
+    for t in range(1, 3):  # queries of two later steps
+        qs.append([gen.decode_step_inputs(w, l, t, qs[-1][l].cpu())[0].cuda() for l in range(w.L)])
+    cur = [torch.empty(B, H, k, dtype=torch.int32, device="cuda") for _ in range(w.L)]
+    spec = [torch.empty_like(c) for c in cur]
+    out = [torch.empty(B, H, D, device="cuda") for _ in range(w.L)]
+    lse = [torch.empty(B, H, device="cuda") for _ in range(w.L)]
+    stats = torch.zeros(w.L, 3, dtype=torch.int64, device="cuda")
+
+    def step(q, pred, parity, reset):
+        ctx.layer_step(q, kd, kh, vh, lens, k, pred=pred, cur=cur, spec=spec, out=out, lse=lse,
+                       stats=stats, resident=state, parity=parity, reset=reset)
+
+    step(qs[0], None, 0, True)
+    p1 = [s.clone() for s in spec]
+    step(qs[1], p1, 1, False)
+    p2 = [s.clone() for s in spec]
+    before = state.clone()     # what the captured step starts from
+    step(qs[2], p2, 0, False)  # the step that is captured, run eagerly first
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in out] + [x.clone() for x in cur] + [x.clone() for x in spec] \
+        + [stats.clone()]
+    assert int(stats[:, 2].sum()) > 0 and int(stats[:, 0].sum()) > 0
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(qs[2], p2, 0, False)
+    scratch = torch.empty(1 << 20, device="cuda")
+    for rep in range(4):
+        for o in out:
+            o.zero_()
+        stats.zero_()
+        state.copy_(before)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in out] + [x.clone() for x in cur] + [x.clone() for x in spec] \
+            + [stats.clone()]
+        assert all(torch.equal(a, b) for a, b in zip(got, ref)), f"replay {rep} differs"
+        scratch.normal_()  # eager work between replays
+        torch.cuda.synchronize()
+    ctx.close()
