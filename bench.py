@@ -354,7 +354,7 @@ def main():
                          "selected rows across steps")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(each GPU would run its own share of requests or heads independently).",
               file=sys.stderr)
         sys.exit(2)

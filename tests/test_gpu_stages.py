@@ -262,7 +262,7 @@ def test_attention_workspace_reuse():
 
 @pytest.mark.parametrize("big_b,big_h,k,m", [
     (4, 160, 1000, 1024),   # 640 (b, h): one 256-thread workgroup each
-    (8, 160, 300, 320),     # 1280 (b, h): two groups, 3 chunks (one group idles in round 2)
+    (8, 160, 300, 320),     # 1280 (b, h): two groups, 3 chunks (one group idles in its second pass)
 ])
 def test_attention_split_does_not_change_bits(big_b, big_h, k, m):
     """The same (b, h) rows give the same bits whether the batch around them
