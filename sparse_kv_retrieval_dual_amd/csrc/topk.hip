@@ -25,11 +25,14 @@
 // bit digits over the whole row, then the same comparison emit 8192 keys at
 // a time.
 //
-// For the current-query row of the layer step, the emit also looks every
-// selected index up in the prediction (held in LDS; each thread walks it
-// forward alongside its own ascending entries, from the first position that
-// falls in its words): hits keep the prediction's slot row, misses get rows
-// k, k + 1, ... in ascending order.
+// For the current-query row of the layer step, the filter path marks the
+// prediction in a bitmap of the row: a selected entry without a mark is a
+// miss and gets slot row k, k + 1, ... in ascending order, and a marked one
+// keeps its position in the prediction as its slot row (each prediction
+// entry finds its place in the selection from the final bitmap and the
+// per-word output positions).  The radix path looks each selected index up
+// in the prediction list (each thread walks it forward alongside its own
+// ascending entries).
 // With attention fused in, that workgroup then runs the sparse decode
 // attention of the current query over its selection (DualDecoder, Figure 1
 // "Attention" box) from the slot rows and entry numbers it left in LDS,
@@ -84,10 +87,6 @@ struct Lay {
 static_assert(Lay<true>::words * 4 <= 160 * 1024, "cached layout exceeds LDS");
 static_assert(Lay<false>::words * 4 <= 160 * 1024, "long-row layout exceeds LDS");
 static_assert(4 * 256 <= kBins, "selection histograms fit the bound histogram");
-// Once the bound is picked, the filter path keeps, above the selection's
-// histograms, the first prediction position of each thread's words.
-constexpr int kLFirst = kLHist + 4 * 256;
-static_assert(4 * 256 + kNT <= kBins, "walk starts fit the bound histogram");
 // attention scratch, both queries (dual-token): per-wave partials and up to
 // 32 chunk partials of D+2 each; the tail of region C for a cached row, the
 // candidate lists otherwise (both free once the selection is emitted)
@@ -208,9 +207,16 @@ __device__ __forceinline__ void select_kth(const uint32_t* fkey, int cnt, int k,
   constexpr int R = CAP / kNT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  // Register r holds candidate tid + kNT r; the loops over r stop at the
+  // first r with kNT r >= cnt (a uniform branch), so only the live ones run.
   uint32_t x[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) x[r] = tid + kNT * r < cnt ? fkey[tid + kNT * r] : 0u;
+  for (int r = 0; r < R; ++r) x[r] = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (kNT * r >= cnt) break;
+    if (tid + kNT * r < cnt) x[r] = fkey[tid + kNT * r];
+  }
   uint32_t prefix = 0u, pmask = 0u;
   int kr = k;
 #pragma unroll 1
@@ -218,8 +224,10 @@ __device__ __forceinline__ void select_kth(const uint32_t* fkey, int cnt, int k,
     const int shift = 24 - 8 * pass;
     uint32_t* h = h4 + 256 * pass;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r) {
+      if (kNT * r >= cnt) break;
       if (tid + kNT * r < cnt && (x[r] & pmask) == prefix) atomicAdd(&h[(x[r] >> shift) & 255u], 1u);
+    }
     __syncthreads();
     // lane l holds digits 255 - 4l .. 252 - 4l, highest first
     const u32x4 c = reinterpret_cast<const u32x4*>(h)[63 - lane];
@@ -264,10 +272,17 @@ __device__ __forceinline__ void select_kth(const uint32_t* fkey, int cnt, int k,
 // (lcur) of every selected entry, in LDS for the fused attention.
 struct Sink {
   int32_t* out;
-  const int32_t* s_pred;  // nullptr: no bookkeeping
+  const int32_t* s_pred;  // the prediction list (radix path), or nullptr
   int plen;
   int32_t* lpos;
   int32_t* lcur;
+  // Filter path: the prediction as a bitmap of the row (pbits, nwords
+  // words), and where the emit leaves the final selection bitmap (gfin) and
+  // the output position of each word's first selected entry (wpre).
+  const uint32_t* pbits = nullptr;
+  uint32_t* gfin = nullptr;
+  int32_t* wpre = nullptr;
+  int nwords = 0;
 };
 
 // Emits, in ascending index order, the selected entries of this thread's
@@ -290,6 +305,51 @@ __device__ __forceinline__ int emit_words(uint32_t (&g)[MAXW], const uint32_t (&
     take -= tw;
   }
   int j = j0;
+  if (sk.pbits != nullptr) {
+    // Hits and misses straight from the prediction's bitmap: an entry is a
+    // miss where the prediction has no bit.  Every entry's slot row is
+    // first a placeholder (INT_MAX); misses get rows k, k + 1, ... after the
+    // scan of miss counts, and hits get their prediction position from
+    // prediction_rows once the final bitmap and word positions are stored.
+    uint32_t mm[MAXW];
+    int my_miss = 0;
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) {
+      const int wi = w0 + w;
+      mm[w] = g[w] != 0u ? g[w] & ~sk.pbits[wi] : 0u;
+      my_miss += __popc(mm[w]);
+#pragma unroll 1
+      for (uint32_t x = g[w]; x != 0u; x &= x - 1u) {
+        const int c = wi * 32 + __ffs(x) - 1;
+        if (j < k) {
+          sk.out[j] = c;
+          sk.lcur[j] = c;
+          sk.lpos[j] = INT_MAX;
+        }
+        ++j;
+      }
+    }
+    int mtot;
+    int mr = miss_base + block_scan<kNW>(my_miss, sb, mtot);
+    int jb = j0;  // output position of word w's first selected entry
+    const int wn = (sk.nwords + kNT - 1) / kNT;  // words per thread: only those are this thread's
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) {
+#pragma unroll 1
+      for (uint32_t x = mm[w]; x != 0u; x &= x - 1u) {
+        const int b = __ffs(x) - 1;
+        const int jj = jb + __popc(g[w] & ((1u << b) - 1u));
+        if (jj < k) sk.lpos[jj] = k + mr;
+        ++mr;
+      }
+      if (w < wn && w0 + w < sk.nwords) {
+        sk.gfin[w0 + w] = g[w];
+        sk.wpre[w0 + w] = jb;
+      }
+      jb += __popc(g[w]);
+    }
+    return mtot;
+  }
   if (sk.s_pred == nullptr) {
 #pragma unroll
     for (int w = 0; w < MAXW; ++w) {
@@ -394,10 +454,51 @@ __device__ __forceinline__ void store_prediction(const int32_t (&pv)[kPR], int k
   pf = pn = 0;
 #pragma unroll
   for (int r = 0; r < kPR; ++r) {
+    if (kNT * r >= k) break;  // entries r and later are -1 (see the load)
     const int p = (int)threadIdx.x + kNT * r;
     if (p < k) s_pred[p] = pv[r];
     pf += (pv[r] >= 0 && (int64_t)pv[r] < n_max) ? 1 : 0;
     pn += pv[r] >= 0 ? 1 : 0;
+  }
+}
+
+// Filter path, bookkeeping rows: sets the prediction's bit of every entry
+// in [0, n) in pbits (cleared before a barrier that precedes this call)
+// and counts this thread's fetchable (in [0, n_max)) and non-negative
+// prediction entries.
+__device__ __forceinline__ void mark_prediction(const int32_t (&pv)[kPR], int k, int n,
+                                                int64_t n_max, uint32_t* pbits, int& pf, int& pn) {
+  pf = pn = 0;
+#pragma unroll
+  for (int r = 0; r < kPR; ++r) {
+    if (kNT * r >= k) break;  // entries r and later are -1
+    const int c = pv[r];
+    if (c >= 0 && c < n) atomicOr(&pbits[c >> 5], 1u << (c & 31));
+    pf += (c >= 0 && (int64_t)c < n_max) ? 1 : 0;
+    pn += c >= 0 ? 1 : 0;
+  }
+}
+
+// Filter path, bookkeeping rows, after the emit and a barrier: each
+// prediction entry p that the selection holds gives the slot row of that
+// entry, p; with repeats the lowest p wins.  Entry j of the selection is
+// wpre[w] plus the selected bits below it in word w.
+__device__ __forceinline__ void prediction_rows(const int32_t (&pv)[kPR], int k, int n,
+                                                const uint32_t* gfin, const int32_t* wpre,
+                                                int32_t* lpos) {
+#pragma unroll
+  for (int r = 0; r < kPR; ++r) {
+    if (kNT * r >= k) break;
+    const int p = (int)threadIdx.x + kNT * r;
+    const int c = pv[r];
+    if (p < k && c >= 0 && c < n) {
+      const uint32_t gw = gfin[c >> 5];
+      const int b = c & 31;
+      if ((gw >> b) & 1u) {
+        const int j = wpre[c >> 5] + __popc(gw & ((1u << b) - 1u));
+        if (j < k) atomicMin(&lpos[j], p);
+      }
+    }
   }
 }
 
@@ -513,8 +614,6 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
   pick_bin(hist, k, sb, bcast, d0, above);
   const float fb = key_floor((uint32_t)d0 << 21);
   clear(hist, 4 * 256);  // the selection's histograms (ordered by the next barrier)
-  int* s_first = reinterpret_cast<int*>(smem + kLFirst);
-  if (book) s_first[tid] = INT_MAX;
 
   // Candidates: every entry >= fb, by index.  Count, scan, then write.
   int cnt;
@@ -582,28 +681,22 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
   const int nw = (n + 31) >> 5;
   uint32_t* gt = regc;
   uint32_t* eq = regc + nw;
-  int32_t* s_pred = reinterpret_cast<int32_t*>(smem + L::pred);
+  // The prediction as a bitmap of the row, where the prediction list would
+  // sit (the filter path never stores the list).
+  uint32_t* pbits = smem + L::pred;
   clear(regc, 2 * nw);
+  if (book) clear(pbits, nw);  // ordered before the marks by select_kth's barriers
   int pf = 0, pn = 0;
-  if (book) {
-    store_prediction(pv, k, n_max, s_pred, pf, pn);
-    sk.s_pred = s_pred;
-    // Where each thread's walk through the prediction starts: the first
-    // position whose entry lies in the thread's bitmap words (the emit's
-    // W words per thread).
-    const int W = (nw + kNT - 1) / kNT;
-#pragma unroll
-    for (int r = 0; r < kPR; ++r) {
-      const int p = tid + kNT * r;
-      if (p < k && pv[r] >= 0 && pv[r] < n) {
-        const int owner = (pv[r] >> 5) / W;
-        atomicMin(&s_first[owner], p);
-      }
-    }
-  }
   uint32_t thr;
   int take_eq;
   select_kth<CAP>(fkey, cnt, k, hist, thr, take_eq);
+  if (book) {
+    mark_prediction(pv, k, n, n_max, pbits, pf, pn);
+    sk.pbits = pbits;
+    sk.gfin = gt;
+    sk.wpre = reinterpret_cast<int32_t*>(eq);  // read into registers by the emit first
+    sk.nwords = nw;
+  }
   for (int i = tid; i < cnt; i += kNT) {
     const uint32_t x = fkey[i];
     const int c = fidx[i];
@@ -612,13 +705,12 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
   }
   __syncthreads();
   // A cached row has at most kTile / 32 bitmap words: 4 per thread.
-  int lo = kNoStart;
-  if (book) {
-    const int f = s_first[tid];
-    lo = f == INT_MAX ? kNoStart : f;
-  }
   misses = emit_bitmaps<CACHED ? kTile / 32 / kNT : kMaxWords>(gt, eq, nw, take_eq, k, sk, pf, pn,
-                                                                  sb, fetchable, lo);
+                                                                  sb, fetchable, kNoStart);
+  if (book) {
+    __syncthreads();  // final bitmap and word positions stored
+    prediction_rows(pv, k, n, gt, reinterpret_cast<const int32_t*>(eq), sk.lpos);
+  }
   return true;
 }
 
@@ -879,11 +971,17 @@ __global__ __launch_bounds__(kNT) void k_topk(
     load_tile(row, (int)n_max, 0, vec, v0);
   }
   // The prediction row, loaded now and stored in LDS once it is needed.
+  // The loops over a thread's entries stop at the first r with
+  // kNT * r >= k (a uniform branch), so a small k runs one iteration of
+  // code; entries past that stay -1.
   int32_t pv[kPR];
 #pragma unroll
+  for (int r = 0; r < kPR; ++r) pv[r] = -1;
+#pragma unroll
   for (int r = 0; r < kPR; ++r) {
+    if (kNT * r >= k) break;
     const int p = tid + kNT * r;
-    pv[r] = (pred_row != nullptr && p < k) ? pred_row[p] : -1;
+    if (pred_row != nullptr && p < k) pv[r] = pred_row[p];
   }
   clear(smem + kLHist, kBins);
   const int32_t len_b = lens[bh / H];
