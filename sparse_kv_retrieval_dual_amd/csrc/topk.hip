@@ -594,13 +594,26 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
     } else {
       load_tile(row, n, c0, vec, v);
     }
+    // A tile whose entries are all below n needs no masks (a uniform
+    // branch; the same maxima either way).
+    if (n >= c0 + kTile) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int q = tid + kNT * u;
-      if (CACHED) reinterpret_cast<f32x4*>(regc)[q] = v[u];
-      const float m = max_valid(v[u], c0 + 4 * q, n);
-      if (CACHED) f4max[u] = m;
-      gmax[u / UPG] = fmaxf(gmax[u / UPG], m);
+      for (int u = 0; u < kU; ++u) {
+        const int q = tid + kNT * u;
+        if (CACHED) reinterpret_cast<f32x4*>(regc)[q] = v[u];
+        const float m = fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w));
+        if (CACHED) f4max[u] = m;
+        gmax[u / UPG] = fmaxf(gmax[u / UPG], m);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int q = tid + kNT * u;
+        if (CACHED) reinterpret_cast<f32x4*>(regc)[q] = v[u];
+        const float m = max_valid(v[u], c0 + 4 * q, n);
+        if (CACHED) f4max[u] = m;
+        gmax[u / UPG] = fmaxf(gmax[u / UPG], m);
+      }
     }
   }
   __syncthreads();  // also orders the caller's clear of hist
@@ -619,9 +632,14 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
   int cnt;
   if (CACHED) {
     uint32_t um = 0u;
+    if (n >= kTile) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
-      um |= (4 * (tid + kNT * u) < n && f4max[u] >= fb) ? (1u << u) : 0u;
+      for (int u = 0; u < kU; ++u) um |= f4max[u] >= fb ? (1u << u) : 0u;
+    } else {
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        um |= (4 * (tid + kNT * u) < n && f4max[u] >= fb) ? (1u << u) : 0u;
+    }
     int my = 0;
 #pragma unroll 1
     for (uint32_t x = um; x != 0u; x &= x - 1u) {
