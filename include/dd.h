@@ -225,8 +225,9 @@ typedef struct dd_ctx_config {
                       is restricted to this many CUs and the layer step's own
                       main stream to the others */
   int prefetch_wgs; /* workgroups of the prefetch gather (0: 32, or 64 for a
-                      layer prefetch of 16 MiB or more; four times as many
-                      when rows are kept across steps).  Fewer keep
+                      layer prefetch of 16 MiB or more inside the scoring
+                      kernel; four times as many when rows are kept across
+                      steps).  Fewer keep
                       fewer host reads outstanding, which disturbs the
                       concurrent HBM-bound scoring less; enough of them
                       still saturate the host link */

@@ -39,11 +39,13 @@ constexpr int kResidentWgsScale = 4;
 
 // Workgroups of one layer's prefetch when the context leaves it open: 32 for
 // a small prefetch (1 MiB at batch 1, k = 128: 16 to 32 were equal, 8 too
-// few), 64 from 16 MiB up (84 MiB at batch 4 x 40 heads, k = 2048: 2.06 ms
-// per layer against 2.14 ms with 32), times kResidentWgsScale for kept rows.
-int prefetch_wgs_for(const dd_ctx* c, int64_t rows, int row_bytes, bool resident) {
+// few); inside the scoring kernel 64 from 16 MiB up (84 MiB at batch 4 x 40
+// heads, k = 2048: 2.06 ms per layer against 2.14 ms with 32), while on the
+// side stream 64 slowed a 32-layer step at batch 16, k = 1024 from 102.5 to
+// 107.6 ms; times kResidentWgsScale for kept rows.
+int prefetch_wgs_for(const dd_ctx* c, int64_t rows, int row_bytes, bool resident, bool fused) {
   int w = c->prefetch_wgs;
-  if (w == 0) w = rows * row_bytes >= (int64_t(16) << 20) && !resident ? 64 : 32;
+  if (w == 0) w = fused && !resident && rows * row_bytes >= (int64_t(16) << 20) ? 64 : 32;
   return resident ? kResidentWgsScale * w : w;
 }
 
@@ -550,7 +552,7 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
                            reinterpret_cast<uint8_t*>(vslot), 2 * (int64_t)k, 0, cs, rowb};
     // Bytes the prefetch moves: V rows (and K rows from the host).
     const int pf_wgs = prefetch_wgs_for(c, ((int64_t)BH * ks) << cs, rowb * (kdev ? 1 : 2),
-                                        resident);
+                                        resident, fused);
 
     if (P && use_side) {
       if (l >= R && !resident)
