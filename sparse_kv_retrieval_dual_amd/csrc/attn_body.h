@@ -146,6 +146,54 @@ __device__ __forceinline__ void attn_fetch(const AttnRows<T>& R, int c0, int lim
   }
 }
 
+// attn_fetch for the common case of the layer step: every K row from the
+// device key copy by row index (kdb set), no previous slot (vob null).  The
+// same rows and addresses as attn_fetch with fewer selects on the way.
+template <typename T, int D, class Entry>
+__device__ __forceinline__ void attn_fetch_kdev(const AttnRows<T>& R, int c0, int lim, Entry entry,
+                                                AttnFetch<T, D>& f, int tid) {
+  using S = AttnShape<T, D>;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane % S::LPR;
+  const int rsub = lane / S::LPR;
+  const int e0 = c0 + wave * kWaveEntries;
+  const bool from_host = R.vhb != nullptr;
+  int krow[S::U];
+#pragma unroll
+  for (int u = 0; u < S::U; ++u) {
+    const int j = e0 + u * S::RPI + rsub;
+    int r = -1, c = -1, o = -1;
+    if (j < lim && R.m > 0) {
+      entry(j, r, c, o);
+      if (r < 0 || r >= R.m) r = -1;
+    }
+    if (c < 0 || (int64_t)c >= R.n_max) r = -1;
+    const bool miss = from_host && r >= R.first_miss_row;
+    f.rows[u] = r;
+    f.hrow[u] = (r >= 0 && miss) ? c : -1;
+    krow[u] = r >= 0 ? c : 0;
+  }
+  const T* vb = R.vb + col * S::EPL;
+  const T* vhb = from_host ? R.vhb + col * S::EPL : vb;
+  const T* kdb = R.kdb + col * S::EPL;
+  const bool any = R.m > 0;
+#pragma unroll
+  for (int u = 0; u < S::U; ++u) {
+    u32x4 kv = u32x4{0u, 0u, 0u, 0u};
+    u32x4 vv = kv;
+    if (any) {
+      kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kdb + (int64_t)krow[u] * D));
+      const bool h = f.hrow[u] >= 0;
+      const T* vsrc = h ? vhb + (int64_t)f.hrow[u] * D
+                        : vb + (int64_t)(f.rows[u] >= 0 ? f.rows[u] : 0) * D;
+      vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vsrc));
+    }
+    f.kr[u] = kv;
+    f.vr[u] = vv;
+  }
+}
+
 // Second half of a chunk fetched by attn_fetch (tid: the thread's index in
 // the 256 that handle the chunk; every thread of the workgroup must call
 // it, since it holds a workgroup barrier), for the first nq <= NQ
@@ -281,14 +329,18 @@ __device__ __forceinline__ void attn_finish(const float* __restrict__ q, const A
   }
 }
 
-// Entries c0 .. c0 + 127 (those < lim): attn_fetch, then attn_finish.
-template <typename T, int D, int NQ, class Entry>
+// Entries c0 .. c0 + 127 (those < lim): attn_fetch (attn_fetch_kdev when
+// KDEV: K rows from the device copy, no previous slot), then attn_finish.
+template <typename T, int D, int NQ, bool KDEV = false, class Entry>
 __device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, const AttnRows<T>& R,
                                                int c0, int lim, float scale, Entry entry,
                                                AttnLds<D, NQ>& lds, int nq, float (&cm)[NQ],
                                                float (&cl)[NQ], float (&od)[NQ]) {
   AttnFetch<T, D> f;
-  attn_fetch<T, D>(R, c0, lim, entry, f, threadIdx.x);
+  if constexpr (KDEV)
+    attn_fetch_kdev<T, D>(R, c0, lim, entry, f, threadIdx.x);
+  else
+    attn_fetch<T, D>(R, c0, lim, entry, f, threadIdx.x);
   attn_finish<T, D, NQ>(q, R, scale, f, lds, nq, cm, cl, od, threadIdx.x);
 }
 

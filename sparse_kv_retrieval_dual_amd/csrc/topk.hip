@@ -884,7 +884,11 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
   const int d = threadIdx.x;
   for (int ch = 0; ch < chunks; ++ch) {
     float cm[NQ], cl[NQ], od[NQ];
-    attend_chunk_n<T, D, NQ>(qrow, R, ch * kAttnChunk, k, fa.scale, entry, lds, nq, cm, cl, od);
+    if (kdev && lold == nullptr)
+      attend_chunk_n<T, D, NQ, true>(qrow, R, ch * kAttnChunk, k, fa.scale, entry, lds, nq, cm, cl,
+                                     od);
+    else
+      attend_chunk_n<T, D, NQ>(qrow, R, ch * kAttnChunk, k, fa.scale, entry, lds, nq, cm, cl, od);
     if (d < D) {
       for (int qi = 0; qi < nq; ++qi) {
         if (chunks == 1) {
