@@ -447,6 +447,58 @@ __device__ __forceinline__ int emit_bitmaps(const uint32_t* gt, const uint32_t* 
   return emit_words<MAXW>(g, e, w0, ex & 0xFFFF, ex >> 16, take_eq, k, sk, sb, 0, lo);
 }
 
+// emit_bitmaps for a bookkeeping row of the filter path when no key equal
+// to T is taken (take_eq = 0; with distinct scores the last radix pass
+// always ends that way): the selection is the "> T" bitmap alone, so each
+// thread knows its misses (selected, no mark in the prediction's bitmap)
+// before the scan, and one scan of (selected | misses, fetchable | non-
+// negative prediction entries) gives every position.  Same outputs as
+// emit_bitmaps + emit_words.
+template <int MAXW>
+__device__ __forceinline__ int emit_book_fast(const uint32_t* gt, int nw, int k, Sink& sk, int pf,
+                                              int pn, ScanBufs& sb, int& fetchable) {
+  const int W = (nw + kNT - 1) / kNT;
+  const int w0 = (int)threadIdx.x * W;
+  uint32_t g[MAXW], mm[MAXW];
+  int gc = 0, mc = 0;
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w) {
+    const bool in = w < W && w0 + w < nw;
+    g[w] = in ? gt[w0 + w] : 0u;
+    mm[w] = g[w] != 0u ? g[w] & ~sk.pbits[w0 + w] : 0u;
+    gc += __popc(g[w]);
+    mc += __popc(mm[w]);
+  }
+  // Both totals are at most k < 2^16.
+  int ex, ep, tx, tp;
+  block_scan_pair<kNW>(gc | (mc << 16), pf | (pn << 16), sb, ex, ep, tx, tp);
+  fetchable = tp & 0xFFFF;
+  int j = ex & 0xFFFF;  // output position of this thread's first entry
+  int mr = ex >> 16;    // misses in lower words
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w) {
+    const int jb = j;
+#pragma unroll 1
+    for (uint32_t x = g[w]; x != 0u; x &= x - 1u) {
+      const int b = __ffs(x) - 1;
+      const int c = (w0 + w) * 32 + b;
+      if (j < k) {
+        sk.out[j] = c;
+        sk.lcur[j] = c;
+        const bool miss = (mm[w] >> b) & 1u;
+        sk.lpos[j] = miss ? k + mr : INT_MAX;
+        mr += miss ? 1 : 0;
+      }
+      ++j;
+    }
+    if (w < W && w0 + w < nw) {
+      sk.gfin[w0 + w] = g[w];
+      sk.wpre[w0 + w] = jb;
+    }
+  }
+  return tx >> 16;
+}
+
 // Stores this thread's prediction entries in s_pred; counts the fetchable
 // (in [0, n_max)) and non-negative ones.
 __device__ __forceinline__ void store_prediction(const int32_t (&pv)[kPR], int k, int64_t n_max,
@@ -723,8 +775,10 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
   }
   __syncthreads();
   // A cached row has at most kTile / 32 bitmap words: 4 per thread.
-  misses = emit_bitmaps<CACHED ? kTile / 32 / kNT : kMaxWords>(gt, eq, nw, take_eq, k, sk, pf, pn,
-                                                                  sb, fetchable, kNoStart);
+  constexpr int MAXW = CACHED ? kTile / 32 / kNT : kMaxWords;
+  misses = (book && take_eq == 0)
+               ? emit_book_fast<MAXW>(gt, nw, k, sk, pf, pn, sb, fetchable)
+               : emit_bitmaps<MAXW>(gt, eq, nw, take_eq, k, sk, pf, pn, sb, fetchable, kNoStart);
   if (book) {
     __syncthreads();  // final bitmap and word positions stored
     prediction_rows(pv, k, n, gt, reinterpret_cast<const int32_t*>(eq), sk.lpos);
