@@ -692,19 +692,45 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
       for (int u = 0; u < kU; ++u)
         um |= (4 * (tid + kNT * u) < n && f4max[u] >= fb) ? (1u << u) : 0u;
     }
-    int my = 0;
+    // The first two of this thread's candidate float4s are read together
+    // and kept in registers for both passes; any others are read per pass.
+    const f32x4* rc4 = reinterpret_cast<const f32x4*>(regc);
+    uint32_t rest = um;
+    const int q0 = rest != 0u ? tid + kNT * (__ffs(rest) - 1) : -1;
+    rest &= rest - 1u;
+    const int q1 = rest != 0u ? tid + kNT * (__ffs(rest) - 1) : -1;
+    rest &= rest - 1u;
+    const f32x4 f0 = rc4[q0 >= 0 ? q0 : tid];
+    const f32x4 f1 = rc4[q1 >= 0 ? q1 : tid];
+    const uint32_t m0 = q0 >= 0 ? passing(f0, 4 * q0, n, fb) : 0u;
+    const uint32_t m1 = q1 >= 0 ? passing(f1, 4 * q1, n, fb) : 0u;
+    int my = __popc(m0) + __popc(m1);
 #pragma unroll 1
-    for (uint32_t x = um; x != 0u; x &= x - 1u) {
+    for (uint32_t x = rest; x != 0u; x &= x - 1u) {
       const int q = tid + kNT * (__ffs(x) - 1);
-      my += __popc(passing(reinterpret_cast<const f32x4*>(regc)[q], 4 * q, n, fb));
+      my += __popc(passing(rc4[q], 4 * q, n, fb));
     }
     int off = block_scan<kNW>(my, sb, cnt);
     if (cnt > CAP) return false;
     // Each candidate's index and key, from the float4 it sits in.
 #pragma unroll 1
-    for (uint32_t x = um; x != 0u; x &= x - 1u) {
+    for (uint32_t m = m0; m != 0u; m &= m - 1u) {
+      const int c = __ffs(m) - 1;
+      fidx[off] = 4 * q0 + c;
+      fkey[off] = order_key(f4_at(f0, c));
+      ++off;
+    }
+#pragma unroll 1
+    for (uint32_t m = m1; m != 0u; m &= m - 1u) {
+      const int c = __ffs(m) - 1;
+      fidx[off] = 4 * q1 + c;
+      fkey[off] = order_key(f4_at(f1, c));
+      ++off;
+    }
+#pragma unroll 1
+    for (uint32_t x = rest; x != 0u; x &= x - 1u) {
       const int q = tid + kNT * (__ffs(x) - 1);
-      const f32x4 f = reinterpret_cast<const f32x4*>(regc)[q];
+      const f32x4 f = rc4[q];
 #pragma unroll 1
       for (uint32_t m = passing(f, 4 * q, n, fb); m != 0u; m &= m - 1u) {
         const int c = __ffs(m) - 1;
