@@ -160,14 +160,25 @@ __device__ __forceinline__ void attn_fetch_kdev(const AttnRows<T>& R, int c0, in
   const int e0 = c0 + wave * kWaveEntries;
   const bool from_host = R.vhb != nullptr;
   int krow[S::U];
+  // Every entry is looked up first (an entry past lim looks up entry
+  // lim - 1 and is dropped), so that the lookups are in flight together.
+  int er[S::U], ec[S::U];
+#pragma unroll
+  for (int u = 0; u < S::U; ++u) er[u] = ec[u] = -1;
+  if (lim > 0 && R.m > 0) {
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      const int j = e0 + u * S::RPI + rsub;
+      int o;
+      entry(j < lim ? j : lim - 1, er[u], ec[u], o);
+    }
+  }
 #pragma unroll
   for (int u = 0; u < S::U; ++u) {
     const int j = e0 + u * S::RPI + rsub;
-    int r = -1, c = -1, o = -1;
-    if (j < lim && R.m > 0) {
-      entry(j, r, c, o);
-      if (r < 0 || r >= R.m) r = -1;
-    }
+    int r = j < lim ? er[u] : -1;
+    const int c = ec[u];
+    if (r < 0 || r >= R.m) r = -1;
     if (c < 0 || (int64_t)c >= R.n_max) r = -1;
     const bool miss = from_host && r >= R.first_miss_row;
     f.rows[u] = r;
