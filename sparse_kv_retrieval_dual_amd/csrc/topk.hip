@@ -521,7 +521,7 @@ __device__ __forceinline__ void store_prediction(const int32_t (&pv)[kPR], int k
 __device__ __forceinline__ void mark_prediction(const int32_t (&pv)[kPR], int k, int n,
                                                 int64_t n_max, uint32_t* pbits, int& pf, int& pn) {
   pf = pn = 0;
-#pragma unroll
+  // (left to the compiler: with the atomic inside, it keeps this loop rolled)
   for (int r = 0; r < kPR; ++r) {
     if (kNT * r >= k) break;  // entries r and later are -1
     const int c = pv[r];
