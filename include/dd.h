@@ -236,6 +236,14 @@ typedef struct dd_ctx_config {
                       DD_PREFETCH_SIDE or DD_PREFETCH_FUSED */
   int k_rows;       /* DD_KROWS_DEVICE (0) or DD_KROWS_HOST: where attention
                       reads the K rows of the selected entries */
+  /* Race detection: when > 0, dd_layer_step enqueues a fixed stall of about
+     this many microseconds (a single-wave kernel that sleeps and ends) on
+     the side stream before each prefetch gather (side) or on the main stream
+     before each selection + attention kernel (main), so that tests can move
+     the two streams' relative timing.  Results must not change; 0 in
+     production. */
+  int perturb_side_us;
+  int perturb_main_us;
 } dd_ctx_config;
 
 /* DD_PREFETCH_SIDE: the prediction of layer l is fetched on the side stream
@@ -354,6 +362,13 @@ DD_API int dd_layer_step(dd_ctx* ctx, const dd_layer_step_args* args);
  * (bytes must be a multiple of 16, pointers 16-byte aligned).  Used to
  * calibrate hardware counters and to measure the achievable HBM rate. */
 DD_API int dd_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+/* Measurement utility: a plain streaming read of bytes at src (a multiple of
+ * 16, 16-byte aligned) with the non-temporal loads the scoring kernel uses;
+ * the achievable HBM read rate, the scoring kernel's own kind of traffic.
+ * sink: device memory of at least 256 bytes (16-byte aligned) whose
+ * contents afterwards are meaningless. */
+DD_API int dd_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -23,6 +23,7 @@ from .api import (  # noqa: F401
     score,
     sparse_attn,
     stream_copy,
+    stream_read,
     topk,
 )
 from ._lib import DD_MAX_K, DD_STAGE_EVENTS, DDError  # noqa: F401

@@ -33,7 +33,8 @@ P = c_void_p  # every pointer crosses as an address
 
 class CtxConfig(ctypes.Structure):
     _fields_ = [("ring_slots", c_int), ("gather_cus", c_int), ("prefetch_wgs", c_int),
-                ("prefetch_mode", c_int), ("k_rows", c_int)]
+                ("prefetch_mode", c_int), ("k_rows", c_int), ("perturb_side_us", c_int),
+                ("perturb_main_us", c_int)]
 
 
 class LayerStepArgs(ctypes.Structure):
@@ -72,6 +73,7 @@ _SIGNATURES = {
     "dd_resident_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int64, c_int, c_int]),
     "dd_layer_step": (c_int, [P, ctypes.POINTER(LayerStepArgs)]),
     "dd_stream_copy": (c_int, [P, P, c_size_t, P]),
+    "dd_stream_read": (c_int, [P, c_size_t, P, P]),
     "dd_gather_chunks": (c_int, [P, P, P, P, c_int, c_int, c_int, c_int, c_int, c_int64, c_int,
                                  P, P, P]),
     "dd_landmarks": (c_int, [P, P, c_int, c_int, c_int, c_int64, c_int, c_int, P, P]),

@@ -256,6 +256,14 @@ def stream_copy(src, dst, stream=None):
     return dst
 
 
+def stream_read(src, sink, stream=None):
+    """dd_stream_read: a streaming read of src's bytes (sink: >= 256 device bytes)."""
+    _dev(src, "src"), _dev(sink, "sink")
+    n = src.numel() * src.element_size()
+    _need(sink.numel() * sink.element_size() >= 256, "sink needs 256 bytes")
+    L.check(_lib().dd_stream_read(_p(src), n, _p(sink), _stream(stream)))
+
+
 # --------------------------------------------------------------------------- layer step
 def ring_bytes(ring_slots: int, B: int, H: int, D: int, k: int, dtype: int) -> int:
     return int(_lib().dd_ring_bytes(ring_slots, B, H, D, k, dtype))
@@ -284,12 +292,14 @@ class Context:
     K_ROWS = {"device": 0, "host": 1}
 
     def __init__(self, ring_slots: int = 2, gather_cus: int = 0, prefetch_wgs: int = 0,
-                 prefetch: str = "auto", k_rows: str = "device"):
+                 prefetch: str = "auto", k_rows: str = "device", perturb_side_us: int = 0,
+                 perturb_main_us: int = 0):
         lib = _lib()
         cfg = L.CtxConfig(ring_slots=int(ring_slots), gather_cus=int(gather_cus),
                           prefetch_wgs=int(prefetch_wgs),
                           prefetch_mode=self.PREFETCH_MODES[prefetch],
-                          k_rows=self.K_ROWS[k_rows])
+                          k_rows=self.K_ROWS[k_rows], perturb_side_us=int(perturb_side_us),
+                          perturb_main_us=int(perturb_main_us))
         h = ctypes.c_void_p()
         L.check(lib.dd_ctx_create(ctypes.byref(cfg), ctypes.byref(h)))
         self._h = h

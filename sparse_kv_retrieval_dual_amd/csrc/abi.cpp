@@ -22,6 +22,8 @@ struct dd_ctx {
   int prefetch_wgs = 0;             // 0: sized per layer (prefetch_wgs_for)
   int prefetch_mode = DD_PREFETCH_AUTO;
   int k_rows = DD_KROWS_DEVICE;
+  int perturb_side_us = 0;          // race detection: stalls before each side /
+  int perturb_main_us = 0;          // main-stream stage of the layer step
   hipStream_t side = nullptr;       // prefetch gathers
   hipStream_t main_own = nullptr;   // CU-masked main stream (gather_cus > 0 only)
   hipEvent_t ev_start = nullptr;    // caller stream at entry
@@ -91,9 +93,10 @@ int check_k(int k) {
   return DD_OK;
 }
 
-// Workspace of the layer step, carved in this order.
+// Workspace of the layer step, carved in this order: the two score planes
+// of a layer and their group maxima (kMaxGroup keys per group).
 struct StepLayout {
-  size_t scores, total;
+  size_t scores, gmax, total;
 };
 
 StepLayout step_layout(int B, int H, int D, int64_t n_max, int k) {
@@ -102,6 +105,8 @@ StepLayout step_layout(int B, int H, int D, int64_t n_max, int k) {
   size_t off = 0;
   l.scores = off;
   off += align_up(BH * 2 * (size_t)n_max * sizeof(float));
+  l.gmax = off;
+  off += align_up(BH * 2 * (size_t)dd::max_group_stride(n_max) * sizeof(float));
   l.total = off;
   (void)D;
   (void)k;
@@ -358,12 +363,17 @@ DD_API int dd_ctx_create(const dd_ctx_config* cfg, dd_ctx** ctx) {
     return fail(DD_ERR_INVALID_ARG, "unknown prefetch_mode %d", cfg->prefetch_mode);
   if (cfg->k_rows != DD_KROWS_DEVICE && cfg->k_rows != DD_KROWS_HOST)
     return fail(DD_ERR_INVALID_ARG, "unknown k_rows %d", cfg->k_rows);
+  if (cfg->perturb_side_us < 0 || cfg->perturb_main_us < 0 || cfg->perturb_side_us > 100000 ||
+      cfg->perturb_main_us > 100000)
+    return fail(DD_ERR_INVALID_ARG, "perturb_side_us / perturb_main_us must be in [0, 100000]");
   dd_ctx* c = new dd_ctx();
   c->ring_slots = cfg->ring_slots;
   c->gather_cus = cfg->gather_cus;
   c->prefetch_wgs = cfg->prefetch_wgs;
   c->prefetch_mode = cfg->prefetch_mode;
   c->k_rows = cfg->k_rows;
+  c->perturb_side_us = cfg->perturb_side_us;
+  c->perturb_main_us = cfg->perturb_main_us;
   hipError_t e = hipGetDevice(&c->device);
   const int cus = dd::device_info().cus;
   if (e == hipSuccess && c->gather_cus > 0) {
@@ -478,11 +488,15 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
   const StepLayout lay = step_layout(B, H, D, a->n_max, k);
   if (!a->ws || a->ws_bytes < lay.total)
     return fail(DD_ERR_WORKSPACE, "workspace too small: need %zu bytes, got %zu", lay.total, a->ws_bytes);
+  if (!aligned16(a->ws)) return fail(DD_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
 
   const float sc = a->scale > 0.f ? a->scale : 1.0f / sqrtf((float)D);
   const int rowb = D * dd::elem_bytes(a->dtype);
   char* ws = static_cast<char*>(a->ws);
   float* scores = reinterpret_cast<float*>(ws + lay.scores);
+  // Group maxima of the score rows, for a selection that reads only the
+  // groups that can hold a selected key (rows longer than one tile).
+  float* gmax = dd::topk_uses_maxima(n_sel) ? reinterpret_cast<float*>(ws + lay.gmax) : nullptr;
   const int R = c->ring_slots;
   hipStream_t caller = a->stream;
   hipStream_t ms = c->main_own ? c->main_own : caller;
@@ -557,6 +571,8 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     if (P && use_side) {
       if (l >= R && !resident)
         DD_CHECK_HIP(hipStreamWaitEvent(side, c->ev_free[slot], 0), "side waits slot");
+      if (c->perturb_side_us > 0)
+        DD_CHECK_HIP(dd::launch_delay(c->perturb_side_us, side), "side-stream stall");
       if (tev(l, 5)) DD_CHECK_HIP(hipEventRecord(tev(l, 5), side), "timing");
       // A kept-rows prefetch runs on more workgroups: each wave's
       // lookups (index, then the old slot's row) leave its host loads idle
@@ -584,10 +600,12 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
                                     pf_wgs, ms,
                                     score_ev ? tev(l, 0) : nullptr,
                                     score_ev ? tev(l, 1) : nullptr, st, cs,
-                                    (P && fused && resident) ? &res : nullptr);
+                                    (P && fused && resident) ? &res : nullptr, gmax);
     if (e != hipSuccess) return hip_fail(e, "score kernel launch");
     if (tev(l, 1) && !score_ev) DD_CHECK_HIP(hipEventRecord(tev(l, 1), ms), "timing");
     if (P && use_side) DD_CHECK_HIP(hipStreamWaitEvent(ms, c->ev_gathered[slot], 0), "main waits prefetch");
+    if (c->perturb_main_us > 0)
+      DD_CHECK_HIP(dd::launch_delay(c->perturb_main_us, ms), "main-stream stall");
     // Top-k of both queries, the bookkeeping of the current one and its
     // attention in one kernel: each current-query row's workgroup attends
     // right after its selection, reading misses from host memory itself
@@ -600,7 +618,7 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
                            (a->out_spec && a->out_spec[l] && a->lse_spec) ? a->lse_spec[l] : nullptr,
                            res.where, res.old_idx, res.new_idx, old_v, res.host_rows};
     e = dd::launch_topk(scores, a->lens, B, H, 2, n_sel, ks, a->cur_idx[l], a->spec_idx[l], ks,
-                        P, &fa, ms, cs);
+                        P, &fa, ms, cs, gmax);
     if (e != hipSuccess) return hip_fail(e, "top-k and attention kernel launch");
     for (int ev = 2; ev <= 4; ++ev)
       if (tev(l, ev)) DD_CHECK_HIP(hipEventRecord(tev(l, ev), ms), "timing");
@@ -620,6 +638,16 @@ DD_API int dd_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t 
     return fail(DD_ERR_INVALID_ARG, "bytes and pointers must be multiples of 16");
   hipError_t e = dd::launch_stream_copy(src, dst, bytes, stream);
   if (e != hipSuccess) return hip_fail(e, "copy kernel launch");
+  return DD_OK;
+}
+
+DD_API int dd_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream) {
+  if (bytes == 0) return DD_OK;
+  if (!src || !sink) return fail(DD_ERR_INVALID_ARG, "null pointer argument");
+  if ((bytes & 15) != 0 || !aligned16(src) || !aligned16(sink))
+    return fail(DD_ERR_INVALID_ARG, "bytes and pointers must be multiples of 16");
+  hipError_t e = dd::launch_stream_read(src, bytes, sink, stream);
+  if (e != hipSuccess) return hip_fail(e, "read kernel launch");
   return DD_OK;
 }
 

@@ -205,67 +205,28 @@ __device__ __forceinline__ void attn_fetch_kdev(const AttnRows<T>& R, int c0, in
   }
 }
 
-// Second half of a chunk fetched by attn_fetch (tid: the thread's index in
-// the 256 that handle the chunk; every thread of the workgroup must call
-// it, since it holds a workgroup barrier), for the first nq <= NQ
-// queries at once: query j is q + j * D (D floats; all NQ are read).  Every
-// K and V row is read once and serves every query; a missed row is first
-// copied into its slot row.  Contraction is off: only the explicit fmaf
-// calls fuse, so a query's result is the same bits whatever nq is.
+// The softmax and weighted V sum of one chunk from its logits, for the
+// first nq <= NQ queries: s[qi * U + u] is query qi's scaled logit of the
+// lane's entry u (entries with rows[u] < 0 are skipped), vr[u] its V row
+// bytes.  Each wave forms its own max, weights and weighted V sum over its
+// 32 entries; the four waves are then merged in LDS in wave order (one
+// workgroup barrier; every thread of the workgroup must call it).
 // Afterwards cm[j] and cl[j] (all threads) are query j's max logit and
 // weight sum over the chunk, and threads d < D hold od[j] = its weighted V
 // sum of column d.  The caller must not touch lds until a barrier after
 // this returns.
 template <typename T, int D, int NQ>
-__device__ __forceinline__ void attn_finish(const float* __restrict__ q, const AttnRows<T>& R,
-                                            float scale, const AttnFetch<T, D>& f,
-                                            AttnLds<D, NQ>& lds, int nq, float (&cm)[NQ],
-                                            float (&cl)[NQ], float (&od)[NQ], int tid) {
+__device__ __forceinline__ void attn_softmax_merge(float* s, const int* rows, const u32x4* vr,
+                                                   AttnLds<D, NQ>& lds, int nq,
+                                                   float (&cm)[NQ], float (&cl)[NQ],
+                                                   float (&od)[NQ], int tid) {
 #pragma clang fp contract(off)
   using S = AttnShape<T, D>;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int col = lane % S::LPR;
   const int rsub = lane / S::LPR;
-  const bool from_host = R.vhb != nullptr;
-  const bool kdev = R.kdb != nullptr;
   const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-  if (from_host && R.m > 0) {  // the slot keeps a copy of every fetched miss
-#pragma unroll
-    for (int u = 0; u < S::U; ++u) {
-      if (f.hrow[u] >= 0) {
-        T* vd = const_cast<T*>(R.vb) + col * S::EPL + (int64_t)f.rows[u] * D;
-        *reinterpret_cast<u32x4*>(vd) = f.vr[u];
-        if (!kdev) {
-          T* kd = const_cast<T*>(R.kb) + col * S::EPL + (int64_t)f.rows[u] * D;
-          *reinterpret_cast<u32x4*>(kd) = f.kr[u];
-        }
-      }
-    }
-  }
-  float qr[NQ][S::EPL];
-#pragma unroll
-  for (int qi = 0; qi < NQ; ++qi)
-#pragma unroll
-    for (int e = 0; e < S::EPL; ++e) qr[qi][e] = qi < nq ? q[qi * D + col * S::EPL + e] : 0.f;
-
-  // Logits: the first query always, the others only when they attend.
-  float s[NQ * S::U];  // s[qi * U + u]
-#pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) {
-    if (qi >= nq) break;
-#pragma unroll
-    for (int u = 0; u < S::U; ++u) {
-      float fk[S::EPL];
-      Unpack<T>::run(f.kr[u], fk);
-      float a = 0.f;
-#pragma unroll
-      for (int e = 0; e < S::EPL; ++e) a = fmaf(fk[e], qr[qi][e], a);
-      s[qi * S::U + u] = a;
-    }
-    group_allreduce<S::LPR, S::U>(s + qi * S::U);
-  }
-
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
     if (qi >= nq) break;
@@ -274,7 +235,7 @@ __device__ __forceinline__ void attn_finish(const float* __restrict__ q, const A
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
       float& x = s[qi * S::U + u];
-      x = (f.rows[u] >= 0) ? x * scale : -INFINITY;
+      x = (rows[u] >= 0) ? x : -INFINITY;
       mx = fmaxf(mx, x);
     }
 #pragma unroll
@@ -285,11 +246,11 @@ __device__ __forceinline__ void attn_finish(const float* __restrict__ q, const A
     for (int e = 0; e < S::EPL; ++e) o[e] = 0.f;
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
-      const float w = (f.rows[u] >= 0) ? exp2f((s[qi * S::U + u] - mx) * kLog2e) : 0.f;
+      const float w = (rows[u] >= 0) ? exp2f((s[qi * S::U + u] - mx) * kLog2e) : 0.f;
       l += w;
       float fv[S::EPL];
-      u32x4 vv = f.vr[u];  // a value select: selecting lvalues would put both in memory
-      if (f.rows[u] < 0) vv = zero;
+      u32x4 vv = vr[u];  // a value select: selecting lvalues would put both in memory
+      if (rows[u] < 0) vv = zero;
       Unpack<T>::run(vv, fv);
 #pragma unroll
       for (int e = 0; e < S::EPL; ++e) o[e] = fmaf(w, fv[e], o[e]);
@@ -338,6 +299,162 @@ __device__ __forceinline__ void attn_finish(const float* __restrict__ q, const A
     cl[qi] = tl;
     od[qi] = acc;
   }
+}
+
+// Second half of a chunk fetched by attn_fetch (tid: the thread's index in
+// the 256 that handle the chunk; every thread of the workgroup must call
+// it, since it holds a workgroup barrier), for the first nq <= NQ
+// queries at once: query j is q + j * D (D floats; all NQ are read).  Every
+// K and V row is read once and serves every query; a missed row is first
+// copied into its slot row.  Contraction is off: only the explicit fmaf
+// calls fuse, so a query's result is the same bits whatever nq is.
+// Outputs as attn_softmax_merge.
+template <typename T, int D, int NQ>
+__device__ __forceinline__ void attn_finish(const float* __restrict__ q, const AttnRows<T>& R,
+                                            float scale, const AttnFetch<T, D>& f,
+                                            AttnLds<D, NQ>& lds, int nq, float (&cm)[NQ],
+                                            float (&cl)[NQ], float (&od)[NQ], int tid) {
+#pragma clang fp contract(off)
+  using S = AttnShape<T, D>;
+  const int lane = tid & 63;
+  const int col = lane % S::LPR;
+  const bool from_host = R.vhb != nullptr;
+  const bool kdev = R.kdb != nullptr;
+  if (from_host && R.m > 0) {  // the slot keeps a copy of every fetched miss
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      if (f.hrow[u] >= 0) {
+        T* vd = const_cast<T*>(R.vb) + col * S::EPL + (int64_t)f.rows[u] * D;
+        *reinterpret_cast<u32x4*>(vd) = f.vr[u];
+        if (!kdev) {
+          T* kd = const_cast<T*>(R.kb) + col * S::EPL + (int64_t)f.rows[u] * D;
+          *reinterpret_cast<u32x4*>(kd) = f.kr[u];
+        }
+      }
+    }
+  }
+  float qr[NQ][S::EPL];
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi)
+#pragma unroll
+    for (int e = 0; e < S::EPL; ++e) qr[qi][e] = qi < nq ? q[qi * D + col * S::EPL + e] : 0.f;
+
+  // Logits: the first query always, the others only when they attend.
+  float s[NQ * S::U];  // s[qi * U + u]
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi) {
+    if (qi >= nq) break;
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      float fk[S::EPL];
+      Unpack<T>::run(f.kr[u], fk);
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < S::EPL; ++e) a = fmaf(fk[e], qr[qi][e], a);
+      s[qi * S::U + u] = a;
+    }
+    group_allreduce<S::LPR, S::U>(s + qi * S::U);
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) s[qi * S::U + u] *= scale;
+  }
+  attn_softmax_merge<T, D, NQ>(s, f.rows, f.vr, lds, nq, cm, cl, od, tid);
+}
+
+// A chunk whose logits are already known (the layer step's own scores of
+// the selected keys): the V rows of its entries and their scores, fetched
+// in one round trip.
+template <typename T, int D, int NQ>
+struct AttnFetchS {
+  using S = AttnShape<T, D>;
+  int rows[S::U];
+  int hrow[S::U];
+  u32x4 vr[S::U];
+  float s[NQ * S::U];
+};
+
+// Entries c0 .. c0 + 127 below lim of one (b, h) whose K rows are not
+// needed: entry(j, r, c, o) gives the slot row r, the key c and the row o
+// of the previous step's slot holding a miss (else -1), as for attn_fetch.
+// Every lane loads the V row of each of its entries (slot, host for a miss,
+// or the previous slot) and the entry's scaled logit of each of the first
+// nq queries, srow[qi * sstride + c].  A skipped entry reads row 0 and
+// score 0 and is masked later.
+template <typename T, int D, int NQ, class Entry>
+__device__ __forceinline__ void attn_fetch_s(const AttnRows<T>& R, const float* __restrict__ srow,
+                                             int64_t sstride, int nq, int c0, int lim,
+                                             Entry entry, AttnFetchS<T, D, NQ>& f, int tid) {
+  using S = AttnShape<T, D>;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane % S::LPR;
+  const int rsub = lane / S::LPR;
+  const int e0 = c0 + wave * kWaveEntries;
+  const bool from_host = R.vhb != nullptr;
+  // Every entry is looked up first (an entry past lim looks up entry
+  // lim - 1 and is dropped), so that the lookups are in flight together.
+  int er[S::U], ec[S::U], eo[S::U];
+#pragma unroll
+  for (int u = 0; u < S::U; ++u) er[u] = ec[u] = eo[u] = -1;
+  if (lim > 0 && R.m > 0) {
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      const int j = e0 + u * S::RPI + rsub;
+      entry(j < lim ? j : lim - 1, er[u], ec[u], eo[u]);
+    }
+  }
+  int cc[S::U], orow[S::U];
+#pragma unroll
+  for (int u = 0; u < S::U; ++u) {
+    const int j = e0 + u * S::RPI + rsub;
+    int r = j < lim ? er[u] : -1;
+    const int c = ec[u];
+    if (r < 0 || r >= R.m) r = -1;
+    if (c < 0 || (int64_t)c >= R.n_max) r = -1;
+    const bool miss = from_host && r >= R.first_miss_row;
+    f.rows[u] = r;
+    f.hrow[u] = (r >= 0 && miss) ? c : -1;
+    cc[u] = r >= 0 ? c : 0;
+    orow[u] = (r >= 0 && miss && R.vob != nullptr && eo[u] >= 0 && eo[u] < R.m) ? eo[u] : -1;
+  }
+  const T* vb = R.vb + col * S::EPL;
+  const T* vhb = from_host ? R.vhb + col * S::EPL : vb;
+  const bool any = R.m > 0;
+#pragma unroll
+  for (int u = 0; u < S::U; ++u) {
+    u32x4 vv = u32x4{0u, 0u, 0u, 0u};
+    if (any) {
+      const bool h = f.hrow[u] >= 0;
+      const T* vsrc = h ? vhb + (int64_t)f.hrow[u] * D
+                        : vb + (int64_t)(f.rows[u] >= 0 ? f.rows[u] : 0) * D;
+      if (orow[u] >= 0) vsrc = R.vob + col * S::EPL + (int64_t)orow[u] * D;
+      vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vsrc));
+    }
+    f.vr[u] = vv;
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi)
+      f.s[qi * S::U + u] = qi < nq ? srow[qi * sstride + cc[u]] : 0.f;
+  }
+}
+
+// Second half of a chunk fetched by attn_fetch_s: a missed row is first
+// copied into its slot row, then attn_softmax_merge over the fetched
+// logits.  Every thread of the workgroup must call it.
+template <typename T, int D, int NQ>
+__device__ __forceinline__ void attn_finish_s(const AttnRows<T>& R, AttnFetchS<T, D, NQ>& f,
+                                              AttnLds<D, NQ>& lds, int nq, float (&cm)[NQ],
+                                              float (&cl)[NQ], float (&od)[NQ], int tid) {
+  using S = AttnShape<T, D>;
+  const int col = (tid & 63) % S::LPR;
+  if (R.vhb != nullptr && R.m > 0) {  // the slot keeps a copy of every fetched miss
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      if (f.hrow[u] >= 0) {
+        T* vd = const_cast<T*>(R.vb) + col * S::EPL + (int64_t)f.rows[u] * D;
+        *reinterpret_cast<u32x4*>(vd) = f.vr[u];
+      }
+    }
+  }
+  attn_softmax_merge<T, D, NQ>(f.s, f.rows, f.vr, lds, nq, cm, cl, od, tid);
 }
 
 // Entries c0 .. c0 + 127 (those < lim): attn_fetch (attn_fetch_kdev when

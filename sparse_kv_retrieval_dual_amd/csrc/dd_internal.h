@@ -26,6 +26,13 @@ inline int elem_bytes(int dtype) { return dtype == kF32 ? 4 : 2; }
 struct GatherJob;
 struct GatherRes;
 
+// Keys per group of the group maxima the scoring kernel can write, and the
+// stride between the maxima rows of [BH][Q][gstride] (16-byte aligned rows).
+constexpr int kMaxGroup = 16;
+inline int64_t max_group_stride(int64_t n_max) {
+  return ((n_max + kMaxGroup - 1) / kMaxGroup + 3) & ~int64_t(3);
+}
+
 // Scaled logits of Q queries against every key; rows past lens[b] become
 // -inf when fill_pad is set and are left untouched otherwise.  When pf is
 // set, pf_wgs extra workgroups (dispatched first) run that row gather
@@ -35,12 +42,16 @@ struct GatherRes;
 // the rows are chunk landmarks, 2^len_shift keys each, and request b has
 // ceil(lens[b] / 2^len_shift) of them.  pres (with pf): the prefetch of a
 // layer whose rows are kept across steps (see launch_gather_resident).
+// gmax (or null): [BH][Q][max_group_stride(n_max)] fp32 receives, for every
+// group g of kMaxGroup keys holding a key below the row's length, the
+// largest score of its keys below the length (groups past it are left as
+// they are).
 hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, int B, int H,
                         int Q, int D, int64_t n_max, int dtype, float scale, bool fill_pad,
                         float* scores, const GatherJob* pf, int pf_wgs, hipStream_t s,
                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
                         int64_t* zero3 = nullptr, int len_shift = 0,
-                        const GatherRes* pres = nullptr);
+                        const GatherRes* pres = nullptr, float* gmax = nullptr);
 
 // In-place softmax of each score row over its valid keys; 0 past lens[b].
 hipError_t launch_softmax_rows(float* scores, const int32_t* lens, int B, int H, int Q,
@@ -82,16 +93,22 @@ struct FusedAttn {
   unsigned long long* pf_host;
 };
 
+// Whether launch_topk takes its bound from group maxima for score rows of
+// n_max entries (longer than one tile); only then are they worth writing.
+bool topk_uses_maxima(int64_t n_max);
+
 // Top-k of each score row.  Plane j of slab bh is written at
 // (j == 0 ? out0 : out1) + bh * out_stride_bh.  attn (or null): the plane-0
 // rows also do the prediction bookkeeping against pred ([BH][k], or null
 // for no prediction) and then the fused attention.  len_shift > 0: the
 // scores are of chunk landmarks of 2^len_shift rows, ceil(lens[b] /
-// 2^len_shift) per request.
+// 2^len_shift) per request.  gmax (or null): the rows' group maxima as the
+// scoring kernel writes them; rows with enough groups then take their bound
+// from these and read only the groups that can hold a selected key.
 hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, int Q,
                        int64_t n_max, int k, int32_t* out0, int32_t* out1,
                        int64_t out_stride_bh, const int32_t* pred, const FusedAttn* attn,
-                       hipStream_t s, int len_shift = 0);
+                       hipStream_t s, int len_shift = 0, const float* gmax = nullptr);
 
 // Row gather from pinned host memory.  Entry j < cnt[bh] (m if cnt is null)
 // of slab bh copies the run of R = 2^run_shift host rows from row
@@ -123,6 +140,13 @@ hipError_t launch_attn(const float* q, int64_t q_stride_bh, const void* k_rows,
                        void* ws, hipStream_t s);
 
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+// A single-wave kernel that stalls its stream for about `us` microseconds
+// (a fixed number of sleeps; it always ends).
+hipError_t launch_delay(int us, hipStream_t s);
+
+// Streaming read of bytes (a multiple of 16) at src; sink: 64 device words.
+hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 
 // Chunk landmarks: out[bh][e] (fp32, D wide, ceil(n_max / 2^chunk_shift)
 // rows per slab) = the mean of keys[bh][i] over the rows i of chunk e below

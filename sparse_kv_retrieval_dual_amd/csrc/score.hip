@@ -11,6 +11,10 @@
 // lanes with a transposing butterfly that leaves exactly one finished score
 // per lane.
 //
+// Optionally each wave also writes the maximum score of every group of 16
+// consecutive keys, per query (the selection takes its bound from these
+// instead of reading the whole score row).
+//
 // Optionally the first few workgroups of the grid do not score: they gather
 // the layer's predicted K/V rows from host memory into its slot (the
 // prefetch), so that the host-link transfer overlaps the HBM-bound scan
@@ -42,6 +46,11 @@ struct ScoreShape {
   static constexpr int KPI = U * RPI;              // keys per wave iteration (= 64 / Q)
   static constexpr int TILE = kScoreWaves * kScoreIters * KPI;
   static_assert(U >= 1 && U * Q == LPR, "shape");
+  // Group maxima: a group of kMaxGroup keys is VPG consecutive vu values of
+  // every rsub; GPI groups per wave iteration.
+  static constexpr int VPG = kMaxGroup / RPI;
+  static constexpr int GPI = KPI / kMaxGroup;
+  static_assert(VPG >= 1 && VPG * RPI == kMaxGroup && GPI * kMaxGroup == KPI, "group shape");
 };
 
 template <typename T, int D, int Q>
@@ -49,7 +58,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void k_score(
     const float* __restrict__ q, const T* __restrict__ keys, const int32_t* __restrict__ lens,
     int BH, int H, int64_t n_max, int tiles, float scale, float* __restrict__ scores,
     int fill_pad, GatherJob pf, int pf_wgs, int64_t* __restrict__ zero3, int len_shift,
-    GatherRes pres) {
+    GatherRes pres, float* __restrict__ gmax, int64_t gstride) {
   using S = ScoreShape<T, D, Q>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -129,10 +138,23 @@ __global__ __launch_bounds__(kScoreWaves * 64) void k_score(
       }
     }
     Butterfly<S::LPR, S::U * Q>::run(acc, lane);
+    const float sc = acc[0] * scale;
     if (my_row < n) {
-      sb[vj * n_max + my_row] = acc[0] * scale;
+      sb[vj * n_max + my_row] = sc;
     } else if (fill_pad && my_row < n_max) {
       sb[vj * n_max + my_row] = -INFINITY;
+    }
+    if (gmax != nullptr) {
+      // Max over the lanes of one group: every rsub (lane bits from LPR up)
+      // and VPG consecutive vu (col bits from Q up); keys past n count as
+      // -inf.  Lane gi * VPG * Q + j then holds group gi of query j.
+      float m = my_row < n ? sc : -INFINITY;
+#pragma unroll
+      for (int b = S::LPR; b < 64; b <<= 1) m = fmaxf(m, __shfl_xor(m, b));
+#pragma unroll
+      for (int b = Q; b < Q * S::VPG; b <<= 1) m = fmaxf(m, __shfl_xor(m, b));
+      if (lane < S::LPR && vu % S::VPG == 0)
+        gmax[((int64_t)bh * Q + vj) * gstride + key0 / kMaxGroup + vu / S::VPG] = m;
     }
   }
 }
@@ -186,6 +208,8 @@ struct ScoreLaunch {
   int64_t* zero3;
   int len_shift;
   GatherRes pres;
+  float* gmax;
+  int64_t gstride;
 };
 
 template <typename T, int D, int Q>
@@ -203,12 +227,13 @@ hipError_t launch_score_t(const ScoreLaunch& a) {
     hipExtLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), lds,
                           a.s, a.ev_start, a.ev_stop, 0, a.q, static_cast<const T*>(a.keys),
                           a.lens, BH, a.H, a.n_max, (int)tiles, a.scale, a.scores,
-                          a.fill_pad ? 1 : 0, a.pf, a.pf_wgs, a.zero3, a.len_shift, a.pres);
+                          a.fill_pad ? 1 : 0, a.pf, a.pf_wgs, a.zero3, a.len_shift, a.pres,
+                          a.gmax, a.gstride);
   } else {
     hipLaunchKernelGGL((k_score<T, D, Q>), dim3((unsigned)grid), dim3(kScoreWaves * 64), lds, a.s,
                        a.q, static_cast<const T*>(a.keys), a.lens, BH, a.H, a.n_max, (int)tiles,
                        a.scale, a.scores, a.fill_pad ? 1 : 0, a.pf, a.pf_wgs, a.zero3,
-                       a.len_shift, a.pres);
+                       a.len_shift, a.pres, a.gmax, a.gstride);
   }
   return hipGetLastError();
 }
@@ -225,9 +250,10 @@ hipError_t launch_score(const float* q, const void* keys, const int32_t* lens, i
                         int Q, int D, int64_t n_max, int dtype, float scale, bool fill_pad,
                         float* scores, const GatherJob* pf, int pf_wgs, hipStream_t s,
                         hipEvent_t ev_start, hipEvent_t ev_stop, int64_t* zero3,
-                        int len_shift, const GatherRes* pres) {
+                        int len_shift, const GatherRes* pres, float* gmax) {
   ScoreLaunch a{q, keys, lens, B, H, n_max, scale, fill_pad, scores, GatherJob{}, 0, s,
-                ev_start, ev_stop, zero3, len_shift, GatherRes{}};
+                ev_start, ev_stop, zero3, len_shift, GatherRes{}, gmax,
+                max_group_stride(n_max)};
   if (pf != nullptr && pf->total > 0 && pf_wgs > 0) {
     // The prefetched K/V rows are the scored rows' size, or (fp32 landmarks
     // of bf16 rows) half of it.

@@ -39,6 +39,7 @@
 // reading each miss from host memory and storing it into its slot row.
 #include <algorithm>
 #include <climits>
+#include <mutex>
 
 #include "attn_body.h"
 #include "dd_device.h"
@@ -63,6 +64,7 @@ constexpr int kFilterMaxN = 1 << 17;     // longest row of the filter path
 constexpr int kMaxWords = kFilterMaxN / 32 / kNT;  // bitmap words per thread
 constexpr int kScr = 64;                 // scan buffers and broadcasts
 constexpr int kSegKeys = 32 * kNT;       // keys per radix-path emit segment
+constexpr int kAttrDevices = 64;         // devices whose launch attributes are kept
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -283,6 +285,9 @@ struct Sink {
   uint32_t* gfin = nullptr;
   int32_t* wpre = nullptr;
   int nwords = 0;
+  // Position in the caller's prediction of each s_pred entry when the list
+  // had to be sorted (nullptr: s_pred is the prediction as given).
+  const int32_t* s_ppos = nullptr;
 };
 
 // Emits, in ascending index order, the selected entries of this thread's
@@ -363,9 +368,10 @@ __device__ __forceinline__ int emit_words(uint32_t (&g)[MAXW], const uint32_t (&
   }
   // Each selected entry is looked up once: hits get their prediction row
   // now, misses are marked and get slot rows after the scan of miss counts.
-  // The selected entries and the prediction both ascend, so the lookup
-  // walks the prediction forward from lo; an entry is a hit only where the
-  // prediction holds it (a prediction out of order can only lose hits).
+  // The selected entries and the prediction list both ascend (the list was
+  // sorted by order_prediction if it had to be), so the lookup walks the
+  // list forward from lo; the first of equal entries, the lowest position
+  // in the prediction, gives the row.
   if (lo == kSearchStart) {
     bool any = false;
 #pragma unroll
@@ -391,7 +397,7 @@ __device__ __forceinline__ int emit_words(uint32_t (&g)[MAXW], const uint32_t (&
         sk.out[j] = c;
         sk.lcur[j] = c;
         if (hit >= 0) {
-          sk.lpos[j] = hit;
+          sk.lpos[j] = sk.s_ppos != nullptr ? sk.s_ppos[hit] : hit;
         } else {
           mm[w] |= 1u << b;
           ++my_miss;
@@ -512,6 +518,71 @@ __device__ __forceinline__ void store_prediction(const int32_t (&pv)[kPR], int k
     pf += (pv[r] >= 0 && (int64_t)pv[r] < n_max) ? 1 : 0;
     pn += pv[r] >= 0 ? 1 : 0;
   }
+}
+
+// Makes the stored prediction list s_pred (k entries) ascend as unsigned
+// values, so that hits can be found by walking or binary search and the
+// non-negative entries come first; returns the position in the prediction
+// of each list entry, or nullptr when the list already ascends (the layer
+// step's own speculated sets always do).  Otherwise the (value, position)
+// pairs are sorted in LDS (bitonic, sortbuf: 2 * kMaxK words), so that
+// among equal entries the lowest position comes first, which is the row the
+// prefetch filled first; s_ppos (kMaxK words, inside sortbuf) receives the
+// positions.  The caller's barrier after store_prediction must precede.
+__device__ __forceinline__ const int32_t* order_prediction(int32_t* s_pred, int k,
+                                                           uint32_t* sortbuf, int* flag) {
+  const int tid = threadIdx.x;
+  int unsorted = 0;
+  for (int p = tid + 1; p < k; p += kNT)
+    unsorted |= (uint32_t)s_pred[p - 1] > (uint32_t)s_pred[p] ? 1 : 0;
+  // Block-wide OR through one LDS word (the runtime's own barrier-OR would
+  // add static LDS beside the kernel's full dynamic allocation).
+  if (tid == 0) *flag = 0;
+  __syncthreads();
+  if (unsorted) *flag = 1;
+  __syncthreads();
+  const bool any = *flag != 0;
+  __syncthreads();  // every thread has read the flag before its word is reused
+  if (!any) return nullptr;
+  int n2 = 1;
+  while (n2 < k) n2 <<= 1;
+  uint64_t* a = reinterpret_cast<uint64_t*>(sortbuf);
+  for (int i = tid; i < n2; i += kNT)
+    a[i] = i < k ? ((uint64_t)(uint32_t)s_pred[i] << 32) | (uint32_t)i : ~0ull;
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int t = tid; t < (n2 >> 1); t += kNT) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const uint64_t x = a[lo], y = a[hi];
+        if ((x > y) == ((lo & size) == 0)) {
+          a[lo] = y;
+          a[hi] = x;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // Every entry to registers before the positions overwrite the buffer.
+  uint64_t mine[kPR];
+#pragma unroll
+  for (int r = 0; r < kPR; ++r) {
+    const int i = tid + kNT * r;
+    mine[r] = i < k ? a[i] : 0ull;
+  }
+  __syncthreads();
+  int32_t* s_ppos = reinterpret_cast<int32_t*>(sortbuf);
+#pragma unroll
+  for (int r = 0; r < kPR; ++r) {
+    const int i = tid + kNT * r;
+    if (i < k) {
+      s_pred[i] = (int32_t)(uint32_t)(mine[r] >> 32);
+      s_ppos[i] = (int32_t)(uint32_t)mine[r];
+    }
+  }
+  __syncthreads();
+  return s_ppos;
 }
 
 // Filter path, bookkeeping rows: sets the prediction's bit of every entry
@@ -812,7 +883,295 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
   return true;
 }
 
+// ---------------------------------------------------------------- maxima path
+
+// The filter path from the scoring kernel's group maxima (kMaxGroup keys per
+// group), for rows longer than one tile (launches with n_max > kTile; the
+// rows of a launch with n_max <= kTile are cached in LDS whole, which is one
+// memory round trip where this path makes two, maxima then candidates) of
+// up to kFilterMaxN keys with at least k groups.  The
+// bound B is the lowest key of the 11-bit digit bin holding the k-th largest
+// group maximum, so at least k keys reach it, and a group whose maximum is
+// below B holds no key that does: only the groups whose maximum reaches B
+// are read, and their keys >= B form the candidate list in ascending index
+// order.  T follows by radix selection over the candidates, and the
+// selection is emitted straight from the list.  The row itself is never
+// streamed whole.
+constexpr int kCapM = 4096;                               // candidates
+constexpr int kGM4 = kFilterMaxN / kMaxGroup / 4 / kNT;  // maxima float4s per thread (8)
+constexpr int kPM = 8;                                    // candidate float4s per thread and round
+
+// LDS of the maxima path: the candidate group list in the bitmap area of
+// region C, the candidate indices and keys past the bookkeeping arrays (a
+// cached row's layout) or in the candidate area (a longer row's); both are
+// free again once the selection is emitted.
+template <bool CACHED>
+struct LayM {
+  static constexpr int groups = Lay<CACHED>::c;
+  static constexpr int idx = CACHED ? Lay<true>::end : kLIdx;
+  static constexpr int key = idx + kCapM;
+};
+static_assert(LayM<true>::groups + kTile / kMaxGroup <= Lay<true>::pred, "group list (cached)");
+static_assert(LayM<true>::key + kCapM <= Lay<true>::words, "candidates (cached)");
+static_assert(LayM<false>::groups + kFilterMaxN / kMaxGroup <= Lay<false>::pred, "group list");
+static_assert(LayM<false>::key + kCapM <= Lay<false>::c, "candidates (long rows)");
+
+// Float4s of the maxima row each thread reads (consecutive ones).
+__device__ __forceinline__ int maxima_w4(int64_t gstride) {
+  const int64_t w = (gstride / 4 + kNT - 1) / kNT;
+  return w < kGM4 ? (int)w : kGM4;
+}
+
+// This thread's maxima: float4s t W4 .. t W4 + W4 - 1 of the row (clamped to
+// the row's storage; entries past the row's groups are masked later).
+__device__ __forceinline__ void load_maxima(const float* __restrict__ gm_row, int64_t gstride,
+                                            f32x4 (&gv)[kGM4]) {
+  const int W4 = maxima_w4(gstride);
+  const uint32_t last = (uint32_t)(gstride / 4) - 1u;
+  const uint32_t q0 = threadIdx.x * (uint32_t)W4;
+#pragma unroll
+  for (int w = 0; w < kGM4; ++w) {
+    uint32_t q = q0 + (uint32_t)w;
+    q = q < last ? q : last;
+    gv[w] = w < W4 ? *reinterpret_cast<const f32x4*>(gm_row + 4 * (size_t)q)
+                   : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  }
+}
+
+// First position of the list s[0, len) (ascending as unsigned values) whose
+// entry is >= c as an unsigned value.
+__device__ __forceinline__ int lower_bound_u32(const int32_t* s, int len, uint32_t c) {
+  int lo = 0, hi = len;
+#pragma unroll 1
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((uint32_t)s[mid] < c) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Returns false, having written nothing to the outputs, when the
+// prediction is not in ascending order (the bitmap path takes it) or more
+// than kCapM keys reach the bound; hist is then clear again.
+template <bool CACHED>
+__device__ __forceinline__ bool maxima_select(const float* __restrict__ row,
+                                              const f32x4 (&gv)[kGM4], int64_t gstride, int n,
+                                              int64_t n_max, int k, uint32_t* smem, Sink& sk,
+                                              bool book, const int32_t (&pv)[kPR], int& misses,
+                                              int& fetchable) {
+  using LM = LayM<CACHED>;
+  const int tid = threadIdx.x;
+  uint32_t* hist = smem + kLHist;
+  ScanBufs sb{reinterpret_cast<int*>(smem + kLScr), 0};
+  int* bcast = reinterpret_cast<int*>(smem + kLScr) + 4 * kNW;
+  int32_t* cg = reinterpret_cast<int32_t*>(smem + LM::groups);
+  int32_t* fidx = reinterpret_cast<int32_t*>(smem + LM::idx);
+  uint32_t* fkey = smem + LM::key;
+  int32_t* s_pred = reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred);
+  const int ng = (n + kMaxGroup - 1) / kMaxGroup;
+  const int W4 = maxima_w4(gstride);
+  const int g0 = tid * 4 * W4;  // this thread's first group
+  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0 && (n_max & 3) == 0;
+
+  int pf = 0, pn = 0;
+  if (book) store_prediction(pv, k, n_max, s_pred, pf, pn);
+
+  // The bound: the digit bin of the k-th largest group maximum.
+  uint32_t gk[4 * kGM4];
+  uint32_t gval = 0u;  // bit i: group g0 + i exists
+#pragma unroll
+  for (int w = 0; w < kGM4; ++w) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * w + e;
+      const bool ok = w < W4 && g0 + i < ng;
+      gk[i] = order_key(f4_at(gv[w], e));
+      gval |= ok ? (1u << i) : 0u;
+      if (ok) atomicAdd(&hist[gk[i] >> 21], 1u);
+    }
+  }
+  __syncthreads();  // histogram complete; the prediction list stored
+  int d0, above;
+  pick_bin(hist, k, sb, bcast, d0, above);
+  const uint32_t bkey = (uint32_t)d0 << 21;
+  const float fb = key_floor(bkey);
+  clear(hist, 4 * 256);  // the selection's histograms (ordered by the barriers below)
+
+  // Candidate groups, and whether the prediction ascends.
+  int unsorted = 0;
+  if (book)
+    for (int p = tid + 1; p < k; p += kNT)
+      unsorted |= (uint32_t)s_pred[p - 1] > (uint32_t)s_pred[p] ? 1 : 0;
+  uint32_t gsel = 0u;
+#pragma unroll
+  for (int i = 0; i < 4 * kGM4; ++i) gsel |= ((gval >> i) & 1u) && gk[i] >= bkey ? (1u << i) : 0u;
+  int goff, eu, G, tu;
+  block_scan_pair<kNW>(__popc(gsel), unsorted, sb, goff, eu, G, tu);
+  if (tu != 0) {
+    clear(hist, kBins);
+    return false;
+  }
+#pragma unroll 1
+  for (uint32_t x = gsel; x != 0u; x &= x - 1u) cg[goff++] = g0 + __ffs(x) - 1;
+  __syncthreads();  // group list complete
+
+  // Candidates: slot s of 4 G is float4 s & 3 of group cg[s >> 2]; each
+  // round covers kNT * kPM slots, kPM consecutive ones per thread, so the
+  // list comes out in ascending index order.
+  const int nslots = 4 * G;
+  const uint32_t nq = (uint32_t)(n + 3) >> 2;  // float4s holding an entry < n
+  int cnt = 0;
+#pragma unroll 1
+  for (int r0 = 0; r0 < nslots; r0 += kNT * kPM) {
+    const int s0 = r0 + tid * kPM;
+    f32x4 v[kPM];
+    int i0[kPM];
+#pragma unroll
+    for (int p = 0; p < kPM; ++p) {
+      const int sl = s0 + p;
+      const int gq = cg[sl < nslots ? sl >> 2 : 0];
+      i0[p] = gq * kMaxGroup + 4 * (sl & 3);
+      if (vec) {
+        uint32_t q = (uint32_t)i0[p] >> 2;
+        q = q < nq ? q : nq - 1u;
+        v[p] = *reinterpret_cast<const f32x4*>(row + 4 * (size_t)q);
+      } else {
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ie = i0[p] + e < n ? i0[p] + e : n - 1;
+          f[e] = row[ie];
+        }
+        v[p] = f32x4{f[0], f[1], f[2], f[3]};
+      }
+    }
+    uint32_t m[kPM];
+    int my = 0;
+#pragma unroll
+    for (int p = 0; p < kPM; ++p) {
+      m[p] = s0 + p < nslots ? passing(v[p], i0[p], n, fb) : 0u;
+      my += __popc(m[p]);
+    }
+    int tot;
+    int off = cnt + block_scan<kNW>(my, sb, tot);
+    if (cnt + tot > kCapM) {
+      clear(hist, kBins);
+      return false;
+    }
+#pragma unroll
+    for (int p = 0; p < kPM; ++p) {
+#pragma unroll 1
+      for (uint32_t x = m[p]; x != 0u; x &= x - 1u) {
+        const int c = __ffs(x) - 1;
+        fidx[off] = i0[p] + c;
+        fkey[off] = order_key(f4_at(v[p], c));
+        ++off;
+      }
+    }
+    cnt += tot;
+  }
+  __syncthreads();  // candidates complete
+
+  uint32_t thr;
+  int take_eq;
+  select_kth<kCapM>(fkey, cnt, k, hist, thr, take_eq);
+
+  // Emit: thread t owns candidates [t E, t E + E) of the ascending list.
+  constexpr int EM = kCapM / kNT;
+  const int E = (cnt + kNT - 1) / kNT;
+  const int c_beg = tid * E;
+  uint32_t xs[EM];
+  int cs_[EM];
+  int gtc = 0, eqc = 0;
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    if (e >= E) break;
+    const int i = c_beg + e;
+    xs[e] = i < cnt ? fkey[i] : 0u;
+    cs_[e] = i < cnt ? fidx[i] : -1;
+    gtc += (i < cnt && xs[e] > thr) ? 1 : 0;
+    eqc += (i < cnt && xs[e] == thr) ? 1 : 0;
+  }
+  // Selected: every key > T, and the first take_eq keys equal to T in
+  // index order (those need the count of equal keys in lower threads).
+  uint32_t selm = 0u;  // bit e: owned candidate e is selected
+  int take = 0;
+  if (take_eq != 0) {
+    int ex, ep, tx, tp;
+    block_scan_pair<kNW>(gtc | (eqc << 16), 0, sb, ex, ep, tx, tp);
+    take = take_eq - (ex >> 16);
+  }
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    if (e >= E) break;
+    const bool in = c_beg + e < cnt;
+    bool sel = in && xs[e] > thr;
+    if (in && xs[e] == thr && take > 0) {
+      sel = true;
+      --take;
+    }
+    selm |= sel ? (1u << e) : 0u;
+  }
+  // Bookkeeping: each selected entry is looked up in the ascending
+  // prediction list (binary search for the thread's first, then a walk).
+  uint32_t hitm = 0u;
+  int hpos[EM];
+  if (book) {
+    int lo = -1;
+#pragma unroll
+    for (int e = 0; e < EM; ++e) {
+      hpos[e] = -1;
+      if (e >= E) break;
+      if ((selm >> e) & 1u) {
+        const uint32_t c = (uint32_t)cs_[e];
+        if (lo < 0) lo = lower_bound_u32(s_pred, k, c);
+#pragma unroll 1
+        while (lo < k && (uint32_t)s_pred[lo] < c) ++lo;
+        if (lo < k && (uint32_t)s_pred[lo] == c) {
+          hitm |= 1u << e;
+          hpos[e] = lo;
+        }
+      }
+    }
+  }
+  const int my_sel = __popc(selm);
+  const int my_miss = my_sel - __popc(hitm);
+  int ex, ep, tx, tp;
+  block_scan_pair<kNW>(my_sel | (my_miss << 16), pf | (pn << 16), sb, ex, ep, tx, tp);
+  int j = ex & 0xFFFF;  // selected entries in lower threads
+  int mr = ex >> 16;
+  fetchable = tp & 0xFFFF;
+  misses = tx >> 16;
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    if (e >= E) break;
+    if ((selm >> e) & 1u) {
+      if (j < k) {
+        sk.out[j] = cs_[e];
+        if (book) {
+          sk.lcur[j] = cs_[e];
+          sk.lpos[j] = ((hitm >> e) & 1u) ? hpos[e] : k + mr;
+        }
+      }
+      mr += ((hitm >> e) & 1u) ? 0 : 1;
+      ++j;
+    }
+  }
+  return true;
+}
+
 // ----------------------------------------------------------------- radix path
+
+// Where order_prediction may sort (2 * kMaxK words) on the paths that keep
+// the prediction as a list: past the bookkeeping arrays of a cached row
+// (the attention's scratch later), the candidate lists of a longer row.
+template <bool CACHED>
+__device__ __forceinline__ uint32_t* sort_buffer(uint32_t* smem) {
+  return smem + (CACHED ? Lay<true>::end : kLIdx);
+}
+static_assert(Lay<true>::end + 2 * kMaxK <= Lay<true>::words, "prediction sort fits (cached)");
+static_assert(kLIdx + 2 * kMaxK <= Lay<false>::c, "prediction sort fits (long rows)");
 
 // Histogram over the row of digit (key >> shift) & dmask, for keys whose
 // bits under pmask equal prefix.
@@ -872,6 +1231,8 @@ __device__ __forceinline__ int radix_select(const float* __restrict__ row, int n
   int pf = 0, pn = 0;
   if (book) {
     store_prediction(pv, k, n_max, s_pred, pf, pn);
+    __syncthreads();
+    sk.s_ppos = order_prediction(s_pred, k, sort_buffer<CACHED>(smem), bcast);
     sk.s_pred = s_pred;
   }
   int out_run = 0, eq_run = 0, miss_run = 0;
@@ -922,7 +1283,7 @@ template <typename T, int D>
 __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, int ks,
                                                   int32_t len, const int32_t* lpos,
                                                   const int32_t* lcur, const int32_t* lold,
-                                                  float* scratch) {
+                                                  float* scratch, const float* srow) {
   constexpr int NQ = 2;
   const int nq = fa.out_spec != nullptr ? 2 : 1;
   AttnLds<D, NQ>& lds = *reinterpret_cast<AttnLds<D, NQ>*>(scratch);
@@ -964,11 +1325,16 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
   const int d = threadIdx.x;
   for (int ch = 0; ch < chunks; ++ch) {
     float cm[NQ], cl[NQ], od[NQ];
-    if (kdev && lold == nullptr)
+    if (srow != nullptr) {
+      AttnFetchS<T, D, NQ> f;
+      attn_fetch_s<T, D, NQ>(R, srow, n_rows, nq, ch * kAttnChunk, k, entry, f, threadIdx.x);
+      attn_finish_s<T, D, NQ>(R, f, lds, nq, cm, cl, od, threadIdx.x);
+    } else if (kdev && lold == nullptr) {
       attend_chunk_n<T, D, NQ, true>(qrow, R, ch * kAttnChunk, k, fa.scale, entry, lds, nq, cm, cl,
                                      od);
-    else
+    } else {
       attend_chunk_n<T, D, NQ>(qrow, R, ch * kAttnChunk, k, fa.scale, entry, lds, nq, cm, cl, od);
+    }
     if (d < D) {
       for (int qi = 0; qi < nq; ++qi) {
         if (chunks == 1) {
@@ -1035,15 +1401,21 @@ __device__ __forceinline__ int resident_bookkeeping(const FusedAttn& fa, int bh,
 }
 
 // scratch: LDS for the attention of both queries (kAttnScratchWords).
+// srow (or null): the score rows of (b, h) ([Q][n_rows]: the current query's,
+// then the speculated one's); with them the logits of the selected keys
+// are those scores, and only V rows are read.
 __device__ __forceinline__ void fused_attention(const FusedAttn& fa, int bh, int ks, int32_t len,
                                                 const int32_t* lpos, const int32_t* lcur,
-                                                const int32_t* lold, float* scratch) {
+                                                const int32_t* lold, float* scratch,
+                                                const float* srow) {
   if (fa.dtype == kBF16) {
-    if (fa.D == 128) fused_attention_t<uint16_t, 128>(fa, bh, ks, len, lpos, lcur, lold, scratch);
-    else fused_attention_t<uint16_t, 64>(fa, bh, ks, len, lpos, lcur, lold, scratch);
+    if (fa.D == 128)
+      fused_attention_t<uint16_t, 128>(fa, bh, ks, len, lpos, lcur, lold, scratch, srow);
+    else
+      fused_attention_t<uint16_t, 64>(fa, bh, ks, len, lpos, lcur, lold, scratch, srow);
   } else {
-    if (fa.D == 128) fused_attention_t<float, 128>(fa, bh, ks, len, lpos, lcur, lold, scratch);
-    else fused_attention_t<float, 64>(fa, bh, ks, len, lpos, lcur, lold, scratch);
+    if (fa.D == 128) fused_attention_t<float, 128>(fa, bh, ks, len, lpos, lcur, lold, scratch, srow);
+    else fused_attention_t<float, 64>(fa, bh, ks, len, lpos, lcur, lold, scratch, srow);
   }
 }
 
@@ -1051,7 +1423,8 @@ template <int G, bool CACHED>
 __global__ __launch_bounds__(kNT) void k_topk(
     const float* __restrict__ scores, const int32_t* __restrict__ lens, int H, int Q, int BH,
     int64_t n_max, int k, int32_t* __restrict__ out0, int32_t* __restrict__ out1,
-    int64_t out_stride, const int32_t* __restrict__ pred, FusedAttn fa, int len_shift) {
+    int64_t out_stride, const int32_t* __restrict__ pred, FusedAttn fa, int len_shift,
+    const float* __restrict__ gmax, int64_t gstride) {
   extern __shared__ uint32_t smem[];
   const int tid = threadIdx.x;
   int bh, j;
@@ -1061,16 +1434,22 @@ __global__ __launch_bounds__(kNT) void k_topk(
   // Bookkeeping and attention: the current-query rows, when attention is fused.
   const bool do_book = fa.q != nullptr && j == 0;
   const int32_t* pred_row = (do_book && pred != nullptr) ? pred + (int64_t)bh * k : nullptr;
-  Sink sk{((j == 0) ? out0 : out1) + (int64_t)bh * out_stride, nullptr, 0,
-          do_book ? reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred) + kMaxK : nullptr,
-          do_book ? reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred) + 2 * kMaxK : nullptr};
-  // A row that fits one tile is loaded now, before its length is known
-  // (over its whole storage), so that the loads overlap those of the length
-  // and the prediction.
+  Sink sk{};
+  sk.out = ((j == 0) ? out0 : out1) + (int64_t)bh * out_stride;
+  sk.lpos = do_book ? reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred) + kMaxK : nullptr;
+  sk.lcur = do_book ? reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred) + 2 * kMaxK : nullptr;
+  // The row's group maxima, when the scoring kernel wrote them, or else a
+  // row that fits one tile (over its whole storage), are loaded now, before
+  // the row's length is known, so that the loads overlap those of the
+  // length and the prediction.
+  const bool use_gm = gmax != nullptr;
+  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0 && (n_max & 3) == 0;
   f32x4 v0[CACHED ? kU : 1];
-  if constexpr (CACHED) {
-    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0 && (n_max & 3) == 0;
-    load_tile(row, (int)n_max, 0, vec, v0);
+  f32x4 gv[kGM4];
+  if (use_gm) {
+    load_maxima(gmax + rowid * gstride, gstride, gv);
+  } else {
+    if constexpr (CACHED) load_tile(row, (int)n_max, 0, vec, v0);
   }
   // The prediction row, loaded now and stored in LDS once it is needed.
   // The loops over a thread's entries stop at the first r with
@@ -1095,14 +1474,21 @@ __global__ __launch_bounds__(kNT) void k_topk(
     ScanBufs sb{reinterpret_cast<int*>(smem + kLScr), 0};
     int32_t* s_pred = reinterpret_cast<int32_t*>(smem + Lay<CACHED>::pred);
     int pf = 0, pn = 0;
-    if (do_book) store_prediction(pv, k, n_max, s_pred, pf, pn);
+    const int32_t* s_ppos = nullptr;
+    if (do_book) {
+      store_prediction(pv, k, n_max, s_pred, pf, pn);
+      __syncthreads();
+      s_ppos = order_prediction(s_pred, k, sort_buffer<CACHED>(smem),
+                                reinterpret_cast<int*>(smem + kLScr) + 4 * kNW);
+    }
     int e0, e1, t0, t1;
     block_scan_pair<kNW>(pf, pn, sb, e0, e1, t0, t1);
     fetchable = t0;
     for (int r0 = 0; r0 < k; r0 += kNT) {
       const int c = r0 + tid;
       const bool valid = c < n;
-      const int hit = (do_book && valid) ? find_in(s_pred, t1, c) : -1;
+      int hit = (do_book && valid) ? find_in(s_pred, t1, c) : -1;
+      if (hit >= 0 && s_ppos != nullptr) hit = s_ppos[hit];
       int mtot;
       const int mr = misses + block_scan<kNW>((do_book && valid && hit < 0) ? 1 : 0, sb, mtot);
       if (c < k) {
@@ -1116,9 +1502,16 @@ __global__ __launch_bounds__(kNT) void k_topk(
     }
   } else {
     bool done = false;
-    if (n <= kFilterMaxN)
+    if (use_gm && n <= kFilterMaxN && (n + kMaxGroup - 1) / kMaxGroup >= k)
+      done = maxima_select<CACHED>(row, gv, gstride, n, n_max, k, smem, sk, do_book, pv, misses,
+                                   fetchable);
+    if (!done && n <= kFilterMaxN) {
+      if constexpr (CACHED) {
+        if (use_gm) load_tile(row, (int)n_max, 0, vec, v0);
+      }
       done = filter_select<G, CACHED>(row, n, n_max, k, smem, sk, do_book, pv, v0, misses,
                                       fetchable);
+    }
     if (!done) {
       sk.s_pred = nullptr;
       misses = radix_select<CACHED>(row, n, n_max, k, smem, sk, do_book, pv, fetchable);
@@ -1155,8 +1548,14 @@ __global__ __launch_bounds__(kNT) void k_topk(
     }
     __syncthreads();  // lold complete
   }
+  // Each selected key's logit is already in the score rows when every key
+  // was scored (K rows from the scoring copy, one row per entry): the
+  // attention then reads only V rows.  Chunk landmarks' scores are not the
+  // keys' logits, and K rows from the host are attended from their bytes.
+  const bool from_scores = fa.k_dev != nullptr && fa.chunk_shift == 0 && Q == 2;
   fused_attention(fa, bh, k, len_b, sk.lpos, sk.lcur, lold,
-                  reinterpret_cast<float*>(smem + (CACHED ? Lay<true>::end : kLIdx)));
+                  reinterpret_cast<float*>(smem + (CACHED ? Lay<true>::end : kLIdx)),
+                  from_scores ? scores + (int64_t)bh * Q * n_max : nullptr);
 }
 
 template <bool CACHED>
@@ -1176,10 +1575,12 @@ TopkKernel<CACHED> pick_kernel(int g) {
 
 }  // namespace
 
+bool topk_uses_maxima(int64_t n_max) { return n_max > kTile; }
+
 hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, int Q,
                        int64_t n_max, int k, int32_t* out0, int32_t* out1,
                        int64_t out_stride_bh, const int32_t* pred, const FusedAttn* attn,
-                       hipStream_t s, int len_shift) {
+                       hipStream_t s, int len_shift, const float* gmax) {
   const int BH = B * H;
   if (BH == 0) return hipSuccess;
   const DeviceInfo& di = device_info();
@@ -1190,24 +1591,54 @@ hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, i
   // Groups per thread: at least 4k group maxima (8192 at most).
   int g = 1;
   while (g < 32 && kNT * g < 4 * k) g *= 2;
-  static bool attr_set[64] = {false};
-  if (di.device >= 0 && di.device < 64 && !attr_set[di.device]) {
-    for (int gg = 1; gg <= 32; gg *= 2) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(pick_kernel<true>(gg)),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, di.lds_per_block);
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(pick_kernel<false>(gg)),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, di.lds_per_block);
+  // Dynamic LDS beyond the runtime's default needs the kernels' opt-in
+  // attribute, set once per device (the first caller sets it while any
+  // others wait) to what the device leaves beside each kernel's static LDS;
+  // a failure is kept and returned by every later launch on that device.
+  // Without it a launch was seen to run with a smaller LDS allocation and
+  // no error.
+  static std::once_flag attr_once[kAttrDevices];
+  static hipError_t attr_err[kAttrDevices];
+  static size_t attr_room[kAttrDevices][2];  // dynamic bytes allowed: [cached]
+  if (di.device < 0 || di.device >= kAttrDevices) return hipErrorInvalidDevice;
+  std::call_once(attr_once[di.device], [&di]() {
+    hipError_t e = hipSuccess;
+    size_t room[2] = {(size_t)di.lds_per_block, (size_t)di.lds_per_block};
+    for (int gg = 1; gg <= 32 && e == hipSuccess; gg *= 2) {
+      for (int c = 0; c < 2 && e == hipSuccess; ++c) {
+        const void* fn = c ? reinterpret_cast<const void*>(pick_kernel<true>(gg))
+                           : reinterpret_cast<const void*>(pick_kernel<false>(gg));
+        hipFuncAttributes fa{};
+        e = hipFuncGetAttributes(&fa, fn);
+        if (e != hipSuccess) break;
+        if (fa.sharedSizeBytes >= (size_t)di.lds_per_block) {
+          e = hipErrorInvalidConfiguration;
+          break;
+        }
+        const size_t r = (size_t)di.lds_per_block - fa.sharedSizeBytes;
+        if (r < room[c]) room[c] = r;
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)r);
+      }
     }
-    attr_set[di.device] = true;
-  }
+    attr_err[di.device] = e;
+    attr_room[di.device][0] = room[0];
+    attr_room[di.device][1] = room[1];
+  });
+  if (attr_err[di.device] != hipSuccess) return attr_err[di.device];
+  if (shmem > attr_room[di.device][cached ? 1 : 0]) return hipErrorInvalidConfiguration;
   FusedAttn fa{};
   if (attn != nullptr) fa = *attn;
+  // Group maxima rows must be 16-byte aligned for their vector loads.
+  if (gmax != nullptr && (reinterpret_cast<uintptr_t>(gmax) & 15u) != 0) return hipErrorInvalidValue;
+  const int64_t gstride = max_group_stride(n_max);
   if (cached) {
     hipLaunchKernelGGL(pick_kernel<true>(g), dim3(BH * Q), dim3(kNT), shmem, s, scores, lens, H, Q,
-                       BH, n_max, k, out0, out1, out_stride_bh, pred, fa, len_shift);
+                       BH, n_max, k, out0, out1, out_stride_bh, pred, fa, len_shift, gmax,
+                       gstride);
   } else {
     hipLaunchKernelGGL(pick_kernel<false>(g), dim3(BH * Q), dim3(kNT), shmem, s, scores, lens, H,
-                       Q, BH, n_max, k, out0, out1, out_stride_bh, pred, fa, len_shift);
+                       Q, BH, n_max, k, out0, out1, out_stride_bh, pred, fa, len_shift, gmax,
+                       gstride);
   }
   return hipGetLastError();
 }

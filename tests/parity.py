@@ -12,6 +12,8 @@ Tolerances:
 from __future__ import annotations
 
 import math
+import os
+import threading
 
 import numpy as np
 
@@ -19,6 +21,29 @@ TIE_REL_GAP = 1e-3
 TIE_LOGIT_GAP = math.log1p(TIE_REL_GAP)
 SCORE_RTOL = 1e-3
 ATTN_RTOL = 1e-2
+
+# Regression bounds, separate from the contract above: what fp32 accumulation
+# actually reaches, with a margin.  A logit is a D-term fp32 dot product:
+# its error is a few units of 2^-24 times sum_d |q_d K_d| (at most about
+# 10 max|s| for the workloads' planted keys), about 1e-6 of max|s|.  An
+# attention output moves by about the absolute error of the logits (each
+# weight exp(s_i - m) changes by that factor) plus the fp32 sums over at most
+# 128 entries per chunk and 32 chunk merges: a few 1e-6 of max|o|, 3e-6
+# measured.  1e-5 (logits) and 1e-4 (attention) leave a 10x margin and still
+# catch a path that loses precision, such as bf16 accumulation (about 4e-3).
+SCORE_REGRESSION_RTOL = 1e-5
+ATTN_REGRESSION_RTOL = 1e-4
+
+# Worst achieved relative errors, per test (printed at the end of the run).
+ACHIEVED: dict = {}
+_ACHIEVED_LOCK = threading.Lock()
+
+
+def _record(kind: str, value: float):
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    key = (test, kind)
+    with _ACHIEVED_LOCK:
+        ACHIEVED[key] = max(ACHIEVED.get(key, 0.0), float(value))
 
 
 def check_index_sets(gpu: np.ndarray, ref: np.ndarray, logits: np.ndarray,
@@ -56,7 +81,8 @@ def check_index_sets(gpu: np.ndarray, ref: np.ndarray, logits: np.ndarray,
 
 
 def check_logits(gpu: np.ndarray, ref: np.ndarray, lens: np.ndarray, pad_value=-np.inf):
-    """gpu fp32, ref fp64, both [rows][n_max]."""
+    """gpu fp32, ref fp64, both [rows][n_max].  Returns the worst relative error."""
+    worst = 0.0
     for r in range(gpu.shape[0]):
         n = int(lens[r])
         g = gpu[r, :n].astype(np.float64)
@@ -65,12 +91,18 @@ def check_logits(gpu: np.ndarray, ref: np.ndarray, lens: np.ndarray, pad_value=-
             scale = max(np.max(np.abs(o)), 1e-30)
             err = np.max(np.abs(g - o))
             assert err <= SCORE_RTOL * scale, f"row {r}: logit error {err} > {SCORE_RTOL} * {scale}"
+            assert err <= SCORE_REGRESSION_RTOL * scale, (
+                f"row {r}: logit error {err / scale:.3e} of max|s| is within the contract but "
+                f"above the fp32 regression bound {SCORE_REGRESSION_RTOL}")
+            worst = max(worst, err / scale)
         if pad_value is not None and n < gpu.shape[1]:
             tail = gpu[r, n:]
             if np.isneginf(pad_value):
                 assert np.all(np.isneginf(tail)), f"row {r}: padding is not -inf"
             else:
                 assert np.all(tail == pad_value), f"row {r}: padding is not {pad_value}"
+    _record("logits", worst)
+    return worst
 
 
 def exchange_slack(logits_row: np.ndarray, ref_sel: np.ndarray, v_rows: np.ndarray,
@@ -102,14 +134,26 @@ def exchange_slack(logits_row: np.ndarray, ref_sel: np.ndarray, v_rows: np.ndarr
 
 
 def check_attention(gpu: np.ndarray, ref: np.ndarray, slack: np.ndarray | None = None,
-                    rtol: float = ATTN_RTOL):
-    """gpu fp32 [rows][D], ref fp64 [rows][D]; slack per row (or None)."""
+                    rtol: float = ATTN_RTOL, regression: float | None = ATTN_REGRESSION_RTOL):
+    """gpu fp32 [rows][D], ref fp64 [rows][D]; slack per row (or None).
+
+    Every row must meet the contract (rtol, plus its exchange slack); rows
+    whose sets match the oracle's (no slack) must also meet the fp32
+    regression bound.  Returns the worst relative error of those rows.
+    """
     worst = 0.0
     for r in range(gpu.shape[0]):
         o = ref[r]
         scale = max(np.abs(o).max(), 1e-30)
         err = np.abs(gpu[r].astype(np.float64) - o).max()
-        tol = rtol * scale + (0.0 if slack is None else float(slack[r]))
+        sl = 0.0 if slack is None else float(slack[r])
+        tol = rtol * scale + sl
         assert err <= tol, f"row {r}: attention error {err} > {tol}"
-        worst = max(worst, err / scale)
+        if sl == 0.0:
+            if regression is not None:
+                assert err <= regression * scale, (
+                    f"row {r}: attention error {err / scale:.3e} of max|o| is within the "
+                    f"contract but above the fp32 regression bound {regression}")
+            worst = max(worst, err / scale)
+    _record("attention", worst)
     return worst
