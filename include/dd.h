@@ -208,6 +208,22 @@ DD_API int dd_sparse_attn(const float* q, int64_t q_stride_bh, const void* k_row
                           int H, int k, int m, int D, int dtype, float scale, float* out,
                           float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* dd_sparse_attn for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation and arguments, without ws / ws_bytes.  The chunk
+ * partials live in a 4 MiB scratch array inside the library, one per device
+ * the library runs on, kept until the process ends; no call allocates or
+ * frees anything.  Sizes whose partials exceed it (more than 4 MiB when
+ * B*H < 512 and k > 128: B*H * ceil(k / 128) * (D + 2) * 4 bytes) return
+ * DD_ERR_WORKSPACE with nothing enqueued.  The scratch needs no initial
+ * contents.  All calls on one device share it: calls whose executions
+ * overlap on one device (concurrent streams, host threads) race and must be
+ * ordered by the caller.  The output is bitwise that of dd_sparse_attn. */
+DD_API int dd_sparse_attn_noalloc(const float* q, int64_t q_stride_bh, const void* k_rows,
+                                  const void* v_rows, const int32_t* pos, const int32_t* cnt,
+                                  int B, int H, int k, int m, int D, int dtype, float scale,
+                                  float* out, float* lse, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Layer step: the layer-aware transfer schedule and the layer-scoped buffer */
 /* (arXiv page, section 1: predicted entries are fetched early enough to hide */

@@ -22,6 +22,7 @@ from .api import (  # noqa: F401
     ring_bytes,
     score,
     sparse_attn,
+    sparse_attn_noalloc,
     stream_copy,
     stream_read,
     topk,

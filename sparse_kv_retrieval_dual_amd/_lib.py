@@ -66,6 +66,8 @@ _SIGNATURES = {
     "dd_attn_workspace": (c_size_t, [c_int, c_int, c_int, c_int]),
     "dd_sparse_attn": (c_int, [P, c_int64, P, P, P, P, c_int, c_int, c_int, c_int, c_int, c_int,
                                c_float, P, P, P, c_size_t, P]),
+    "dd_sparse_attn_noalloc": (c_int, [P, c_int64, P, P, P, P, c_int, c_int, c_int, c_int, c_int,
+                                       c_int, c_float, P, P, P]),
     "dd_ctx_create": (c_int, [ctypes.POINTER(CtxConfig), ctypes.POINTER(c_void_p)]),
     "dd_ctx_destroy": (c_int, [P]),
     "dd_ring_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),

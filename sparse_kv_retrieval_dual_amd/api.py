@@ -247,6 +247,43 @@ def sparse_attn(q, k_rows, v_rows, pos=None, cnt=None, k: int | None = None, sca
     return out, lse
 
 
+def sparse_attn_noalloc(q, k_rows, v_rows, out, lse=None, pos=None, cnt=None,
+                        k: int | None = None, scale: float = 0.0, stream=None):
+    """dd_sparse_attn_noalloc: dd_sparse_attn with the library's own scratch.
+
+    The caller passes the outputs (out fp32 [B][H][D], lse fp32 [B][H] or
+    None); neither this wrapper nor the library allocates anything."""
+    _dev(q, "q"), _dev(k_rows, "k_rows"), _dev(v_rows, "v_rows"), _dev(out, "out")
+    _need(q.dtype == torch.float32, "q must be fp32")
+    B, H, m, D = k_rows.shape
+    _need(v_rows.shape == k_rows.shape and v_rows.dtype == k_rows.dtype, "k_rows/v_rows mismatch")
+    if q.dim() == 3:
+        _need(q.shape == (B, H, D), "q must be [B][H][D]")
+        q_stride = D
+    else:
+        _need(q.dim() == 4 and q.shape[0] == B and q.shape[1] == H and q.shape[3] == D,
+              "q must be [B][H][Q][D]")
+        q_stride = q.shape[2] * D
+    if pos is not None:
+        _dev(pos, "pos")
+        _need(pos.dtype == torch.int32 and pos.dim() == 3 and pos.shape[:2] == (B, H), "pos must be int32 [B][H][k]")
+        kk = pos.shape[2] if k is None else int(k)
+        _need(pos.shape[2] == kk, "pos must have k entries per (b, h)")
+    else:
+        kk = m if k is None else int(k)
+    if cnt is not None:
+        _dev(cnt, "cnt")
+        _need(cnt.dtype == torch.int32 and cnt.numel() == B * H, "cnt must be int32 [B][H]")
+    _need(out.shape == (B, H, D) and out.dtype == torch.float32, "out must be fp32 [B][H][D]")
+    if lse is not None:
+        _dev(lse, "lse")
+        _need(lse.shape == (B, H) and lse.dtype == torch.float32, "lse must be fp32 [B][H]")
+    L.check(_lib().dd_sparse_attn_noalloc(_p(q), q_stride, _p(k_rows), _p(v_rows), _p(pos),
+                                          _p(cnt), B, H, kk, m, D, kv_dtype(k_rows), float(scale),
+                                          _p(out), _p(lse), _stream(stream)))
+    return out, lse
+
+
 def stream_copy(src, dst, stream=None):
     """dd_stream_copy: device-to-device streaming copy of src's bytes into dst."""
     _dev(src, "src"), _dev(dst, "dst")

@@ -337,6 +337,37 @@ DD_API int dd_sparse_attn(const float* q, int64_t q_stride_bh, const void* k_row
   return DD_OK;
 }
 
+DD_API int dd_sparse_attn_noalloc(const float* q, int64_t q_stride_bh, const void* k_rows,
+                                  const void* v_rows, const int32_t* pos, const int32_t* cnt,
+                                  int B, int H, int k, int m, int D, int dtype, float scale,
+                                  float* out, float* lse, hipStream_t stream) {
+  int rc = check_shape(B, H, D, 0, dtype);
+  if (rc) return rc;
+  rc = check_k(k);
+  if (rc) return rc;
+  if (m < 0) return fail(DD_ERR_INVALID_ARG, "m must be >= 0 (got %d)", m);
+  if ((int64_t)B * H == 0) return DD_OK;
+  if (!q || !out || (m > 0 && (!k_rows || !v_rows)))
+    return fail(DD_ERR_INVALID_ARG, "null pointer argument");
+  if (q_stride_bh < D) return fail(DD_ERR_INVALID_ARG, "q_stride_bh must be >= D");
+  if (m > 0 && (!aligned16(k_rows) || !aligned16(v_rows)))
+    return fail(DD_ERR_INVALID_ARG, "row buffers must be 16-byte aligned");
+  const size_t need = dd::attn_workspace_used(B, H, k, D);
+  if (need > dd::kAttnScratchMaxBytes)
+    return fail(DD_ERR_WORKSPACE,
+                "dd_sparse_attn_noalloc: these sizes need %zu bytes of chunk partials, more than "
+                "the library's %zu-byte scratch (fewer chunks per (b, h), or B*H >= 512, fit; "
+                "dd_sparse_attn takes a workspace of any size)",
+                need, dd::kAttnScratchMaxBytes);
+  void* ws = nullptr;
+  if (need > 0) DD_CHECK_HIP(dd::attn_scratch(&ws), "scratch address");
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
+  hipError_t e = dd::launch_attn(q, q_stride_bh, k_rows, v_rows, pos, cnt, B, H, k, m, D, dtype,
+                                 sc, out, lse, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  return DD_OK;
+}
+
 DD_API size_t dd_ring_bytes(int ring_slots, int B, int H, int D, int k, int dtype) {
   if (ring_slots <= 0 || B <= 0 || H <= 0 || k <= 0) return 0;
   return (size_t)ring_slots * slot_bytes(B, H, D, k, dtype);

@@ -12,13 +12,27 @@
 // a small kernel merges them.  The merge is the same log-sum-exp over all
 // chunks in chunk order either way, so the result does not depend on the
 // split.
+#include <mutex>
+
 #include "attn_body.h"
 #include "dd_device.h"
 #include "dd_internal.h"
 
+// The chunk partials of dd_sparse_attn_noalloc: library memory, one copy on
+// every device the library runs on, held until the process ends.  In host
+// code this name is only a stand-in for the symbol: its device address on
+// each device comes from hipGetSymbolAddress (attn_scratch) and is what
+// kernels receive.
+static __device__ __align__(256) unsigned char scratch[dd::kAttnScratchMaxBytes];
+
 namespace dd {
 
 namespace {
+
+constexpr int kScratchDevices = 64;
+std::once_flag scratch_once[kScratchDevices];
+void* scratch_ptr[kScratchDevices];
+hipError_t scratch_err[kScratchDevices];
 
 constexpr int kAttnMaxChunks = 4096 / kAttnChunk;  // k <= 4096
 // (b, h) count from which each (b, h) gets a single workgroup (the chip is
@@ -153,6 +167,27 @@ size_t attn_workspace(int B, int H, int k, int D) {
   const int chunks = (k + kAttnChunk - 1) / kAttnChunk;
   if (chunks <= 1) return 0;
   return (size_t)B * H * chunks * (D + 2) * sizeof(float);
+}
+
+size_t attn_workspace_used(int B, int H, int k, int D) {
+  const int chunks = (k + kAttnChunk - 1) / kAttnChunk;
+  if (chunks <= 1 || (int64_t)B * H >= kAttnMinWgs) return 0;  // partials stay in LDS
+  return attn_workspace(B, H, k, D);
+}
+
+hipError_t attn_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  // Once per device, with that device current: the array's address there.
+  std::call_once(scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    scratch_ptr[dev] = scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *ptr = scratch_ptr[dev];
+  return scratch_err[dev];
 }
 
 hipError_t launch_attn(const float* q, int64_t q_stride_bh, const void* k_rows,

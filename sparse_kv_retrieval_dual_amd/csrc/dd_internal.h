@@ -133,6 +133,18 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 
 size_t attn_workspace(int B, int H, int k, int D);
 
+// Bytes of workspace launch_attn actually writes for these sizes (0 when
+// one chunk per (b, h), or when a workgroup per (b, h) keeps every chunk
+// partial in LDS).
+size_t attn_workspace_used(int B, int H, int k, int D);
+
+// Largest workspace the library's own attention scratch holds (4 MiB).
+constexpr size_t kAttnScratchMaxBytes = size_t(4) << 20;
+
+// The device address of the library's own attention scratch on the current
+// device (kAttnScratchMaxBytes, 256-byte aligned), looked up once per device.
+hipError_t attn_scratch(void** ptr);
+
 // Sparse attention over gathered rows (entry j is row pos[j], or j).
 hipError_t launch_attn(const float* q, int64_t q_stride_bh, const void* k_rows,
                        const void* v_rows, const int32_t* pos, const int32_t* cnt, int B, int H,
