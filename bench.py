@@ -157,7 +157,7 @@ def multi_layer(dd, w, lay, kh, vh, k_dev, lens, layers: int, h2d_gbps: float, d
     N = layers
     ctx = dd.Context(ring_slots=2, prefetch=prefetch, k_rows=k_rows)
     q = lay["q"]
-    lists = ([q] * N, [k_dev] * N, [kh] * N, [vh] * N)
+    lists = ([q] * N, [k_dev] * N, None if kh is None else [kh] * N, [vh] * N)
     res = ctx.layer_step(*lists, lens, w.k)
     pred = [s.clone() for s in res["spec"]]
     stats = torch.zeros(N, 3, dtype=torch.int64, device=dev)
@@ -269,12 +269,151 @@ def components(dd, gen, w, kh, vh, h2d_gbps: float, dev, reps: int = 6):
     }
 
 
+def stage_inputs(dd, gen, w, dev, copies: int, k_host: bool = True):
+    """One layer of the workload resident: keys in HBM (`copies` identical
+    copies to rotate over), V (and K unless k_host is False: a step that
+    reads K rows from HBM never reads the host K plane) in pinned host
+    memory.  K and V are drawn one request at a time straight into their
+    destinations, so a large workload never holds its whole V in HBM."""
+    import torch
+
+    kd = torch.empty(w.B, w.H, w.n_max, w.D, dtype=w.torch_dtype, device=dev)
+    vh = dd.host_empty(kd.shape, kd.dtype)
+    lay = gen.make_layer(w, 0, dev, k_out=kd, v_out=vh)
+    torch.cuda.synchronize()
+    kh = None
+    if k_host:
+        kh = dd.host_empty(kd.shape, kd.dtype)
+        kh.copy_(kd)
+    lay["k"] = kd
+    k_copies = [kd] + [kd.clone() for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    return lay, kh, vh, k_copies
+
+
+def one_workload(dd, gen, name: str, h2d_gbps: float, dev, steps: int = 6):
+    """One layer step of a workload at its full per-layer shape: eager
+    steps, each bracketed by events on the caller's stream (median), the
+    scoring kernel's own duration from events its dispatch records, and the
+    host-link bytes the step moved (prefetched and missed V rows) against
+    the measured pinned-copy rate.  Keys rotate over two HBM copies when
+    they fit the 256 MB Infinity Cache twice over, else one copy."""
+    import gc
+
+    import numpy as np
+    import torch
+    from sparse_kv_retrieval_dual_amd.hipevents import EventSet
+
+    w = gen.workload(name)
+    key_bytes = w.B * w.H * w.n_max * w.D * w.elem_bytes
+    copies = 4 if key_bytes <= (64 << 20) else (2 if key_bytes <= (1 << 30) else 1)
+    t0 = time.time()
+    lay, kh, vh, k_copies = stage_inputs(dd, gen, w, dev, copies, k_host=False)
+    lens = lay["lens"]
+    t_stage = time.time() - t0
+    ctx = dd.Context(ring_slots=2)
+    q = lay["q"]
+    res = ctx.layer_step([q], [k_copies[0]], None, [vh], lens, w.k)
+    pred = [s_.clone() for s_ in res["spec"]]
+    stats = torch.zeros(1, 3, dtype=torch.int64, device=dev)
+    E = dd.DD_STAGE_EVENTS
+    ev = EventSet(2 * (steps + 2))
+    tev = EventSet(E * (steps + 2))
+    for i in range(steps + 2):
+        ev.record(2 * i)
+        t = [None] * E
+        t[0], t[1] = tev.handles[E * i], tev.handles[E * i + 1]
+        ctx.layer_step([q], [k_copies[i % len(k_copies)]], None, [vh], lens, w.k, pred=pred,
+                       cur=res["cur"], spec=res["spec"], out=res["out"], lse=res["lse"],
+                       stats=stats, timing=t)
+        ev.record(2 * i + 1)
+    torch.cuda.synchronize()
+    step_us = float(np.median([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(2, steps + 2)])) * 1e3
+    score_us = float(np.median([tev.elapsed_ms(E * i, E * i + 1) for i in range(2, steps + 2)])) * 1e3
+    st = stats[0].cpu().tolist()
+    n_keys = int(lens.sum().item()) * w.H
+    score_bytes = n_keys * (w.D * w.elem_bytes + 8)
+    link_bytes = st[2] * w.D * w.elem_bytes
+    floor_us = link_bytes / (h2d_gbps * 1e9) * 1e6
+    ctx.close()
+    out = {"B": w.B, "H": w.H, "context": w.n_max, "top_k": w.k, "kv_dtype": w.dtype,
+           "ragged_lengths": w.len_lo != w.len_hi, "hbm_key_copies": len(k_copies),
+           "layer_step_us": step_us, "keys_per_s": n_keys / (step_us * 1e-6),
+           "score_us": score_us, "score_frac_of_hbm_peak":
+               score_bytes / (score_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+           "link_bytes": link_bytes, "link_floor_us": floor_us,
+           "frac_of_link_floor": floor_us / step_us,
+           "recall": st[1] / max(st[0] + st[1], 1), "misses": st[0],
+           "timing": "eager, events around each step, median", "inputs_staged_s": t_stage}
+    del lay, kh, vh, k_copies, res, pred, stats
+    gc.collect()
+    torch.cuda.empty_cache()
+    return out
+
+
+def gather_worked_example(dd, w, kh, vh, lens, h2d_gbps: float, dev, reps: int = 21):
+    """dd_gather of exactly the transfer the worked example sizes: k = 128
+    rows of K and V per head, 32 heads, bf16, head dim 128 = 2,097,152 B,
+    from this workload's pinned host cache into HBM.  Each call is timed
+    alone (events around it on the caller's stream; median)."""
+    import numpy as np
+    import torch
+    from sparse_kv_retrieval_dual_amd.hipevents import EventSet
+
+    B, H, D, m = w.B, w.H, w.D, 128
+    g = torch.Generator().manual_seed(11)
+    n = int(lens.min().item())
+    idx = torch.stack([torch.randperm(n, generator=g)[:m].sort().values
+                       for _ in range(B * H)]).view(B, H, m).to(torch.int32).to(dev)
+    ko = torch.empty(B, H, m, D, dtype=w.torch_dtype, device=dev)
+    vo = torch.empty_like(ko)
+    nbytes = 2 * B * H * m * D * w.elem_bytes
+    ev = EventSet(2)
+    ts = []
+    for i in range(reps + 1):
+        ev.record(0)
+        dd.gather(kh, vh, idx, k_out=ko, v_out=vo)
+        ev.record(1)
+        torch.cuda.synchronize()
+        if i > 0:
+            ts.append(ev.elapsed_ms(0, 1))
+    t = float(np.median(ts))
+    return {"bytes": nbytes, "rows": 2 * B * H * m, "us": t * 1e3,
+            "GBps": nbytes / (t * 1e-3) / 1e9, "frac_of_h2d": nbytes / (t * 1e-3) / 1e9 / h2d_gbps,
+            "timing": "one call alone, events around it, median of %d" % reps}
+
+
+def hbm_read_rate(dd, dev, reps: int = 5):
+    """Achievable HBM read rate: dd_stream_read of 1 GiB (non-temporal
+    loads, as the scorer's), median GB/s."""
+    import numpy as np
+    import torch
+    from sparse_kv_retrieval_dual_amd.hipevents import EventSet
+
+    big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(256, dtype=torch.uint8, device=dev)
+    ev = EventSet(2)
+    dd.stream_read(big, sink)
+    rates = []
+    for _ in range(reps):
+        ev.record(0)
+        dd.stream_read(big, sink)
+        ev.record(1)
+        torch.cuda.synchronize()
+        rates.append(big.numel() / (ev.elapsed_ms(0, 1) * 1e-3) / 1e9)
+    del big
+    return float(np.median(rates))
+
+
 def cpu_baseline(w, lay, budget_s: float):
     """The oracle as it stands, on the same workload, on the host's cores: a
-    pool of threads (one per core available to this process, at most 16)
-    runs whole oracle layer steps of one (request, head) each, BLAS held to
+    pool of threads runs oracle layer steps of one (request, head) each --
+    its scoring, its full-sort top-k, its byte gather of the selected K and V
+    rows and its dense-then-masked attention, each timed -- with BLAS held to
     one thread per call; heads are independent, so the layer is the sum of
-    its heads.  Layers repeat until about budget_s seconds have passed."""
+    its heads.  Layers repeat until about budget_s seconds have passed.  The
+    pool has one thread per core this process may run on, at most 16 (the
+    host's share per GPU)."""
     import numpy as np
     import torch
     from concurrent.futures import ThreadPoolExecutor
@@ -299,15 +438,30 @@ def cpu_baseline(w, lay, budget_s: float):
     lens = lay["lens"][:nb].cpu().numpy()
     units = [(q[:, h:h + 1].copy(), k16[:, h:h + 1].copy(), v16[:, h:h + 1].copy())
              for h in range(w.H)]
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    threads = max(1, min(16, affinity))
 
     def run(u):
-        oracle.layer_step(u[0], u[1], u[1], u[2], lens, w.k, w.dtype)
+        qq, kk, vv = u
+        t = [time.perf_counter()]
+        s_ = oracle.scaled_logits(qq, kk, lens, w.dtype)
+        t.append(time.perf_counter())
+        sel = oracle.select_topk(s_, lens, w.k)
+        t.append(time.perf_counter())
+        cur = np.ascontiguousarray(sel[:, :, 0])
+        oracle.gather_rows(kk, cur)
+        oracle.gather_rows(vv, cur)
+        t.append(time.perf_counter())
+        oracle.masked_attention(qq[:, :, 0], kk, vv, lens, cur, w.dtype)
+        t.append(time.perf_counter())
+        return np.diff(t)
 
     reps, t0 = 0, time.perf_counter()
+    stage = np.zeros(4)
     with ThreadPoolExecutor(threads) as ex:
         while True:
-            list(ex.map(run, units))
+            for d in ex.map(run, units):
+                stage += d
             reps += 1
             el = time.perf_counter() - t0
             if el >= budget_s:
@@ -315,10 +469,16 @@ def cpu_baseline(w, lay, budget_s: float):
     if limiter is not None:
         limiter.unregister()
     keys = int(np.sum(lens)) * w.H * reps
+    names = ("score", "topk_full_sort", "gather", "masked_attention")
+    per_layer = {n: float(x) / reps * 1e3 for n, x in zip(names, stage)}
     return {"value": keys / el, "unit": "keys/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full oracle layer steps of {w.name} (B={nb} H={w.H} n={w.n_max} "
-                      f"k={w.k}; fp64 scoring, full sort, dense-masked attention), one "
-                      f"(request, head) per task on {threads} threads, in {el:.1f} s"}
+            "affinity_cores": affinity,
+            "layer_step_ms_wall": el / reps * 1e3,
+            "stage_thread_ms_per_layer": per_layer,
+            "sample": f"{reps} oracle layer steps of {w.name} (B={nb} H={w.H} n={w.n_max} "
+                      f"k={w.k}; fp64 scoring, full sort, byte gather of K and V, dense-masked "
+                      f"attention), one (request, head) per task on {threads} threads, in "
+                      f"{el:.1f} s; stage times are thread time summed over a layer's heads"}
 
 
 def main():
@@ -352,6 +512,11 @@ def main():
     ap.add_argument("--resident", action="store_true",
                     help="in the decode loop, also time it with each layer keeping its "
                          "selected rows across steps")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the one-layer steps of the other workloads and the "
+                         "multi-layer 7B step")
+    ap.add_argument("--workload-layers", type=int, default=32,
+                    help="layers of the multi-layer 7B step in the workloads section")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -402,8 +567,8 @@ def main():
     ring = torch.empty(dd.ring_bytes(args.ring, B, H, D, k, dd.kv_dtype(lay["k"])), dtype=torch.uint8, device=dev)
     ws = torch.empty(dd.layer_step_workspace_bytes(B, H, D, w.n_max, k), dtype=torch.uint8, device=dev)
 
-    def step(i, pred, timing=None):
-        ctx.layer_step([q], [k_copies[i % len(k_copies)]], [kh], [vh], lens, k, pred=pred,
+    def step(i, pred, timing=None, c=None):
+        (c or ctx).layer_step([q], [k_copies[i % len(k_copies)]], [kh], [vh], lens, k, pred=pred,
                        cur=cur, spec=spec, out=out, lse=lse, stats=stats, ring=ring, ws=ws,
                        timing=timing, chunk=chunk if chunk > 1 else 0,
                        landmarks=[lm_copies[i % len(lm_copies)]] if chunk > 1 else None,
@@ -514,15 +679,39 @@ def main():
     # is fetched over the host link on the critical path (eager, events
     # around each step on the caller's stream).
     cold_ev = EventSet(2)
-    cold = []
+    cold_sc = EventSet(2)
+    cold, cold_score = [], []
     for i in range(max(3, min(K, 20))):
         cold_ev.record(0)
-        step(i, None)
+        t = [None] * E
+        t[0], t[1] = cold_sc.handles[0], cold_sc.handles[1]
+        step(i, None, timing=t)
         cold_ev.record(1)
         torch.cuda.synchronize()
         cold.append(cold_ev.elapsed_ms(0, 1) * 1e3)
+        cold_score.append(cold_sc.elapsed_ms(0, 1) * 1e3)
     step(0, pred)  # leaves the stats and outputs of a predicted step
     torch.cuda.synchronize()
+
+    # The prefetch alone: the prediction's V rows (and K rows with K from the
+    # host) gathered by a stand-alone dd_gather, each call timed alone.
+    pf_ev = EventSet(2)
+    pf_times = []
+    pf_v = torch.empty(B, H, ks * chunk, D, dtype=w.torch_dtype, device=dev)
+    pf_k = torch.empty_like(pf_v) if args.k_rows == "host" else None
+    for i in range(8):
+        pf_ev.record(0)
+        if chunk > 1:
+            dd.gather_chunks(kh if pf_k is not None else None, vh, pred[0], chunk,
+                             k_out=pf_k, v_out=pf_v)
+        else:
+            dd.gather(kh if pf_k is not None else None, vh, pred[0], k_out=pf_k, v_out=pf_v)
+        pf_ev.record(1)
+        torch.cuda.synchronize()
+        if i >= 2:
+            pf_times.append(pf_ev.elapsed_ms(0, 1) * 1e3)
+    del pf_v, pf_k
+    t_prefetch_alone = float(np.median(pf_times))
 
     # The landmark build (once per cache, not per step), over the same copies.
     lm_info = None
@@ -565,8 +754,59 @@ def main():
         h2d.append(big.numel() / (ev.elapsed_ms(0, 1) * 1e-3) / 1e9)
     h2d_gbps = float(np.median(h2d))
     del big, big2, hpin
+    hbm_read = hbm_read_rate(dd, dev)
+    worked = (gather_worked_example(dd, w, kh, vh, lens, h2d_gbps, dev)
+              if (B, H, D, w.dtype) == (1, 32, 128, "bf16") else None)
     comp = None if args.no_components else components(dd, gen, w, kh, vh, h2d_gbps, dev)
     _progress("reference rates and components done")
+
+    # The same step with K and V rows both gathered from the host copy (the
+    # pages' transfer: K rows of the selection cross the link too, and
+    # attention reads the gathered K rows), timed the same way as the
+    # headline when a graph is available, else eagerly.
+    host_kv = None
+    if args.k_rows == "device" and chunk == 1:
+        hctx = dd.Context(ring_slots=args.ring, gather_cus=args.gather_cus,
+                          prefetch_wgs=args.prefetch_wgs, prefetch=args.prefetch, k_rows="host")
+        step(0, pred, c=hctx)
+        torch.cuda.synchronize()
+        hstats0 = stats[0].cpu().tolist()
+        hev = EventSet(2)
+        h_note = "eager"
+        try:
+            hg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(hg):
+                for c_ in range(S):
+                    step(c_, pred, c=hctx)
+            hg.replay()
+            torch.cuda.synchronize()
+            hreps = max(1, K // S)
+            hev.record(0)
+            for i in range(hreps):
+                hg.replay()
+            hev.record(1)
+            torch.cuda.synchronize()
+            h_us = hev.elapsed_ms(0, 1) / (hreps * S) * 1e3
+            h_note = f"hip-graph replay, {S} steps per graph"
+            del hg
+        except Exception:  # noqa: BLE001
+            hts = []
+            for i in range(K):
+                hev.record(0)
+                step(i, pred, c=hctx)
+                hev.record(1)
+                torch.cuda.synchronize()
+                hts.append(hev.elapsed_ms(0, 1) * 1e3)
+            h_us = float(np.median(hts))
+        hlink = hstats0[2] * 2 * D * eb
+        host_kv = {"layer_step_us": h_us, "keys_per_s": n_keys / (h_us * 1e-6), "timing": h_note,
+                   "link_bytes": hlink,
+                   "link_floor_us": hlink / (h2d_gbps * 1e9) * 1e6,
+                   "note": "K and V rows of the prediction and the misses over the host link "
+                           "(the pages' transfer); attention reads the gathered K rows"}
+        hctx.close()
+        step(0, pred)
+        torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -612,15 +852,42 @@ def main():
                                "note": "eager, no prediction: every selected row over the "
                                        "host link on the critical path"},
         "score_keys_per_s": n_keys / (t_score * 1e-3),
-        "score_frac_of_measured_hbm_copy": score_gbps / hbm_copy,
-        "gather_GBps": prefetch_gbps,
-        "gather_frac_of_h2d": prefetch_gbps / h2d_gbps,
+        "score_frac_of_measured_hbm_read": score_gbps / hbm_read,
+        "hbm_stream_read_GBps": hbm_read,
+        "gather_GBps_lower_bound": prefetch_gbps,
+        "gather_frac_of_h2d_lower_bound": prefetch_gbps / h2d_gbps,
+        "gather_lower_bound_note": ("the step's prefetched bytes over the whole scoring kernel "
+                                    "it rides in (or its side-stream span): a lower bound on "
+                                    "the gather's rate; gather_worked_example and components "
+                                    "time the gather alone"),
+        "gather_worked_example": worked,
         "h2d_memcpy_GBps": h2d_gbps,
         "hbm_stream_copy_GBps": hbm_copy,
+        "hbm_stream_copy_note": "1 GiB read + 1 GiB written per copy, both counted",
         "prediction": {"misses": misses, "hits": hits, "rows_fetched": fetched,
                        "recall": hits / max(valid, 1), "miss_bytes": miss_bytes,
                        "unit": "keys" if chunk == 1 else f"chunks of {chunk} keys"},
     }
+    # Overlap: the stages measured alone (scoring without the prefetch, the
+    # prefetch gather alone, the top-k + bookkeeping + attention kernel of a
+    # predicted step) against the step, and the floors the step cannot beat.
+    t_score_alone = float(np.median(cold_score))
+    sum_stages = t_score_alone + t_prefetch_alone + t_select_attn * 1e3
+    hbm_floor = score_bytes / (HBM_PEAK_GBPS * 1e9) * 1e6
+    link_floor = (fetched * chunk * planes * D * eb) / (h2d_gbps * 1e9) * 1e6
+    step_us = ms_per_step * 1e3
+    result["overlap"] = {
+        "eta": (sum_stages - step_us) / max(sum_stages - max(hbm_floor, link_floor), 1e-9),
+        "definition": "(sum of stage times - step) / (sum of stage times - max(HBM floor, "
+                      "host-link floor))",
+        "sum_stages_us": sum_stages, "step_us": step_us,
+        "stages_alone_us": {"score_without_prefetch": t_score_alone,
+                            "prefetch_gather_alone": t_prefetch_alone,
+                            "select_bookkeeping_attention": t_select_attn * 1e3},
+        "hbm_floor_us": hbm_floor, "link_floor_us": link_floor,
+        "step_frac_of_floor": max(hbm_floor, link_floor) / step_us}
+    if host_kv is not None:
+        result["k_rows_host"] = host_kv
     if comp is not None:
         result["components"] = comp
     if lm_info is not None:
@@ -642,6 +909,43 @@ def main():
                 layers=args.layers, resident=True, h2d_gbps=h2d_gbps,
                 prefetch_wgs=args.prefetch_wgs, prefetch=args.prefetch)
     ctx.close()
+    if not args.no_workloads and w.name == "llama7b_32k_layer":
+        # Largest first, while the most host memory is free; a workload that
+        # cannot be staged or run is recorded with its error, not fatal.
+        import gc
+        del k_copies, kh, vh, lay, lm_copies, ring, ws, cur, spec, out, lse, out_spec, pred
+        graph = None
+        gc.collect()
+        torch.cuda.empty_cache()
+        if hasattr(torch._C, "_host_emptyCache"):
+            torch._C._host_emptyCache()  # the pinned buffer of the H2D reference
+        wl = {}
+        for name in ("hiconc_64", "llama13b_128k", "llama7b_32k_step", "tiny"):
+            try:
+                wl[name] = one_workload(dd, gen, name, h2d_gbps, dev)
+                _progress(f"workload {name}: {wl[name]['layer_step_us']:.1f} us per layer step")
+            except Exception as e:  # noqa: BLE001
+                wl[name] = {"error": f"{type(e).__name__}: {e}"}
+                _progress(f"workload {name}: {wl[name]['error']}")
+            gc.collect()
+            torch.cuda.empty_cache()
+        # The multi-layer step of the 7B decode workload: layer l+1's prefetch
+        # overlaps layer l (side stream), its layers sharing one layer's tensors.
+        try:
+            sw = gen.workload("llama7b_32k_step")
+            slay, skh, svh, sk = stage_inputs(dd, gen, sw, dev, 1, k_host=False)
+            ml = multi_layer(dd, sw, slay, skh, svh, sk[0], slay["lens"], args.workload_layers,
+                             h2d_gbps, dev, 3, "side", "device")
+            del slay, skh, svh, sk
+            _progress("multi-layer step done")
+        except Exception as e:  # noqa: BLE001
+            ml = {"error": f"{type(e).__name__}: {e}"}
+            _progress(f"multi-layer step: {ml['error']}")
+        if "error" not in wl["llama7b_32k_step"]:
+            wl["llama7b_32k_step"]["multi_layer"] = ml
+        else:
+            wl["llama7b_32k_step_multi_layer"] = ml
+        result["workloads"] = wl
     print(json.dumps(result))
 
 

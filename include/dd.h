@@ -300,7 +300,11 @@ typedef struct dd_layer_step_args {
   /* Host arrays of L pointers each: */
   const float* const* q;        /* device fp32 [B][H][2][D]: current, speculated */
   const void* const* k_dev;     /* device [B][H][n_max][D]: keys for scoring */
-  const void* const* k_host;    /* pinned host [B][H][n_max][D]: the full cache */
+  const void* const* k_host;    /* pinned host [B][H][n_max][D]: the full cache.
+                                   May be NULL (or hold NULL entries) when the
+                                   context reads K rows from k_dev
+                                   (DD_KROWS_DEVICE): the host K plane is then
+                                   never read, and only V needs pinned memory */
   const void* const* v_host;    /* pinned host [B][H][n_max][D] */
   const int32_t* const* pred;   /* NULL (no prediction) or device int32 [B][H][k]
                                    per layer (an entry may be NULL): the previous

@@ -364,7 +364,8 @@ class Context:
         """dd_layer_step over the layers given as lists (one tensor per layer).
 
         q[l] fp32 [B][H][2][D]; k_dev[l] device [B][H][n_max][D]; k_host[l], v_host[l]
-        pinned host tensors of the same shape; pred: None or a list whose entries are
+        pinned host tensors of the same shape (k_host may be None, or hold None entries,
+        when K rows come from k_dev: k_rows="device"); pred: None or a list whose entries are
         None or int32 [B][H][k].  Returns dict(cur, spec, out, lse, stats).
         chunk > 1: landmarks[l] fp32 [B][H][ceil(n_max/chunk)][D] are scored and
         pred / cur / spec hold k // chunk chunk indices per (b, h).
@@ -376,6 +377,9 @@ class Context:
         `timing` is None or a sequence of L * DD_STAGE_EVENTS raw hipEvent_t handles.
         """
         Lyr = len(q)
+        if k_host is None:
+            _need(self.k_rows == "device", "k_host is needed when K rows come from the host")
+            k_host = [None] * len(k_dev)
         _need(Lyr == len(k_dev) == len(k_host) == len(v_host), "per-layer lists differ in length")
         B, H, two, D = q[0].shape
         _need(two == 2, "q must hold two query planes")
@@ -390,7 +394,11 @@ class Context:
             _dev(q[l], "q"), _dev(k_dev[l], "k_dev")
             _need(q[l].shape == (B, H, 2, D) and q[l].dtype == torch.float32, "q shape")
             _need(k_dev[l].shape == (B, H, n_max, D) and kv_dtype(k_dev[l]) == dt, "k_dev shape")
+            _need(k_host[l] is not None or self.k_rows == "device",
+                  "k_host is needed when K rows come from the host")
             for t in (k_host[l], v_host[l]):
+                if t is None:
+                    continue
                 _need(not t.is_cuda and t.is_contiguous() and t.shape == (B, H, n_max, D)
                       and t.dtype == k_dev[l].dtype, "host K/V must be contiguous [B][H][n_max][D]")
             if pred is not None and pred[l] is not None:

@@ -466,14 +466,18 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
   if (rc) return rc;
   if (a->L < 0) return fail(DD_ERR_INVALID_ARG, "L must be >= 0");
   if (a->L == 0 || (int64_t)a->B * a->H == 0) return DD_OK;
-  if (!a->lens || !a->q || !a->k_dev || !a->k_host || !a->v_host || !a->cur_idx ||
-      !a->spec_idx || !a->out)
+  // With K rows read from the scoring copy the host K plane is never read,
+  // so it may be absent.
+  const bool k_from_dev = c->k_rows == DD_KROWS_DEVICE;
+  if (!a->lens || !a->q || !a->k_dev || (!a->k_host && !k_from_dev) || !a->v_host ||
+      !a->cur_idx || !a->spec_idx || !a->out)
     return fail(DD_ERR_INVALID_ARG, "null pointer argument");
   for (int l = 0; l < a->L; ++l) {
-    if (!a->q[l] || !a->k_dev[l] || !a->k_host[l] || !a->v_host[l] || !a->cur_idx[l] ||
+    const void* kh = a->k_host ? a->k_host[l] : nullptr;
+    if (!a->q[l] || !a->k_dev[l] || (!kh && !k_from_dev) || !a->v_host[l] || !a->cur_idx[l] ||
         !a->spec_idx[l] || !a->out[l])
       return fail(DD_ERR_INVALID_ARG, "null pointer for layer %d", l);
-    if (!aligned16(a->k_dev[l]) || !aligned16(a->k_host[l]) || !aligned16(a->v_host[l]))
+    if (!aligned16(a->k_dev[l]) || (kh && !aligned16(kh)) || !aligned16(a->v_host[l]))
       return fail(DD_ERR_INVALID_ARG, "K/V buffers of layer %d must be 16-byte aligned", l);
   }
   // Selection by chunk landmarks: ks chunks of 2^cs rows each, k rows in all.
@@ -590,7 +594,7 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     // With K rows read from the scoring copy, only V rows cross the host
     // link (the slot's K plane stays unused).
     const bool kdev = c->k_rows == DD_KROWS_DEVICE;
-    const void* khost = kdev ? nullptr : a->k_host[l];
+    const void* khost = kdev ? nullptr : a->k_host[l];  // present unless kdev
     const dd::GatherJob pf{static_cast<const uint8_t*>(khost),
                            static_cast<const uint8_t*>(a->v_host[l]), a->n_max, P, ks, nullptr,
                            (int64_t)BH * ks, reinterpret_cast<uint8_t*>(kslot),
@@ -642,7 +646,7 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     // right after its selection, reading misses from host memory itself
     // (and storing them into their slot rows k + t); K rows come from the
     // scoring copy when kdev.
-    const dd::FusedAttn fa{a->q[l], kslot, vslot, a->k_host[l], a->v_host[l],
+    const dd::FusedAttn fa{a->q[l], kslot, vslot, khost, a->v_host[l],
                            kdev ? a->k_dev[l] : nullptr, a->n_max, cs, D, a->dtype, sc,
                            a->out[l], a->lse ? a->lse[l] : nullptr, st,
                            a->out_spec ? a->out_spec[l] : nullptr,
