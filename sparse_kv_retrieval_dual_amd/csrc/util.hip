@@ -30,30 +30,27 @@ __global__ __launch_bounds__(256) void k_stream_copy(const u32x4* __restrict__ s
   for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
-// Grid-stride streaming read: every 16-byte word of src is loaded once
-// (non-temporal, as the scoring kernel reads its keys) and folded into a
-// per-lane xor; one word per wave goes to the 64-word sink, so the loads
-// cannot be dropped.  Waves share sink words: the values are meaningless.
+// Streaming read in the scoring kernel's shape: a one-shot grid whose
+// workgroups read 64 KB each, every lane with 16 non-temporal 16-byte loads
+// in flight (each load instruction of the workgroup covers 4 KB), folded
+// into a xor; one word per wave goes to the 64-word sink so that the loads
+// cannot be dropped (waves share sink words: the values are meaningless).
+constexpr int kReadUnroll = 16;
 __global__ __launch_bounds__(256) void k_stream_read(const u32x4* __restrict__ src, int64_t n16,
                                                      uint32_t* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * (256 * kReadUnroll) + threadIdx.x;
+  u32x4 v[kReadUnroll];
+#pragma unroll
+  for (int u = 0; u < kReadUnroll; ++u) {
+    const int64_t i = base + 256 * u;
+    v[u] = __builtin_nontemporal_load(src + (i < n16 ? i : n16 - 1));
+  }
   uint32_t acc = 0u;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = __builtin_nontemporal_load(src + i);
-    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-    acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^
-           (d.x ^ d.y ^ d.z ^ d.w);
-  }
-  for (; i < n16; i += stride) {
-    const u32x4 a = __builtin_nontemporal_load(src + i);
-    acc ^= a.x ^ a.y ^ a.z ^ a.w;
-  }
+#pragma unroll
+  for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
 #pragma unroll
   for (int b = 1; b < 64; b <<= 1) acc ^= (uint32_t)__shfl_xor((int)acc, b);
-  if ((threadIdx.x & 63) == 0) sink[(blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64) & 63u] = acc;
+  if ((threadIdx.x & 63) == 0) sink[(blockIdx.x * 4 + threadIdx.x / 64) & 63u] = acc;
 }
 
 // A fixed delay: one wave sleeps `rounds` times for the longest s_sleep
@@ -119,10 +116,8 @@ hipError_t launch_delay(int us, hipStream_t s) {
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s) {
   const int64_t n16 = (int64_t)(bytes / 16);
   if (n16 == 0) return hipSuccess;
-  const DeviceInfo& di = device_info();
-  int64_t grid = (n16 + 255) / 256;
-  const int64_t cap = (int64_t)(di.cus > 0 ? di.cus : 256) * 16;
-  if (grid > cap) grid = cap;
+  const int64_t grid = (n16 + 256 * kReadUnroll - 1) / (256 * kReadUnroll);
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_stream_read, dim3((unsigned)grid), dim3(256), 0, s,
                      static_cast<const u32x4*>(src), n16, static_cast<uint32_t*>(sink));
   return hipGetLastError();
