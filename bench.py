@@ -510,6 +510,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time the eager loop only")
     ap.add_argument("--prefetch-wgs", type=int, default=0)
     ap.add_argument("--prefetch", default="auto", choices=["auto", "side", "fused"])
+    ap.add_argument("--select-prefetch-slabs", type=int, default=0,
+                    help="slabs whose prefetch the selection kernel does (0: split by "
+                         "sizes, -1: none)")
     ap.add_argument("--k-rows", default="device", choices=["device", "host"],
                     help="where attention reads the selected K rows")
     ap.add_argument("--chunk", type=int, default=0,
@@ -567,7 +570,8 @@ def main():
     _progress(f"{w.name}: inputs resident ({n_keys} keys)")
 
     ctx = dd.Context(ring_slots=args.ring, gather_cus=args.gather_cus,
-                     prefetch_wgs=args.prefetch_wgs, prefetch=args.prefetch, k_rows=args.k_rows)
+                     prefetch_wgs=args.prefetch_wgs, prefetch=args.prefetch, k_rows=args.k_rows,
+                     select_prefetch_slabs=args.select_prefetch_slabs)
     chunk = args.chunk if args.chunk > 1 else 1
     ks = k // chunk                                      # entries selected per query
     # Landmarks are built once per cache (untimed here, measured below), one

@@ -34,7 +34,7 @@ P = c_void_p  # every pointer crosses as an address
 class CtxConfig(ctypes.Structure):
     _fields_ = [("ring_slots", c_int), ("gather_cus", c_int), ("prefetch_wgs", c_int),
                 ("prefetch_mode", c_int), ("k_rows", c_int), ("perturb_side_us", c_int),
-                ("perturb_main_us", c_int)]
+                ("perturb_main_us", c_int), ("select_prefetch_slabs", c_int)]
 
 
 class LayerStepArgs(ctypes.Structure):

@@ -330,13 +330,14 @@ class Context:
 
     def __init__(self, ring_slots: int = 2, gather_cus: int = 0, prefetch_wgs: int = 0,
                  prefetch: str = "auto", k_rows: str = "device", perturb_side_us: int = 0,
-                 perturb_main_us: int = 0):
+                 perturb_main_us: int = 0, select_prefetch_slabs: int = 0):
         lib = _lib()
         cfg = L.CtxConfig(ring_slots=int(ring_slots), gather_cus=int(gather_cus),
                           prefetch_wgs=int(prefetch_wgs),
                           prefetch_mode=self.PREFETCH_MODES[prefetch],
                           k_rows=self.K_ROWS[k_rows], perturb_side_us=int(perturb_side_us),
-                          perturb_main_us=int(perturb_main_us))
+                          perturb_main_us=int(perturb_main_us),
+                          select_prefetch_slabs=int(select_prefetch_slabs))
         h = ctypes.c_void_p()
         L.check(lib.dd_ctx_create(ctypes.byref(cfg), ctypes.byref(h)))
         self._h = h

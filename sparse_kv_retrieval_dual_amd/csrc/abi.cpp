@@ -24,6 +24,7 @@ struct dd_ctx {
   int k_rows = DD_KROWS_DEVICE;
   int perturb_side_us = 0;          // race detection: stalls before each side /
   int perturb_main_us = 0;          // main-stream stage of the layer step
+  int select_prefetch_slabs = 0;    // 0: split by sizes; > 0: that many; -1: none
   hipStream_t side = nullptr;       // prefetch gathers
   hipStream_t main_own = nullptr;   // CU-masked main stream (gather_cus > 0 only)
   hipEvent_t ev_start = nullptr;    // caller stream at entry
@@ -38,6 +39,13 @@ namespace {
 // 32) was the fastest of 1 to 8, on the side stream and inside the scoring
 // kernel alike, for a 4-layer decode step at batch 16, k = 1024 on MI355X.
 constexpr int kResidentWgsScale = 4;
+
+// Host-link bytes a layer's selection kernel hides before its attention
+// needs the prediction's rows: about 8 us at about 50 GB/s.
+constexpr int64_t kSelectWindowLinkBytes = int64_t(384) << 10;
+// Bytes the key scan streams from HBM while the host link moves one byte
+// of prefetch beside it.
+constexpr int64_t kScanBytesPerLinkByte = 100;
 
 // Workgroups of one layer's prefetch when the context leaves it open: 32 for
 // a small prefetch (1 MiB at batch 1, k = 128: 16 to 32 were equal, 8 too
@@ -397,6 +405,8 @@ DD_API int dd_ctx_create(const dd_ctx_config* cfg, dd_ctx** ctx) {
   if (cfg->perturb_side_us < 0 || cfg->perturb_main_us < 0 || cfg->perturb_side_us > 100000 ||
       cfg->perturb_main_us > 100000)
     return fail(DD_ERR_INVALID_ARG, "perturb_side_us / perturb_main_us must be in [0, 100000]");
+  if (cfg->select_prefetch_slabs < -1)
+    return fail(DD_ERR_INVALID_ARG, "select_prefetch_slabs must be >= -1");
   dd_ctx* c = new dd_ctx();
   c->ring_slots = cfg->ring_slots;
   c->gather_cus = cfg->gather_cus;
@@ -405,6 +415,7 @@ DD_API int dd_ctx_create(const dd_ctx_config* cfg, dd_ctx** ctx) {
   c->k_rows = cfg->k_rows;
   c->perturb_side_us = cfg->perturb_side_us;
   c->perturb_main_us = cfg->perturb_main_us;
+  c->select_prefetch_slabs = cfg->select_prefetch_slabs;
   hipError_t e = hipGetDevice(&c->device);
   const int cus = dd::device_info().cus;
   if (e == hipSuccess && c->gather_cus > 0) {
@@ -551,6 +562,26 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
   const bool fused = c->prefetch_mode == DD_PREFETCH_FUSED ||
                      (c->prefetch_mode == DD_PREFETCH_AUTO && (a->L == 1 || resident));
   const bool use_side = any_pred && !fused;
+  // Where a fused prefetch runs.  Inside the scoring kernel it overlaps the
+  // layer's key scan; the slabs whose transfer the scan cannot hide (HBM
+  // streams about kScanBytesPerLinkByte bytes while the host link moves
+  // one), up to what the link moves during a selection, are read instead by
+  // their own selection workgroups, overlapping the selection (V rows of
+  // kPrefetchRowBytes, at most kPrefetchMaxRows per slab, cached score rows).
+  int pf_sel_slabs = 0;
+  if (any_pred && fused && !resident && c->k_rows == DD_KROWS_DEVICE &&
+      D * dd::elem_bytes(a->dtype) == dd::kPrefetchRowBytes && k <= dd::kPrefetchMaxRows &&
+      n_sel <= dd::kPrefetchMaxScoreRow) {
+    const int64_t per_slab = (int64_t)k * dd::kPrefetchRowBytes;
+    const int64_t scan = (int64_t)BH * n_sel * D * (cs ? 4 : dd::elem_bytes(a->dtype));
+    const int64_t hidden = scan / (kScanBytesPerLinkByte * per_slab);
+    const int64_t window = kSelectWindowLinkBytes / per_slab;
+    if (c->select_prefetch_slabs > 0)
+      pf_sel_slabs = c->select_prefetch_slabs < BH ? c->select_prefetch_slabs : BH;
+    else if (c->select_prefetch_slabs == 0 && hidden < BH)
+      pf_sel_slabs = (int)(BH - hidden < window ? BH - hidden : window);
+  }
+  const int pf_score_slabs = BH - pf_sel_slabs;
 
   if (resident && a->reset) {  // both slots hold nothing; counters at zero
     for (int l = 0; l < a->L; ++l) {
@@ -597,10 +628,11 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     const void* khost = kdev ? nullptr : a->k_host[l];  // present unless kdev
     const dd::GatherJob pf{static_cast<const uint8_t*>(khost),
                            static_cast<const uint8_t*>(a->v_host[l]), a->n_max, P, ks, nullptr,
-                           (int64_t)BH * ks, reinterpret_cast<uint8_t*>(kslot),
+                           (int64_t)(fused ? pf_score_slabs : BH) * ks,
+                           reinterpret_cast<uint8_t*>(kslot),
                            reinterpret_cast<uint8_t*>(vslot), 2 * (int64_t)k, 0, cs, rowb};
     // Bytes the prefetch moves: V rows (and K rows from the host).
-    const int pf_wgs = prefetch_wgs_for(c, ((int64_t)BH * ks) << cs, rowb * (kdev ? 1 : 2),
+    const int pf_wgs = prefetch_wgs_for(c, pf.total << cs, rowb * (kdev ? 1 : 2),
                                         resident, fused);
 
     if (P && use_side) {
@@ -631,7 +663,7 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
     if (tev(l, 0) && !score_ev) DD_CHECK_HIP(hipEventRecord(tev(l, 0), ms), "timing");
     hipError_t e = dd::launch_score(a->q[l], cs ? static_cast<const void*>(a->landmarks[l]) : a->k_dev[l],
                                     a->lens, B, H, 2, D, n_sel, cs ? DD_F32 : a->dtype,
-                                    sc, false, scores, (P && fused) ? &pf : nullptr,
+                                    sc, false, scores, (P && fused && pf.total > 0) ? &pf : nullptr,
                                     pf_wgs, ms,
                                     score_ev ? tev(l, 0) : nullptr,
                                     score_ev ? tev(l, 1) : nullptr, st, cs,
@@ -651,7 +683,8 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
                            a->out[l], a->lse ? a->lse[l] : nullptr, st,
                            a->out_spec ? a->out_spec[l] : nullptr,
                            (a->out_spec && a->out_spec[l] && a->lse_spec) ? a->lse_spec[l] : nullptr,
-                           res.where, res.old_idx, res.new_idx, old_v, res.host_rows};
+                           res.where, res.old_idx, res.new_idx, old_v, res.host_rows,
+                           P ? pf_sel_slabs : 0};
     e = dd::launch_topk(scores, a->lens, B, H, 2, n_sel, ks, a->cur_idx[l], a->spec_idx[l], ks,
                         P, &fa, ms, cs, gmax);
     if (e != hipSuccess) return hip_fail(e, "top-k and attention kernel launch");

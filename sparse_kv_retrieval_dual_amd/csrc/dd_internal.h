@@ -91,7 +91,21 @@ struct FusedAttn {
   int32_t* new_idx;
   const void* old_vslot;
   unsigned long long* pf_host;
+  // The last pf_slabs slabs' prediction V rows were not prefetched before
+  // this kernel: each of their current-query workgroups reads its own from
+  // host memory during its selection (k << chunk_shift rows of
+  // kPrefetchRowBytes, at most kPrefetchMaxRows) and stores them into slot
+  // rows [0, k << chunk_shift) before its attention, as the prefetch gather
+  // would (zero rows for entries outside the cache).  0: none.
+  int pf_slabs;
 };
+
+// The prefetch a selection workgroup can do itself: rows of this size, at
+// most this many (one 16-byte load per thread for each 16 rows), for score
+// rows of at most kPrefetchMaxScoreRow entries (rows the kernel holds in LDS).
+constexpr int kPrefetchRowBytes = 256;
+constexpr int kPrefetchMaxRows = 128;
+constexpr int64_t kPrefetchMaxScoreRow = 32768;
 
 // Whether launch_topk takes its bound from group maxima for score rows of
 // n_max entries (longer than one tile); only then are they worth writing.

@@ -56,6 +56,7 @@ constexpr int kNW = kNT / 64;
 constexpr int kBins = 2048;              // 11-bit digits
 constexpr int kU = 32;                   // float4 per thread per tile
 constexpr int kTile = 4 * kNT * kU;      // 32768 keys
+static_assert(kTile == kPrefetchMaxScoreRow, "selection-side prefetch needs cached rows");
 constexpr int kMaxK = 4096;              // largest k (DD_MAX_K)
 constexpr int kPR = kMaxK / kNT;         // prediction entries per thread
 constexpr int kCapCached = 2560;         // candidates of a row cached in LDS
@@ -684,10 +685,11 @@ __device__ __forceinline__ uint32_t passing(const f32x4& v, int i, int n, float 
 // read again from global memory.  G groups of float4s per thread.  Returns
 // false, having written nothing, when more than the list's capacity of
 // keys pass the bound.
-template <int G, bool CACHED>
+template <int G, bool CACHED, typename AfterRow>
 __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int n, int64_t n_max, int k,
                               uint32_t* smem, Sink& sk, bool book, const int32_t (&pv)[kPR],
-                              const f32x4 (&v0)[CACHED ? kU : 1], int& misses, int& fetchable) {
+                              const f32x4 (&v0)[CACHED ? kU : 1], int& misses, int& fetchable,
+                              AfterRow&& after_row) {
   using L = Lay<CACHED>;
   constexpr int CAP = L::cap;
   constexpr int UPG = kU / G;  // float4s per group and tile
@@ -740,6 +742,7 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
     }
   }
   __syncthreads();  // also orders the caller's clear of hist
+  after_row();      // the caller's work once the row's registers are free
 
   // The bound: lowest key of the digit bin holding the k-th largest group
   // maximum (256 G >= k groups).
@@ -1419,7 +1422,7 @@ __device__ __forceinline__ void fused_attention(const FusedAttn& fa, int bh, int
   }
 }
 
-template <int G, bool CACHED>
+template <int G, bool CACHED, bool PF>
 __global__ __launch_bounds__(kNT) void k_topk(
     const float* __restrict__ scores, const int32_t* __restrict__ lens, int H, int Q, int BH,
     int64_t n_max, int k, int32_t* __restrict__ out0, int32_t* __restrict__ out1,
@@ -1442,6 +1445,26 @@ __global__ __launch_bounds__(kNT) void k_topk(
   // row that fits one tile (over its whole storage), are loaded now, before
   // the row's length is known, so that the loads overlap those of the
   // length and the prediction.
+  // The prediction's V rows, when this workgroup prefetches them itself (PF
+  // kernels, the last fa.pf_slabs slabs): row r of the slot (entry r >>
+  // chunk_shift, row r & mask of its chunk) is read from host memory, 16
+  // bytes per thread per 16 rows, and stored before the attention, so that
+  // the transfer overlaps the selection.  Loads complete in issue order, so
+  // the entries are loaded first and the rows only after the score row,
+  // the prediction and the length; and every workgroup of a PF kernel issues
+  // the same loads (one without rows to fetch reads its slab's slot rows
+  // and drops them), so that no join in the kernel has to wait for them.
+  constexpr int kPfU = kPrefetchMaxRows * kPrefetchRowBytes / 16 / kNT;
+  const bool pf_here = PF && do_book && pred_row != nullptr && bh >= BH - fa.pf_slabs;
+  const int pf_rows = k << fa.chunk_shift;
+  int pf_e[kPfU];
+  if constexpr (PF) {
+#pragma unroll
+    for (int u = 0; u < kPfU; ++u) {
+      const int r = min(tid / 16 + 16 * u, pf_rows - 1);
+      pf_e[u] = *(pf_here ? pred_row + (r >> fa.chunk_shift) : lens);
+    }
+  }
   const bool use_gm = gmax != nullptr;
   const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0 && (n_max & 3) == 0;
   f32x4 v0[CACHED ? kU : 1];
@@ -1468,7 +1491,32 @@ __global__ __launch_bounds__(kNT) void k_topk(
   const int32_t len_b = lens[bh / H];
   const int n = (int)chunk_len(len_b, len_shift, n_max);
   int misses = 0, fetchable = 0;
-
+  // The rows' loads, issued once the score row has left the registers (the
+  // filter path calls this after storing the row in LDS; any other path
+  // issues them before the attention).  Rows outside the cache, and rows
+  // past the prediction, read the slot row itself (the load is
+  // unconditional) and are replaced by zeros or not stored.
+  u32x4 pfv[kPfU];
+  bool pf_ok[kPfU];
+  bool pf_issued = false;
+  auto pf_issue = [&]() {
+    if constexpr (PF) {
+      const int cs = fa.chunk_shift;
+      const uint8_t* vh = static_cast<const uint8_t*>(fa.v_host) +
+                          (int64_t)bh * fa.n_rows * kPrefetchRowBytes + (tid % 16) * 16;
+      const uint8_t* vs = static_cast<const uint8_t*>(fa.vslot) +
+                          (int64_t)bh * 2 * pf_rows * kPrefetchRowBytes + (tid % 16) * 16;
+#pragma unroll
+      for (int u = 0; u < kPfU; ++u) {
+        const int r = min(tid / 16 + 16 * u, pf_rows - 1);
+        const int64_t hr = ((int64_t)pf_e[u] << cs) + (r & ((1 << cs) - 1));
+        pf_ok[u] = pf_here && pf_e[u] >= 0 && hr < fa.n_rows;
+        const uint8_t* src = pf_ok[u] ? vh + hr * kPrefetchRowBytes : vs + r * kPrefetchRowBytes;
+        pfv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+      }
+    }
+    pf_issued = true;
+  };
   if (n <= k) {
     // Every valid key is selected: entry c is c itself.
     ScanBufs sb{reinterpret_cast<int*>(smem + kLScr), 0};
@@ -1510,7 +1558,7 @@ __global__ __launch_bounds__(kNT) void k_topk(
         if (use_gm) load_tile(row, (int)n_max, 0, vec, v0);
       }
       done = filter_select<G, CACHED>(row, n, n_max, k, smem, sk, do_book, pv, v0, misses,
-                                      fetchable);
+                                      fetchable, pf_issue);
     }
     if (!done) {
       sk.s_pred = nullptr;
@@ -1519,6 +1567,23 @@ __global__ __launch_bounds__(kNT) void k_topk(
   }
 
   if (!do_book) return;
+  if constexpr (PF) {  // the prefetched rows into their slot rows (see above)
+    if (!pf_issued) pf_issue();
+    uint8_t* vs = static_cast<uint8_t*>(const_cast<void*>(fa.vslot)) +
+                  (int64_t)bh * 2 * pf_rows * kPrefetchRowBytes + (tid % 16) * 16;
+    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < kPfU; ++u) {
+      // An empty statement that takes the row as an operand: the first use
+      // of the loaded data stays here, so the compiler cannot move the
+      // zero select (and with it the wait for the host reads) up to the
+      // loads.
+      asm volatile("" : "+v"(pfv[u]));
+      const int r = tid / 16 + 16 * u;
+      if (pf_here && r < pf_rows)
+        *reinterpret_cast<u32x4*>(vs + r * kPrefetchRowBytes) = pf_ok[u] ? pfv[u] : zero;
+    }
+  }
   const int valid = n < k ? n : k;
   const bool resident = fa.where != nullptr;
   if (tid == 0 && fa.stats != nullptr) {
@@ -1558,20 +1623,23 @@ __global__ __launch_bounds__(kNT) void k_topk(
                   from_scores ? scores + (int64_t)bh * Q * n_max : nullptr);
 }
 
-template <bool CACHED>
-using TopkKernel = decltype(&k_topk<1, CACHED>);
+using TopkKernel = decltype(&k_topk<1, true, false>);
 
 template <bool CACHED>
-TopkKernel<CACHED> pick_kernel(int g) {
+TopkKernel pick_kernel(int g) {
   switch (g) {
-    case 1: return k_topk<1, CACHED>;
-    case 2: return k_topk<2, CACHED>;
-    case 4: return k_topk<4, CACHED>;
-    case 8: return k_topk<8, CACHED>;
-    case 16: return k_topk<16, CACHED>;
-    default: return k_topk<32, CACHED>;
+    case 1: return k_topk<1, CACHED, false>;
+    case 2: return k_topk<2, CACHED, false>;
+    case 4: return k_topk<4, CACHED, false>;
+    case 8: return k_topk<8, CACHED, false>;
+    case 16: return k_topk<16, CACHED, false>;
+    default: return k_topk<32, CACHED, false>;
   }
 }
+
+// The kernels with the selection-side prefetch: cached rows, k <= 128
+// entries (so g is 1 or 2).
+TopkKernel pick_pf_kernel(int g) { return g == 1 ? k_topk<1, true, true> : k_topk<2, true, true>; }
 
 }  // namespace
 
@@ -1605,9 +1673,11 @@ hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, i
     hipError_t e = hipSuccess;
     size_t room[2] = {(size_t)di.lds_per_block, (size_t)di.lds_per_block};
     for (int gg = 1; gg <= 32 && e == hipSuccess; gg *= 2) {
-      for (int c = 0; c < 2 && e == hipSuccess; ++c) {
-        const void* fn = c ? reinterpret_cast<const void*>(pick_kernel<true>(gg))
-                           : reinterpret_cast<const void*>(pick_kernel<false>(gg));
+      for (int c = 0; c < 3 && e == hipSuccess; ++c) {
+        if (c == 2 && gg > 2) break;
+        const void* fn = c == 2 ? reinterpret_cast<const void*>(pick_pf_kernel(gg))
+                         : c  ? reinterpret_cast<const void*>(pick_kernel<true>(gg))
+                              : reinterpret_cast<const void*>(pick_kernel<false>(gg));
         hipFuncAttributes fa{};
         e = hipFuncGetAttributes(&fa, fn);
         if (e != hipSuccess) break;
@@ -1616,7 +1686,7 @@ hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, i
           break;
         }
         const size_t r = (size_t)di.lds_per_block - fa.sharedSizeBytes;
-        if (r < room[c]) room[c] = r;
+        if (r < room[c ? 1 : 0]) room[c ? 1 : 0] = r;
         e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)r);
       }
     }
@@ -1631,7 +1701,20 @@ hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, i
   // Group maxima rows must be 16-byte aligned for their vector loads.
   if (gmax != nullptr && (reinterpret_cast<uintptr_t>(gmax) & 15u) != 0) return hipErrorInvalidValue;
   const int64_t gstride = max_group_stride(n_max);
-  if (cached) {
+  // A selection-side prefetch: V rows of kPrefetchRowBytes from host memory,
+  // at most kPrefetchMaxRows of them per slab, with a prediction to read.
+  const bool pf = fa.pf_slabs != 0;
+  if (pf && (fa.q == nullptr || fa.pf_slabs < 0 || fa.pf_slabs > BH || fa.v_host == nullptr ||
+             fa.vslot == nullptr || fa.D * elem_bytes(fa.dtype) != kPrefetchRowBytes ||
+             fa.chunk_shift < 0 || fa.chunk_shift > 7 ||
+             ((int64_t)k << fa.chunk_shift) > kPrefetchMaxRows || fa.where != nullptr ||
+             !cached || g > 2))
+    return hipErrorInvalidValue;
+  if (pf) {
+    hipLaunchKernelGGL(pick_pf_kernel(g), dim3(BH * Q), dim3(kNT), shmem, s, scores, lens, H, Q,
+                       BH, n_max, k, out0, out1, out_stride_bh, pred, fa, len_shift, gmax,
+                       gstride);
+  } else if (cached) {
     hipLaunchKernelGGL(pick_kernel<true>(g), dim3(BH * Q), dim3(kNT), shmem, s, scores, lens, H, Q,
                        BH, n_max, k, out0, out1, out_stride_bh, pred, fa, len_shift, gmax,
                        gstride);

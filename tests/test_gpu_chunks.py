@@ -255,3 +255,61 @@ def test_chunk_layer_step_full_size_7b():
     worst = parity.check_attention(got, want.reshape(B * H, w.D), np.zeros(B * H))
     ctx.close()
     print(f"worst relative attention error {worst:.2e}")
+
+
+@pytest.mark.parametrize("H,n_max,c,sel", [(8, 4096, 8, 0), (8, 4096, 8, 3), (6, 1000, 16, 0),
+                                           (32, 32768, 8, 0)])
+def test_selection_side_prefetch_matches_side_stream(H, n_max, c, sel):
+    """One layer with 256-byte V rows and k <= 128 rows: the prediction's rows
+    are fetched by the selection kernel for the last slabs (by the layer's
+    sizes: all slabs at the two small shapes, 12 of 32 at the full 7B shape;
+    or the last `sel`) and by the scoring kernel for the rest.  Outputs,
+    statistics and every slab's prefetched slot rows must equal those of a
+    side-stream prefetch bit for bit, and the slot rows must hold the host
+    rows of the prediction (zero rows for entries outside the cache, -1, and
+    rows past the last key)."""
+    dd = require_gpu()
+    w = gen.workload("llama7b_32k_layer").scaled(L=1, H=H, n_max=n_max)
+    announce(f"selection-side prefetch H={H} n_max={n_max} chunk={c} slabs={sel}")
+    data = _stage(dd, w, c)
+    B, ks, k = w.B, w.k // c, w.k
+    nc = -(-n_max // c)
+    eb = w.elem_bytes
+    nbytes = dd.ring_bytes(1, B, H, w.D, k, dd.kv_dtype(data[0]["k_dev"]))
+    ctx0 = dd.Context(ring_slots=1)
+    cold = _run(ctx0, w, data, c)
+    ctx0.close()
+    p = cold["spec"][0].cpu().numpy().copy()
+    rng = np.random.default_rng(5 + c)
+    for b in range(B):
+        for h in range(H):
+            p[b, h] = rng.permutation(p[b, h])
+    p[0, 0, 0] = -1
+    p[0, H - 1, 1] = nc + 3         # past the cache
+    p[B - 1, H // 2, 2] = nc - 1    # the last, partial chunk
+    pred = [torch.from_numpy(p).cuda()]
+    out = {}
+    for mode in ("fused", "side"):
+        ctx = dd.Context(ring_slots=1, prefetch=mode, select_prefetch_slabs=sel)
+        ring = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda")
+        out[mode] = (_run(ctx, w, data, c, pred=pred, ring=ring), ring.cpu().numpy())
+        ctx.close()
+    (fr, fring), (sr, sring) = out["fused"], out["side"]
+    for key in ("out", "lse", "cur", "spec", "stats"):
+        got, want = fr[key], sr[key]
+        if isinstance(got, list):
+            got, want = got[0], want[0]
+        assert torch.equal(got, want), key
+    vplane = lambda raw: raw[nbytes // 2:].reshape(B, H, 2 * k, w.D * eb)
+    fv, sv = vplane(fring), vplane(sring)
+    assert np.array_equal(fv[:, :, :k], sv[:, :, :k]), "prediction rows differ"
+    vh = stored(data[0]["v_host"]).view(np.uint8).reshape(B, H, n_max, w.D * eb)
+    zero = np.zeros(w.D * eb, np.uint8)
+    for b in range(B):
+        for h in range(H):
+            for j in range(ks):
+                e = int(p[b, h, j])
+                for i in range(c):
+                    r = e * c + i
+                    want = vh[b, h, r] if 0 <= e < nc and r < n_max else zero
+                    assert np.array_equal(fv[b, h, j * c + i], want), (b, h, j, i)
