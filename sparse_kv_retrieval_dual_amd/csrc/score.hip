@@ -104,6 +104,28 @@ __global__ __launch_bounds__(kScoreWaves * 64) void k_score(
   const int vj = col % Q;
   const int vu = col / Q;
 
+  // Both iterations' rows are loaded before either is scored, so that a
+  // lane keeps 2U loads in flight.  Rows past n load row n-1 instead (an
+  // iteration with no row below n loads nothing): the loads stay
+  // unconditional so all of them are in flight together, and the butterfly
+  // never mixes rows, so those lanes' scores are simply not stored.  The
+  // keys are read once: non-temporal loads keep them from evicting the
+  // scores (and prefetched rows) that the next kernels read from L2.
+  u32x4 raw_it[kScoreIters][S::U];
+#pragma unroll
+  for (int it = 0; it < kScoreIters; ++it) {
+    const int64_t key0 = tile0 + ((int64_t)it * kScoreWaves + wave) * S::KPI;
+    if (key0 < n) {
+#pragma unroll
+      for (int u = 0; u < S::U; ++u) {
+        const int64_t row = key0 + u * S::RPI + rsub;
+        const int64_t rr = row < n ? row : n - 1;
+        raw_it[it][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + rr * D));
+      }
+    }
+  }
+
+#pragma unroll
   for (int it = 0; it < kScoreIters; ++it) {
     const int64_t key0 = tile0 + ((int64_t)it * kScoreWaves + wave) * S::KPI;
     if (key0 >= n_max) break;
@@ -112,18 +134,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void k_score(
       if (fill_pad && my_row < n_max) sb[vj * n_max + my_row] = -INFINITY;
       continue;
     }
-    // Rows past n load row n-1 instead (n >= 1 here): the loads stay
-    // unconditional so all U of them are in flight together, and the
-    // butterfly never mixes rows, so those lanes' scores are simply not stored.
-    // The keys are read once: non-temporal loads keep them from evicting
-    // the scores (and prefetched rows) that the next kernels read from L2.
-    u32x4 raw[S::U];
-#pragma unroll
-    for (int u = 0; u < S::U; ++u) {
-      const int64_t row = key0 + u * S::RPI + rsub;
-      const int64_t rr = row < n ? row : n - 1;
-      raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + rr * D));
-    }
+    const u32x4 (&raw)[S::U] = raw_it[it];
     float acc[S::U * Q];
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
