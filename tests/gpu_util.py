@@ -10,7 +10,7 @@ import torch
 
 
 def require_gpu():
-    """Skips without a GPU; on a GPU machine a missing library is a failure."""
+    """Skips without a GPU; where a GPU is present a missing library is a failure."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import sparse_kv_retrieval_dual_amd as dd
