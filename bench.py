@@ -143,13 +143,15 @@ def decode_loop(dd, gen, w, lay, kh, vh, k_dev, lens, steps: int, chunk: int, de
 
 
 def multi_layer(dd, w, lay, kh, vh, k_dev, lens, layers: int, h2d_gbps: float, dev,
-                steps: int, prefetch: str, k_rows: str):
+                steps: int, prefetch: str, k_rows: str, chunk: int = 1, lm=None):
     """One decode step over `layers` layers of the workload's shape (the same
-    tensors serve every layer; each layer keeps its own prediction and
+    queries and host cache serve every layer, the keys and landmarks rotate
+    over the copies given; each layer keeps its own prediction and
     outputs): the multi-layer schedule, where layer l+1's prefetch overlaps
     layer l (on the side stream by default).  Eager steps, each bracketed by
     events on the caller's stream; the link floor is the host-link bytes the
-    step moved (prefetched and missed rows) at the measured pinned-copy rate."""
+    step moved (prefetched and missed rows) at the measured pinned-copy rate.
+    chunk > 1: selection by the chunk landmarks lm (the stats count chunks)."""
     import numpy as np
     import torch
     from sparse_kv_retrieval_dual_amd.hipevents import EventSet
@@ -157,8 +159,14 @@ def multi_layer(dd, w, lay, kh, vh, k_dev, lens, layers: int, h2d_gbps: float, d
     N = layers
     ctx = dd.Context(ring_slots=2, prefetch=prefetch, k_rows=k_rows)
     q = lay["q"]
-    lists = ([q] * N, [k_dev] * N, None if kh is None else [kh] * N, [vh] * N)
-    res = ctx.layer_step(*lists, lens, w.k)
+    # k_dev / lm: one tensor, or copies that the layers take in turn (so
+    # that a later layer's scan is not served by the Infinity Cache).
+    kd = k_dev if isinstance(k_dev, (list, tuple)) else [k_dev]
+    lms = lm if isinstance(lm, (list, tuple)) else [lm]
+    lists = ([q] * N, [kd[i % len(kd)] for i in range(N)], None if kh is None else [kh] * N,
+             [vh] * N)
+    ck = dict(chunk=chunk, landmarks=[lms[i % len(lms)] for i in range(N)]) if chunk > 1 else {}
+    res = ctx.layer_step(*lists, lens, w.k, **ck)
     pred = [s.clone() for s in res["spec"]]
     stats = torch.zeros(N, 3, dtype=torch.int64, device=dev)
     ev = EventSet(2)
@@ -166,19 +174,51 @@ def multi_layer(dd, w, lay, kh, vh, k_dev, lens, layers: int, h2d_gbps: float, d
     for i in range(steps + 2):
         ev.record(0)
         ctx.layer_step(*lists, lens, w.k, pred=pred, cur=res["cur"], spec=res["spec"],
-                       out=res["out"], lse=res["lse"], stats=stats)
+                       out=res["out"], lse=res["lse"], stats=stats, **ck)
         ev.record(1)
         torch.cuda.synchronize()
         if i >= 2:
             times.append(ev.elapsed_ms(0, 1) * 1e3)
+    # The same step replayed from a HIP graph (checked against the eager
+    # outputs on two replays first), as a decode loop would run it.
+    t_graph, graph_note = None, None
+    try:
+        ref = [o.clone() for o in res["out"]]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ctx.layer_step(*lists, lens, w.k, pred=pred, cur=res["cur"], spec=res["spec"],
+                           out=res["out"], lse=res["lse"], stats=stats, **ck)
+        for _ in range(2):
+            for o in res["out"]:
+                o.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(a, b) for a, b in zip(res["out"], ref)):
+                raise RuntimeError("graph replay differs from the eager step")
+        gt = []
+        for i in range(steps + 2):
+            ev.record(0)
+            g.replay()
+            ev.record(1)
+            torch.cuda.synchronize()
+            if i >= 2:
+                gt.append(ev.elapsed_ms(0, 1) * 1e3)
+        t_graph = float(np.median(gt))
+        del g
+    except Exception as e:  # noqa: BLE001
+        graph_note = f"graph replay unavailable: {e}"
     st = stats.cpu().numpy()
     ctx.close()
     t = float(np.median(times))
     planes = 1 if k_rows == "device" else 2
-    link_bytes = int(st[:, 2].sum()) * w.D * w.elem_bytes * planes
+    link_bytes = int(st[:, 2].sum()) * max(chunk, 1) * w.D * w.elem_bytes * planes
     floor_us = link_bytes / (h2d_gbps * 1e9) * 1e6
-    return {"layers": N, "prefetch": prefetch, "step_us_median": t, "per_layer_us": t / N,
+    return {"layers": N, "prefetch": prefetch, "chunk": max(chunk, 1), "step_us_median": t,
+            "per_layer_us": t / N,
             "timing": "eager, events around each whole step",
+            "graph_step_us_median": t_graph,
+            "graph_per_layer_us": None if t_graph is None else t_graph / N,
+            "graph_note": graph_note,
             "link_bytes_per_step": link_bytes, "link_floor_us": floor_us,
             "frac_of_link_floor": floor_us / t,
             "misses": int(st[:, 0].sum()), "hits": int(st[:, 1].sum()),
@@ -930,10 +970,10 @@ def main():
     if lm_info is not None:
         result["landmarks_build"] = lm_info
     if args.layers > 1:
-        result["multi_layer"] = multi_layer(dd, w, lay, kh, vh, k_copies[0], lens, args.layers,
+        result["multi_layer"] = multi_layer(dd, w, lay, kh, vh, k_copies, lens, args.layers,
                                             h2d_gbps, dev, max(3, min(args.steps, 10)),
                                             "auto" if args.prefetch == "auto" else args.prefetch,
-                                            args.k_rows)
+                                            args.k_rows, chunk, lm_copies)
     if args.decode_steps > 0:
         c0 = chunk if chunk > 1 else 0
         result["decode_loop"] = decode_loop(dd, gen, w, lay, kh, vh, k_copies[0], lens,

@@ -247,9 +247,10 @@ typedef struct dd_ctx_config {
                       fewer host reads outstanding, which disturbs the
                       concurrent HBM-bound scoring less; enough of them
                       still saturate the host link */
-  int prefetch_mode; /* DD_PREFETCH_AUTO (fused for L == 1 or when rows are
-                      kept across steps, side stream otherwise),
-                      DD_PREFETCH_SIDE or DD_PREFETCH_FUSED */
+  int prefetch_mode; /* DD_PREFETCH_AUTO (fused for L == 1, when rows are
+                      kept across steps, or when a layer's prefetch is under
+                      16 MiB; side stream otherwise), DD_PREFETCH_SIDE or
+                      DD_PREFETCH_FUSED */
   int k_rows;       /* DD_KROWS_DEVICE (0) or DD_KROWS_HOST: where attention
                       reads the K rows of the selected entries */
   /* Race detection: when > 0, dd_layer_step enqueues a fixed stall of about

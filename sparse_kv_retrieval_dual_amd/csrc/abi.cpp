@@ -46,6 +46,9 @@ constexpr int64_t kSelectWindowLinkBytes = int64_t(384) << 10;
 // Bytes the key scan streams from HBM while the host link moves one byte
 // of prefetch beside it.
 constexpr int64_t kScanBytesPerLinkByte = 100;
+// Smallest per-layer prefetch that DD_PREFETCH_AUTO puts on the side stream
+// when there are several layers.
+constexpr int64_t kSideMinPrefetchBytes = int64_t(16) << 20;
 
 // Workgroups of one layer's prefetch when the context leaves it open: 32 for
 // a small prefetch (1 MiB at batch 1, k = 128: 16 to 32 were equal, 8 too
@@ -558,9 +561,17 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
   // With rows kept across steps, a layer's prefetch has its own slot to
   // fill and no slot to wait for; inside the layer's scoring kernel it
   // disturbed the main stream least (a 4-layer step at batch 16, k = 1024:
-  // 5.96 ms against 6.70 ms on the side stream).
+  // 5.96 ms against 6.70 ms on the side stream).  Without them the side
+  // stream pays only where a layer's prefetch is large: its cross-stream
+  // waits cost about 13 us per layer in graph replays (8 layers of the 7B
+  // shape at batch 1, 1 MiB per layer: 78.5 against 66.1 us per layer, and
+  // 54.0 against 40.9 with 8-key chunks), while at batch 16, k = 1024 (128
+  // MiB per layer) it was 1% ahead.
+  const int64_t pf_layer_bytes =
+      (int64_t)BH * k * rowb * (c->k_rows == DD_KROWS_DEVICE ? 1 : 2);
   const bool fused = c->prefetch_mode == DD_PREFETCH_FUSED ||
-                     (c->prefetch_mode == DD_PREFETCH_AUTO && (a->L == 1 || resident));
+                     (c->prefetch_mode == DD_PREFETCH_AUTO &&
+                      (a->L == 1 || resident || pf_layer_bytes < kSideMinPrefetchBytes));
   const bool use_side = any_pred && !fused;
   // Where a fused prefetch runs.  Inside the scoring kernel it overlaps the
   // layer's key scan; the slabs whose transfer the scan cannot hide (HBM

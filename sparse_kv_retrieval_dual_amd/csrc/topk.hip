@@ -1450,10 +1450,12 @@ __global__ __launch_bounds__(kNT) void k_topk(
   // chunk_shift, row r & mask of its chunk) is read from host memory, 16
   // bytes per thread per 16 rows, and stored before the attention, so that
   // the transfer overlaps the selection.  Loads complete in issue order, so
-  // the entries are loaded first and the rows only after the score row,
-  // the prediction and the length; and every workgroup of a PF kernel issues
-  // the same loads (one without rows to fetch reads its slab's slot rows
-  // and drops them), so that no join in the kernel has to wait for them.
+  // the entries are loaded first, before the score row, and the rows only
+  // once the score row is in LDS (pf_issue below), when nothing the
+  // selection waits for is issued after them; and every workgroup of a PF
+  // kernel issues the same loads (one without rows to fetch reads its
+  // slab's slot rows and drops them), so that no join in the kernel has to
+  // wait for them.
   constexpr int kPfU = kPrefetchMaxRows * kPrefetchRowBytes / 16 / kNT;
   const bool pf_here = PF && do_book && pred_row != nullptr && bh >= BH - fa.pf_slabs;
   const int pf_rows = k << fa.chunk_shift;

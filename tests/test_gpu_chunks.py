@@ -124,13 +124,18 @@ def test_chunk_layer_step_matches_oracle(name, kw, c, R):
     hot = _run(ctx, w, data, c, pred=pred, ring=ring)
     hctx = dd.Context(ring_slots=R, k_rows="host")
     host = _run(hctx, w, data, c, pred=pred)
+    sctx = dd.Context(ring_slots=R, prefetch="side")
+    side = _run(sctx, w, data, c, pred=pred)
+    sctx.close()
     worst = 0.0
     for l in range(w.L):
         d = data[l]
-        # outputs do not depend on the prediction, nor on where K rows come from
+        # outputs do not depend on the prediction, on where K rows come from,
+        # nor on where the prefetch runs
         for key in ("out", "lse", "cur", "spec"):
             assert torch.equal(hot[key][l], cold[key][l]), (key, l)
             assert torch.equal(host[key][l], hot[key][l]), (key, l)
+            assert torch.equal(side[key][l], hot[key][l]), (key, l)
         lens = d["lens"].numpy()
         kst, vst = stored(d["k"]), stored(d["v"])
         ref = oracle.layer_step(d["q"].numpy(), kst, kst, vst, lens, w.k, w.dtype, chunk=c)
