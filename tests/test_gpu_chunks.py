@@ -262,20 +262,28 @@ def test_chunk_layer_step_full_size_7b():
     print(f"worst relative attention error {worst:.2e}")
 
 
-@pytest.mark.parametrize("H,n_max,c,sel", [(8, 4096, 8, 0), (8, 4096, 8, 3), (6, 1000, 16, 0),
-                                           (32, 32768, 8, 0)])
-def test_selection_side_prefetch_matches_side_stream(H, n_max, c, sel):
+@pytest.mark.parametrize("name,kw,c,sel", [
+    ("llama7b_32k_layer", dict(H=8, n_max=4096), 8, 0),
+    ("llama7b_32k_layer", dict(H=8, n_max=4096), 8, 3),
+    ("llama7b_32k_layer", dict(H=6, n_max=1000), 16, 0),
+    ("llama7b_32k_layer", dict(H=32, n_max=32768), 8, 0),
+    # ragged: some requests shorter than k rows (every chunk selected)
+    ("hiconc_64", dict(B=4, H=2, n_max=4096, len_lo=1, len_hi=4096, k=128), 8, 0),
+    ("hiconc_64", dict(B=4, H=2, n_max=4096, len_lo=1, len_hi=4096, k=128), 8, 5),
+])
+def test_selection_side_prefetch_matches_side_stream(name, kw, c, sel):
     """One layer with 256-byte V rows and k <= 128 rows: the prediction's rows
     are fetched by the selection kernel for the last slabs (by the layer's
-    sizes: all slabs at the two small shapes, 12 of 32 at the full 7B shape;
-    or the last `sel`) and by the scoring kernel for the rest.  Outputs,
+    sizes: all slabs at the small shapes, 12 of 32 at the full 7B shape; or
+    the last `sel`) and by the scoring kernel for the rest.  Outputs,
     statistics and every slab's prefetched slot rows must equal those of a
     side-stream prefetch bit for bit, and the slot rows must hold the host
     rows of the prediction (zero rows for entries outside the cache, -1, and
     rows past the last key)."""
     dd = require_gpu()
-    w = gen.workload("llama7b_32k_layer").scaled(L=1, H=H, n_max=n_max)
-    announce(f"selection-side prefetch H={H} n_max={n_max} chunk={c} slabs={sel}")
+    w = gen.workload(name).scaled(L=1, **kw)
+    H, n_max = w.H, w.n_max
+    announce(f"selection-side prefetch {name} {kw} chunk={c} slabs={sel}")
     data = _stage(dd, w, c)
     B, ks, k = w.B, w.k // c, w.k
     nc = -(-n_max // c)
