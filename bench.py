@@ -28,6 +28,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "keys scored/s (% HBM peak) + gather GB/s + layer decode step µs, 7B-shape 32K"
 HBM_PEAK_GBPS = 8000.0
+# The host link the pages' cost model takes (a PCIe 5.0 x16 figure, arXiv
+# page, section 2.2); the measured pinned copy is the other reference.
+LINK_PAGES_GBPS = 64.0
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -39,6 +42,18 @@ def _progress(msg: str) -> None:
     """A line on stderr as each phase of the run ends (stdout holds only the
     JSON result)."""
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo (or "unknown")."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _source_hash(files) -> str:
@@ -298,10 +313,12 @@ def components(dd, gen, w, kh, vh, h2d_gbps: float, dev, reps: int = 6):
     return {
         "gather_rows": {"rows_per_head": m, "planes": 2, "bytes": gbytes, "us": t_rows * 1e3,
                         "GBps": gbytes / (t_rows * 1e-3) / 1e9,
-                        "frac_of_h2d": gbytes / (t_rows * 1e-3) / 1e9 / h2d_gbps},
+                        "frac_of_h2d": gbytes / (t_rows * 1e-3) / 1e9 / h2d_gbps,
+                        "frac_of_64GBps": gbytes / (t_rows * 1e-3) / 1e9 / LINK_PAGES_GBPS},
         "gather_chunks8": {"chunks_per_head": m // c, "planes": 2, "bytes": gbytes,
                            "us": t_chunks * 1e3, "GBps": gbytes / (t_chunks * 1e-3) / 1e9,
-                           "frac_of_h2d": gbytes / (t_chunks * 1e-3) / 1e9 / h2d_gbps},
+                           "frac_of_h2d": gbytes / (t_chunks * 1e-3) / 1e9 / h2d_gbps,
+                           "frac_of_64GBps": gbytes / (t_chunks * 1e-3) / 1e9 / LINK_PAGES_GBPS},
         "sparse_attention": {"shape": f"B={aB} H={aH} k={ak} D={aD} {sw.dtype}",
                              "algorithmic_bytes": abytes, "us": t_attn * 1e3,
                              "GBps": abytes / (t_attn * 1e-3) / 1e9,
@@ -435,7 +452,9 @@ def gather_worked_example(dd, w, kh, vh, lens, h2d_gbps: float, dev, reps: int =
             "GBps": nbytes / (t * 1e-3) / 1e9, "frac_of_h2d": nbytes / (t * 1e-3) / 1e9 / h2d_gbps,
             "timing": "one call alone, events around it, median of %d" % reps,
             "back_to_back_us": tb * 1e3, "back_to_back_GBps": nbytes / (tb * 1e-3) / 1e9,
-            "back_to_back_frac_of_h2d": nbytes / (tb * 1e-3) / 1e9 / h2d_gbps}
+            "back_to_back_frac_of_h2d": nbytes / (tb * 1e-3) / 1e9 / h2d_gbps,
+            "frac_of_64GBps": nbytes / (t * 1e-3) / 1e9 / LINK_PAGES_GBPS,
+            "back_to_back_frac_of_64GBps": nbytes / (tb * 1e-3) / 1e9 / LINK_PAGES_GBPS}
 
 
 def hbm_read_rate(dd, dev, reps: int = 5, slice_bytes: int = 1 << 28):
@@ -540,7 +559,7 @@ def cpu_baseline(w, lay, budget_s: float):
     names = ("score", "topk_full_sort", "gather", "masked_attention")
     per_layer = {n: float(x) / reps * 1e3 for n, x in zip(names, stage)}
     return {"value": keys / el, "unit": "keys/s", "cores": threads, "kind": "oracle",
-            "affinity_cores": affinity,
+            "affinity_cores": affinity, "cpu_model": _cpu_model(),
             "layer_step_ms_wall": el / reps * 1e3,
             "stage_thread_ms_per_layer": per_layer,
             "sample": f"{reps} oracle layer steps of {w.name} (B={nb} H={w.H} n={w.n_max} "
