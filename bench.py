@@ -351,6 +351,7 @@ def stage_inputs(dd, gen, w, dev, copies: int, k_host: bool = True):
 def one_workload(dd, gen, name: str, h2d_gbps: float, dev, steps: int = 6):
     """One layer step of a workload at its full per-layer shape: eager
     steps, each bracketed by events on the caller's stream (median), the
+    same step replayed from a HIP graph, the
     scoring kernel's own duration from events its dispatch records, and the
     host-link bytes the step moved (prefetched and missed V rows) against
     the measured pinned-copy rate.  Keys rotate over two HBM copies when
@@ -388,6 +389,33 @@ def one_workload(dd, gen, name: str, h2d_gbps: float, dev, steps: int = 6):
     step_us = float(np.median([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(2, steps + 2)])) * 1e3
     score_us = float(np.median([tev.elapsed_ms(E * i, E * i + 1) for i in range(2, steps + 2)])) * 1e3
     st = stats[0].cpu().tolist()
+    # The same step replayed from a HIP graph (one step per key copy,
+    # checked against the eager output first), as a decode loop runs it.
+    graph_us, graph_note = None, None
+    try:
+        ref = res["out"][0].clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in range(len(k_copies)):
+                ctx.layer_step([q], [k_copies[c]], None, [vh], lens, w.k, pred=pred,
+                               cur=res["cur"], spec=res["spec"], out=res["out"],
+                               lse=res["lse"], stats=stats)
+        res["out"][0].zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(res["out"][0], ref):
+            raise RuntimeError("graph replay differs from the eager step")
+        gt = []
+        for i in range(steps):
+            ev.record(0)
+            g.replay()
+            ev.record(1)
+            torch.cuda.synchronize()
+            gt.append(ev.elapsed_ms(0, 1) * 1e3 / len(k_copies))
+        graph_us = float(np.median(gt))
+        del g
+    except Exception as e:  # noqa: BLE001
+        graph_note = f"graph replay unavailable: {e}"
     n_keys = int(lens.sum().item()) * w.H
     score_bytes = n_keys * (w.D * w.elem_bytes + 8)
     link_bytes = st[2] * w.D * w.elem_bytes
@@ -401,7 +429,10 @@ def one_workload(dd, gen, name: str, h2d_gbps: float, dev, steps: int = 6):
            "link_bytes": link_bytes, "link_floor_us": floor_us,
            "frac_of_link_floor": floor_us / step_us,
            "recall": st[1] / max(st[0] + st[1], 1), "misses": st[0],
-           "timing": "eager, events around each step, median", "inputs_staged_s": t_stage}
+           "timing": "eager, events around each step, median",
+           "graph_layer_step_us": graph_us, "graph_keys_per_s":
+               None if graph_us is None else n_keys / (graph_us * 1e-6),
+           "graph_note": graph_note, "inputs_staged_s": t_stage}
     del lay, kh, vh, k_copies, res, pred, stats
     gc.collect()
     torch.cuda.empty_cache()

@@ -261,12 +261,13 @@ typedef struct dd_ctx_config {
      production. */
   int perturb_side_us;
   int perturb_main_us;
-  /* Where a fused prefetch of 256-byte V rows (k <= 128 rows, score rows of
-     at most 32768 entries, K rows from k_dev) runs: 0 splits it by the
-     layer's sizes between the scoring kernel (beside the key scan) and the
-     selection kernel (beside the selection; the last slabs); n > 0 gives
-     the last min(n, B*H) slabs to the selection kernel; -1 keeps it all in
-     the scoring kernel.  Results are identical for any value. */
+  /* Where a fused prefetch (no rows kept across steps) of 256-byte V rows
+     (k <= 128 rows, score rows of at most 32768 entries, K rows from k_dev)
+     runs: 0 splits it by the layer's sizes between the scoring kernel
+     (beside the key scan) and the selection kernel (beside the selection;
+     the last slabs); n > 0 gives the last min(n, B*H) slabs to the
+     selection kernel; -1 keeps it all in the scoring kernel.  Other
+     prefetches ignore it.  Results are identical for any value. */
   int select_prefetch_slabs;
 } dd_ctx_config;
 
