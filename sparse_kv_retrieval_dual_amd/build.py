@@ -35,9 +35,22 @@ COMMON_FLAGS = [
 ]
 
 
+# Flags of single sources.  topk.hip: the backend's atomic optimizer turns
+# an atomic at a uniform address into a wave-wide reduction loop; the only
+# such atomics there are the per-layer counters, added by one lane, and the
+# loop's register reuse made that lane wait for each atomic to complete
+# before the workgroup's next barrier (a device-scope round trip on the
+# selection's critical path).  Without it the three adds are issued back to
+# back and nothing waits for them.
+SOURCE_FLAGS = {
+    "topk.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
