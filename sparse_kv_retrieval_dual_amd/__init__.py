@@ -10,6 +10,7 @@ from . import _lib
 from .api import (  # noqa: F401
     Context,
     Decoder,
+    PreparedStep,
     attn_workspace_bytes,
     gather,
     gather_chunks,

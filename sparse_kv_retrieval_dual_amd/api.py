@@ -377,6 +377,23 @@ class Context:
         reset clears it first, for the first step of a sequence).
         `timing` is None or a sequence of L * DD_STAGE_EVENTS raw hipEvent_t handles.
         """
+        step = self.prepare_step(q, k_dev, k_host, v_host, lens, k, scale=scale, cur=cur,
+                                 spec=spec, out=out, lse=lse, stats=stats, ring=ring, ws=ws,
+                                 chunk=chunk, landmarks=landmarks, dual=dual, out_spec=out_spec,
+                                 lse_spec=lse_spec, resident=resident, parity=parity,
+                                 reset=reset)
+        return step.run(pred=pred, timing=timing, stream=stream)
+
+    def prepare_step(self, q, k_dev, k_host, v_host, lens, k: int, scale: float = 0.0,
+                     cur=None, spec=None, out=None, lse=None, stats=None, ring=None, ws=None,
+                     chunk: int = 0, landmarks=None, dual: bool = False, out_spec=None,
+                     lse_spec=None, resident=None, parity: int = 0, reset: bool = False):
+        """The arguments of layer_step, checked and marshalled once: the
+        returned PreparedStep runs dd_layer_step on them as often as needed,
+        taking only the prediction (checked like layer_step's), the timing
+        events and the stream per call.  The tensors given here (and the
+        outputs allocated here) are used by every run; their contents may
+        change between runs, their storage may not."""
         Lyr = len(q)
         if k_host is None:
             _need(self.k_rows == "device", "k_host is needed when K rows come from the host")
@@ -402,10 +419,6 @@ class Context:
                     continue
                 _need(not t.is_cuda and t.is_contiguous() and t.shape == (B, H, n_max, D)
                       and t.dtype == k_dev[l].dtype, "host K/V must be contiguous [B][H][n_max][D]")
-            if pred is not None and pred[l] is not None:
-                _dev(pred[l], "pred")
-                _need(pred[l].shape == (B, H, ks) and pred[l].dtype == torch.int32,
-                      "pred must be int32 [B][H][k // chunk]")
             if chunk > 1:
                 _dev(landmarks[l], "landmarks")
                 _need(landmarks[l].shape == (B, H, (n_max + chunk - 1) // chunk, D)
@@ -439,21 +452,18 @@ class Context:
         if ws is None:
             ws = self._buffer("_ws", wb, dev)
         keep = [_ptr_array(q), _ptr_array(k_dev), _ptr_array(k_host), _ptr_array(v_host),
-                _ptr_array(pred) if pred is not None else None,
+                (ctypes.c_void_p * Lyr)(),
                 _ptr_array(cur), _ptr_array(spec), _ptr_array(out),
                 _ptr_array(lse) if lse is not None else None,
                 _ptr_array(landmarks) if chunk > 1 else None,
                 _ptr_array(out_spec) if dual else None,
                 _ptr_array(lse_spec) if dual else None]
-        tarr = None
-        if timing is not None:
-            tarr = (ctypes.c_void_p * len(timing))(*timing)
         a = L.LayerStepArgs(
             L=Lyr, B=B, H=H, D=D, k=int(k), dtype=dt, n_max=n_max, scale=float(scale),
             lens=lens.data_ptr(),
             q=ctypes.cast(keep[0], ctypes.c_void_p), k_dev=ctypes.cast(keep[1], ctypes.c_void_p),
             k_host=ctypes.cast(keep[2], ctypes.c_void_p), v_host=ctypes.cast(keep[3], ctypes.c_void_p),
-            pred=None if keep[4] is None else ctypes.cast(keep[4], ctypes.c_void_p),
+            pred=None,
             cur_idx=ctypes.cast(keep[5], ctypes.c_void_p), spec_idx=ctypes.cast(keep[6], ctypes.c_void_p),
             out=ctypes.cast(keep[7], ctypes.c_void_p),
             lse=None if keep[8] is None else ctypes.cast(keep[8], ctypes.c_void_p),
@@ -461,9 +471,7 @@ class Context:
             ring=None if ring is None else ring.data_ptr(),
             ring_bytes=0 if ring is None else ring.numel() * ring.element_size(),
             ws=ws.data_ptr(), ws_bytes=ws.numel() * ws.element_size(),
-            stream=_stream(stream).value,
-            timing=None if tarr is None else ctypes.cast(tarr, ctypes.c_void_p),
-            chunk=chunk,
+            stream=None, timing=None, chunk=chunk,
             landmarks=None if keep[9] is None else ctypes.cast(keep[9], ctypes.c_void_p),
             out_spec=None if keep[10] is None else ctypes.cast(keep[10], ctypes.c_void_p),
             lse_spec=None if keep[11] is None else ctypes.cast(keep[11], ctypes.c_void_p),
@@ -471,11 +479,56 @@ class Context:
             resident_bytes=0 if resident is None else resident.numel() * resident.element_size(),
             parity=int(parity), reset=1 if reset else 0,
         )
-        L.check(_lib().dd_layer_step(self._h, ctypes.byref(a)))
         res = {"cur": cur, "spec": spec, "out": out, "lse": lse, "stats": stats}
         if dual:
             res["out_spec"], res["lse_spec"] = out_spec, lse_spec
-        return res
+        # Tensors whose storage the marshalled pointers name stay referenced.
+        held = (q, k_dev, k_host, v_host, lens, landmarks, ring, ws, resident)
+        return PreparedStep(self, a, keep, res, (B, H, ks, Lyr), held)
+
+
+class PreparedStep:
+    """One dd_layer_step call's arguments, marshalled by Context.prepare_step."""
+
+    def __init__(self, ctx, args, keep, result, shape, held):
+        self._ctx = ctx
+        self._a = args
+        self._keep = keep
+        self._pred_arr = keep[4]
+        self._pred_ptr = ctypes.cast(keep[4], ctypes.c_void_p)
+        self.result = result
+        self._shape = shape
+        self._held = held
+
+    def run(self, pred=None, timing=None, stream=None):
+        """dd_layer_step on the prepared arguments.  pred: None or a list of
+        one int32 [B][H][k // chunk] device tensor (or None) per layer.
+        `timing`: None or a sequence of L * DD_STAGE_EVENTS raw hipEvent_t
+        handles.  Returns the result dict (the prepared output tensors)."""
+        a = self._a
+        B, H, ks, Lyr = self._shape
+        if pred is None:
+            a.pred = None
+        else:
+            _need(len(pred) == Lyr, "pred needs one entry per layer")
+            arr = self._pred_arr
+            for l in range(Lyr):
+                p = pred[l]
+                if p is None:
+                    arr[l] = None
+                    continue
+                _dev(p, "pred")
+                _need(p.shape == (B, H, ks) and p.dtype == torch.int32,
+                      "pred must be int32 [B][H][k // chunk]")
+                arr[l] = p.data_ptr()
+            a.pred = self._pred_ptr
+        tarr = None
+        if timing is not None:
+            tarr = (ctypes.c_void_p * len(timing))(*timing)
+        a.timing = None if tarr is None else ctypes.cast(tarr, ctypes.c_void_p)
+        a.stream = _stream(stream).value
+        L.check(_lib().dd_layer_step(self._ctx._h, ctypes.byref(a)))
+        return self.result
 
 
 class Decoder:
@@ -491,6 +544,13 @@ class Decoder:
     keeps its selected rows across steps (dd_layer_step_args.resident), so a
     step fetches over the host link only rows its previous step did not
     bring in; the state is cleared on the first step.
+
+    The outputs of a step (cur, spec, out, lse, stats) live in one of two
+    buffer sets used in turn, so a step's results stay valid through the
+    next step and are overwritten by the one after; clone what must live
+    longer.  Each step's arguments are marshalled once per buffer set,
+    parity and set of query tensors (prepared steps), so a loop that reuses
+    its query tensors pays the argument checks only on its first steps.
     """
 
     def __init__(self, ctx: Context, k_dev, k_host, v_host, lens, k: int, chunk: int = 0,
@@ -507,6 +567,9 @@ class Decoder:
             self.landmarks = [landmarks(kd, self._lens[0], self.chunk) for kd in self.k_dev]
         self.pred = None
         self.history = []  # per step: stats [L][3] (device)
+        self._bufs = [None, None]  # output sets, used in turn
+        self._buf = 0
+        self._plans = {}
         self.state = None
         self._parity, self._reset = 0, True
         if resident:
@@ -528,12 +591,28 @@ class Decoder:
                       landmarks=None if self.landmarks is None else self.landmarks[l],
                       stream=stream)
         self._cur = 1 - self._cur
-        res = self.ctx.layer_step(list(q), self.k_dev, self.k_host, self.v_host, self.lens, self.k,
-                                  pred=self.pred, stream=stream, chunk=self.chunk,
-                                  landmarks=self.landmarks, resident=self.state,
-                                  parity=self._parity, reset=self._reset)
+        q = list(q)
+        b = self._buf
+        key = (b, self._cur, self._parity, self._reset, tuple(t.data_ptr() for t in q))
+        plan = self._plans.get(key)
+        if plan is None:
+            if len(self._plans) >= 16:  # query tensors that change every step
+                self._plans.clear()
+            o = self._bufs[b] or {}
+            plan = self.ctx.prepare_step(q, self.k_dev, self.k_host, self.v_host, self.lens,
+                                         self.k, cur=o.get("cur"), spec=o.get("spec"),
+                                         out=o.get("out"), lse=o.get("lse"),
+                                         stats=o.get("stats"), chunk=self.chunk,
+                                         landmarks=self.landmarks, resident=self.state,
+                                         parity=self._parity, reset=self._reset)
+            self._bufs[b] = plan.result
+            self._plans[key] = plan
+        res = plan.run(pred=self.pred, stream=stream)
         if self.state is not None:
             self._parity, self._reset = 1 - self._parity, False
-        self.pred = [s.clone() for s in res["spec"]]
+        # The next step reads this step's speculated sets from this buffer
+        # set while it writes the other one.
+        self.pred = res["spec"]
+        self._buf = 1 - b
         self.history.append(res["stats"].clone())
         return res

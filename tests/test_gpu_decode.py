@@ -72,12 +72,16 @@ def _check_step(w, res, ref, lens, chunk, q_cur, kst, vst):
     return not d_cur and not d_spec
 
 
-@pytest.mark.parametrize("name,kw,chunk", [
-    ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000), 0),
-    ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000), 8),
-    ("tiny", dict(n_max=2048, len_lo=1500, len_hi=1500), 0),
+@pytest.mark.parametrize("name,kw,chunk,qbuf", [
+    ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000), 0, False),
+    ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000), 8, False),
+    ("tiny", dict(n_max=2048, len_lo=1500, len_hi=1500), 0, False),
+    # the queries written into one buffer each step: the decoder reuses its
+    # prepared steps (and its two output sets) from the third step on
+    ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000), 0, True),
+    ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000), 8, True),
 ])
-def test_decode_loop_matches_oracle(name, kw, chunk):
+def test_decode_loop_matches_oracle(name, kw, chunk, qbuf):
     """Four real steps: at each, the GPU's sets, attention and (where the sets
     agree) statistics match the oracle's loop on the same grown cache."""
     dd = require_gpu()
@@ -97,10 +101,19 @@ def test_decode_loop_matches_oracle(name, kw, chunk):
     dec.pred = [s.clone() for s in res["spec"]]
     ref = oracle.layer_step(q.numpy(), kst, kst, vst, lens, w.k, w.dtype, chunk=chunk)
     same = _check_step(w, res, ref, lens, chunk, q[:, :, 0].numpy(), kst, vst)
+    qd = q.cuda()
+    prev = None
     for t in range(1, 5):
         q, nk, nv = gen.decode_step_inputs(w, 0, t, q)
-        res = dec.step([q.cuda()], [nk.cuda()], [nv.cuda()])
+        if qbuf:
+            qd.copy_(q)
+        else:
+            qd = q.cuda()
+        res = dec.step([qd], [nk.cuda()], [nv.cuda()])
         torch.cuda.synchronize()
+        if prev is not None:  # the previous step's results are still intact
+            assert torch.equal(prev[1], prev[0]["out"][0]), t
+        prev = (res, res["out"][0].clone())
         kst, _ = oracle.append_rows(kst, lens, stored(nk))
         vst, lens = oracle.append_rows(vst, lens, stored(nv))
         assert dec.lens.cpu().numpy().tolist() == lens.tolist()

@@ -180,3 +180,39 @@ def test_layer_step_workspace_errors():
         _run(dd, ctx, w, data, ws=small)
     assert e.value.code == 3
     ctx.close()
+
+
+def test_prepared_step_matches_layer_step():
+    """A prepared step run with a prediction, with none and with another one
+    gives what layer_step gives for each, bit for bit (outputs, sets,
+    statistics), and layer_step's outputs do not depend on the prediction."""
+    dd = require_gpu()
+    w = gen.workload("llama7b_32k_layer").scaled(L=2, B=2, H=4, n_max=5000, k=256)
+    announce("prepared step against layer_step")
+    data = []
+    for l in range(w.L):
+        lay = gen.make_layer(w, l, "cpu")
+        data.append(dict(q=lay["q"].cuda(), k=lay["k"].cuda(), kh=to_host(dd, lay["k"]),
+                         vh=to_host(dd, lay["v"]), lens=lay["lens"].cuda()))
+    args = ([d["q"] for d in data], [d["k"] for d in data], [d["kh"] for d in data],
+            [d["vh"] for d in data], data[0]["lens"], w.k)
+    ctx = dd.Context(ring_slots=2)
+    cold = ctx.layer_step(*args)
+    pa = [s.clone() for s in cold["spec"]]
+    pb = [torch.flip(s, dims=[2]).contiguous() for s in cold["cur"]]
+    want = {}
+    for name, p in (("a", pa), ("none", None), ("b", pb)):
+        r = ctx.layer_step(*args, pred=p)
+        torch.cuda.synchronize()
+        want[name] = {k_: [t.clone() for t in r[k_]] for k_ in ("out", "lse", "cur", "spec")}
+        want[name]["stats"] = r["stats"].clone()
+    step = ctx.prepare_step(*args)
+    for name, p in (("a", pa), ("none", None), ("b", pb), ("a", pa)):
+        r = step.run(pred=p)
+        torch.cuda.synchronize()
+        for k_ in ("out", "lse", "cur", "spec"):
+            for l in range(w.L):
+                assert torch.equal(r[k_][l], want[name][k_][l]), (name, k_, l)
+                assert torch.equal(r[k_][l], want["none"][k_][l]), (name, k_, l)
+        assert torch.equal(r["stats"], want[name]["stats"]), name
+    ctx.close()
