@@ -265,6 +265,7 @@ def test_chunk_layer_step_full_size_7b():
 @pytest.mark.parametrize("name,kw,c,sel", [
     ("llama7b_32k_layer", dict(H=8, n_max=4096), 8, 0),
     ("llama7b_32k_layer", dict(H=8, n_max=4096), 8, 3),
+    ("llama7b_32k_layer", dict(H=8, n_max=4096), 8, -1),   # all in the scoring kernel
     ("llama7b_32k_layer", dict(H=6, n_max=1000), 16, 0),
     ("llama7b_32k_layer", dict(H=32, n_max=32768), 8, 0),
     # ragged: some requests shorter than k rows (every chunk selected)
@@ -275,7 +276,7 @@ def test_selection_side_prefetch_matches_side_stream(name, kw, c, sel):
     """One layer with 256-byte V rows and k <= 128 rows: the prediction's rows
     are fetched by the selection kernel for the last slabs (by the layer's
     sizes: all slabs at the small shapes, 12 of 32 at the full 7B shape; or
-    the last `sel`) and by the scoring kernel for the rest.  Outputs,
+    the last `sel`; none for -1) and by the scoring kernel for the rest.  Outputs,
     statistics and every slab's prefetched slot rows must equal those of a
     side-stream prefetch bit for bit, and the slot rows must hold the host
     rows of the prediction (zero rows for entries outside the cache, -1, and
