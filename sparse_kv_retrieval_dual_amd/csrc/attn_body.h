@@ -210,7 +210,8 @@ __device__ __forceinline__ void attn_fetch_kdev(const AttnRows<T>& R, int c0, in
 // lane's entry u (entries with rows[u] < 0 are skipped), vr[u] its V row
 // bytes.  Each wave forms its own max, weights and weighted V sum over its
 // 32 entries; the four waves are then merged in LDS in wave order (one
-// workgroup barrier; every thread of the workgroup must call it).
+// workgroup barrier; every thread of the workgroup must call it: in a
+// workgroup of more than four waves the others have no entries).
 // Afterwards cm[j] and cl[j] (all threads) are query j's max logit and
 // weight sum over the chunk, and threads d < D hold od[j] = its weighted V
 // sum of column d.  The caller must not touch lds until a barrier after
@@ -261,7 +262,7 @@ __device__ __forceinline__ void attn_softmax_merge(float* s, const int* rows, co
 #pragma unroll
       for (int e = 0; e < S::EPL; ++e) o[e] += __shfl_xor(o[e], off);
     }
-    if (rsub == 0) {
+    if (rsub == 0 && wave < kAttnWaves) {  // (a larger workgroup's other waves hold nothing)
 #pragma unroll
       for (int e = 0; e < S::EPL; ++e) lds.o[qi][wave][col * S::EPL + e] = o[e];
       if (col == 0) {

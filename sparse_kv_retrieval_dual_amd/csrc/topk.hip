@@ -3,14 +3,14 @@
 // page), with the prediction bookkeeping of the layer step fused into the
 // current-query rows.
 //
-// One workgroup of 256 threads (one wave per SIMD) per row.  Scores become
+// One workgroup of 512 threads (two waves per SIMD) per row.  Scores become
 // order-preserving 32-bit keys; the selection is every key > T plus the
 // first k - #(> T) keys equal to T (lower index wins), T being the exact
 // k-th largest key, written in ascending index order.
 //
 // Filter path (rows of up to kFilterMaxN keys).  Thread t reads float4
-// t + 256 u of each 32768-key tile (u < 32, coalesced) and keeps the maximum
-// of each of its G groups of float4s.  With 256 G >= k groups, the lowest
+// t + 512 u of each 32768-key tile (u < 16, coalesced) and keeps the maximum
+// of each of its G groups of float4s.  With 512 G >= k groups, the lowest
 // key B of the 11-bit digit bin holding the k-th largest group maximum has
 // at least k keys >= B, and real score rows have only a small multiple of
 // k of them.  Those candidates are located through the float4 maxima (a row
@@ -22,7 +22,7 @@
 // the row to the radix path.
 //
 // Radix path (every other row): MSB-first radix selection with 11 + 11 + 10
-// bit digits over the whole row, then the same comparison emit 8192 keys at
+// bit digits over the whole row, then the same comparison emit 32 kNT keys at
 // a time.
 //
 // For the current-query row of the layer step, the filter path marks the
@@ -51,10 +51,14 @@ namespace dd {
 
 namespace {
 
-constexpr int kNT = 256;                 // threads per row workgroup
+// Threads per row workgroup: two waves per SIMD, so that one wave's LDS
+// and barrier latencies overlap the other's work (one wave per SIMD left
+// every phase of the selection chain exposed: 19.06 against 17.48 us for
+// the 7B layer's top-k, bookkeeping and attention).
+constexpr int kNT = 512;
 constexpr int kNW = kNT / 64;
 constexpr int kBins = 2048;              // 11-bit digits
-constexpr int kU = 32;                   // float4 per thread per tile
+constexpr int kU = 16;                   // float4 per thread per tile
 constexpr int kTile = 4 * kNT * kU;      // 32768 keys
 static_assert(kTile == kPrefetchMaxScoreRow, "selection-side prefetch needs cached rows");
 constexpr int kMaxK = 4096;              // largest k (DD_MAX_K)
@@ -65,6 +69,7 @@ constexpr int kFilterMaxN = 1 << 17;     // longest row of the filter path
 constexpr int kMaxWords = kFilterMaxN / 32 / kNT;  // bitmap words per thread
 constexpr int kScr = 64;                 // scan buffers and broadcasts
 constexpr int kSegKeys = 32 * kNT;       // keys per radix-path emit segment
+static_assert(kSegKeys < 65536, "a segment's counts fit 16 bits");
 constexpr int kAttrDevices = 64;         // devices whose launch attributes are kept
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -197,7 +202,7 @@ __device__ __forceinline__ void pick_bin(const uint32_t* hist, int kr, ScanBufs&
 
 // The exact k-th largest key T among the cnt candidate keys (k <= cnt <=
 // CAP) and how many keys equal to T the selection takes, by MSB-first radix
-// selection with 8-bit digits.  Thread t holds candidates t + 256 r in
+// selection with 8-bit digits.  Thread t holds candidates t + kNT r in
 // registers; pass p counts into its own 256-counter histogram h4 + 256 p,
 // cleared by the caller before a barrier that precedes this call.  After
 // each pass's barrier every wave scans the histogram itself, so T needs no
@@ -628,7 +633,7 @@ __device__ __forceinline__ void prediction_rows(const int32_t (&pv)[kPR], int k,
 
 // ---------------------------------------------------------------- filter path
 
-// Float4 q = t + 256 u of the tile starting at entry c0 of the row, u < 32,
+// Float4 q = t + kNT u of the tile starting at entry c0 of the row, u < kU,
 // loaded unconditionally (clamped to the first nload entries).  vec: the
 // row is 16-byte aligned and n_max is a multiple of 4, so every float4
 // holding an entry < nload lies inside the row's storage.
@@ -692,6 +697,7 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
                               AfterRow&& after_row) {
   using L = Lay<CACHED>;
   constexpr int CAP = L::cap;
+  static_assert(G >= 1 && G <= kU, "a group holds at least one float4");
   constexpr int UPG = kU / G;  // float4s per group and tile
   const int tid = threadIdx.x;
   uint32_t* hist = smem + kLHist;
@@ -745,7 +751,7 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
   after_row();      // the caller's work once the row's registers are free
 
   // The bound: lowest key of the digit bin holding the k-th largest group
-  // maximum (256 G >= k groups).
+  // maximum (kNT G >= k groups).
 #pragma unroll
   for (int g = 0; g < G; ++g) atomicAdd(&hist[order_key(gmax[g]) >> 21], 1u);
   __syncthreads();
@@ -1197,7 +1203,7 @@ __device__ __forceinline__ void row_hist(const float* __restrict__ row, int n, u
   }
 }
 
-// The radix path: T over the whole row, then, 8192 keys at a time, thread
+// The radix path: T over the whole row, then, 32 kNT keys at a time, thread
 // t compares keys 32 t .. 32 t + 31 of the segment with T.
 template <bool CACHED>
 __device__ __forceinline__ int radix_select(const float* __restrict__ row, int n, int64_t n_max, int k,
@@ -1258,7 +1264,7 @@ __device__ __forceinline__ int radix_select(const float* __restrict__ row, int n
       fetchable = tp & 0xFFFF;
       if (sk.s_pred != nullptr) sk.plen = tp >> 16;
     }
-    // Per-segment counts stay below 2^16 (8192 keys).
+    // Per-segment counts stay below 2^16 (kSegKeys = 32 kNT keys).
     const int mtot = emit_words<1>(g, e, base / 32, out_run + (ex & 0xFFFF),
                                    eq_run + (ex >> 16), kr, k, sk, sb, miss_run, kSearchStart);
     out_run += tx & 0xFFFF;
@@ -1326,17 +1332,21 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
   float* const outs[2] = {fa.out, fa.out_spec};
   float* const lses[2] = {fa.lse, fa.lse_spec};
   const int d = threadIdx.x;
+  // Four waves attend a chunk of kAttnChunk entries; the workgroup's other
+  // waves find no entry below the chunk's limit and only join its barriers.
   for (int ch = 0; ch < chunks; ++ch) {
     float cm[NQ], cl[NQ], od[NQ];
     if (srow != nullptr) {
       AttnFetchS<T, D, NQ> f;
-      attn_fetch_s<T, D, NQ>(R, srow, n_rows, nq, ch * kAttnChunk, k, entry, f, threadIdx.x);
+      attn_fetch_s<T, D, NQ>(R, srow, n_rows, nq, ch * kAttnChunk,
+                             min(k, (ch + 1) * kAttnChunk), entry, f, threadIdx.x);
       attn_finish_s<T, D, NQ>(R, f, lds, nq, cm, cl, od, threadIdx.x);
     } else if (kdev && lold == nullptr) {
-      attend_chunk_n<T, D, NQ, true>(qrow, R, ch * kAttnChunk, k, fa.scale, entry, lds, nq, cm, cl,
-                                     od);
+      attend_chunk_n<T, D, NQ, true>(qrow, R, ch * kAttnChunk, min(k, (ch + 1) * kAttnChunk),
+                                     fa.scale, entry, lds, nq, cm, cl, od);
     } else {
-      attend_chunk_n<T, D, NQ>(qrow, R, ch * kAttnChunk, k, fa.scale, entry, lds, nq, cm, cl, od);
+      attend_chunk_n<T, D, NQ>(qrow, R, ch * kAttnChunk, min(k, (ch + 1) * kAttnChunk),
+                               fa.scale, entry, lds, nq, cm, cl, od);
     }
     if (d < D) {
       for (int qi = 0; qi < nq; ++qi) {
@@ -1463,7 +1473,7 @@ __global__ __launch_bounds__(kNT) void k_topk(
   if constexpr (PF) {
 #pragma unroll
     for (int u = 0; u < kPfU; ++u) {
-      const int r = min(tid / 16 + 16 * u, pf_rows - 1);
+      const int r = min(tid / 16 + (kNT / 16) * u, pf_rows - 1);
       pf_e[u] = *(pf_here ? pred_row + (r >> fa.chunk_shift) : lens);
     }
   }
@@ -1510,7 +1520,7 @@ __global__ __launch_bounds__(kNT) void k_topk(
                           (int64_t)bh * 2 * pf_rows * kPrefetchRowBytes + (tid % 16) * 16;
 #pragma unroll
       for (int u = 0; u < kPfU; ++u) {
-        const int r = min(tid / 16 + 16 * u, pf_rows - 1);
+        const int r = min(tid / 16 + (kNT / 16) * u, pf_rows - 1);
         const int64_t hr = ((int64_t)pf_e[u] << cs) + (r & ((1 << cs) - 1));
         pf_ok[u] = pf_here && pf_e[u] >= 0 && hr < fa.n_rows;
         const uint8_t* src = pf_ok[u] ? vh + hr * kPrefetchRowBytes : vs + r * kPrefetchRowBytes;
@@ -1581,7 +1591,7 @@ __global__ __launch_bounds__(kNT) void k_topk(
       // zero select (and with it the wait for the host reads) up to the
       // loads.
       asm volatile("" : "+v"(pfv[u]));
-      const int r = tid / 16 + 16 * u;
+      const int r = tid / 16 + (kNT / 16) * u;
       if (pf_here && r < pf_rows)
         *reinterpret_cast<u32x4*>(vs + r * kPrefetchRowBytes) = pf_ok[u] ? pfv[u] : zero;
     }
@@ -1634,8 +1644,7 @@ TopkKernel pick_kernel(int g) {
     case 2: return k_topk<2, CACHED, false>;
     case 4: return k_topk<4, CACHED, false>;
     case 8: return k_topk<8, CACHED, false>;
-    case 16: return k_topk<16, CACHED, false>;
-    default: return k_topk<32, CACHED, false>;
+    default: return k_topk<16, CACHED, false>;
   }
 }
 
@@ -1660,7 +1669,7 @@ hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, i
   const size_t shmem = (size_t)words * 4;
   // Groups per thread: at least 4k group maxima (8192 at most).
   int g = 1;
-  while (g < 32 && kNT * g < 4 * k) g *= 2;
+  while (g < kU && kNT * g < 4 * k) g *= 2;
   // Dynamic LDS beyond the runtime's default needs the kernels' opt-in
   // attribute, set once per device (the first caller sets it while any
   // others wait) to what the device leaves beside each kernel's static LDS;
@@ -1674,7 +1683,7 @@ hipError_t launch_topk(const float* scores, const int32_t* lens, int B, int H, i
   std::call_once(attr_once[di.device], [&di]() {
     hipError_t e = hipSuccess;
     size_t room[2] = {(size_t)di.lds_per_block, (size_t)di.lds_per_block};
-    for (int gg = 1; gg <= 32 && e == hipSuccess; gg *= 2) {
+    for (int gg = 1; gg <= kU && e == hipSuccess; gg *= 2) {
       for (int c = 0; c < 3 && e == hipSuccess; ++c) {
         if (c == 2 && gg > 2) break;
         const void* fn = c == 2 ? reinterpret_cast<const void*>(pick_pf_kernel(gg))
