@@ -98,6 +98,14 @@ __device__ __forceinline__ void attn_fetch(const AttnRows<T>& R, int c0, int lim
   const int col = lane % S::LPR;
   const int rsub = lane / S::LPR;
   const int e0 = c0 + wave * kWaveEntries;  // this wave's first entry
+  if (wave >= kAttnWaves) {  // a larger workgroup's other waves: no entries, no loads
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      f.rows[u] = f.hrow[u] = -1;
+      f.kr[u] = f.vr[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
   const bool from_host = R.vhb != nullptr;
   const bool kdev = R.kdb != nullptr;
   int krow[S::U];  // row of the device key copy (kdev), else -1
@@ -158,6 +166,14 @@ __device__ __forceinline__ void attn_fetch_kdev(const AttnRows<T>& R, int c0, in
   const int col = lane % S::LPR;
   const int rsub = lane / S::LPR;
   const int e0 = c0 + wave * kWaveEntries;
+  if (wave >= kAttnWaves) {  // a larger workgroup's other waves: no entries, no loads
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      f.rows[u] = f.hrow[u] = -1;
+      f.kr[u] = f.vr[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
   const bool from_host = R.vhb != nullptr;
   int krow[S::U];
   // Every entry is looked up first (an entry past lim looks up entry
@@ -390,6 +406,16 @@ __device__ __forceinline__ void attn_fetch_s(const AttnRows<T>& R, const float* 
   const int col = lane % S::LPR;
   const int rsub = lane / S::LPR;
   const int e0 = c0 + wave * kWaveEntries;
+  if (wave >= kAttnWaves) {  // a larger workgroup's other waves: no entries, no loads
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      f.rows[u] = f.hrow[u] = -1;
+      f.vr[u] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int qi = 0; qi < NQ; ++qi) f.s[qi * S::U + u] = 0.f;
+    }
+    return;
+  }
   const bool from_host = R.vhb != nullptr;
   // Every entry is looked up first (an entry past lim looks up entry
   // lim - 1 and is dropped), so that the lookups are in flight together.
