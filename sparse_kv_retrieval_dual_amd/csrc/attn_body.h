@@ -1,13 +1,16 @@
 // One chunk of sparse decode attention for one (b, h), shared by the
 // attention kernel and the layer step's fused top-k + attention kernel.
 //
-// A 256-thread workgroup handles up to 128 entries; each wave owns 32.  A
-// row is read by LPR lanes, 16 B each; every lane issues its K and V loads
-// for all of its entries at once (one memory round trip), the dot products
-// are summed across the LPR lanes by a DPP butterfly that leaves every lane
-// with all of its entries' logits, and the wave forms its own max, weights
-// and weighted V sum without a workgroup barrier.  The four waves are
-// merged in LDS by log-sum-exp in a fixed order.  Every reduction runs in
+// A chunk of 128 entries is shared by NW waves, 128 / NW consecutive
+// entries each: four waves in the attention kernel's 256-thread groups,
+// eight in the top-k kernel's 512-thread workgroups (two waves per SIMD,
+// so each wave's issue and latency overlap the other's).  A row is read by
+// LPR lanes, 16 B each; every lane issues its K and V loads for all of its
+// entries at once (one memory round trip), the dot products are summed
+// across the LPR lanes by a DPP butterfly that leaves every lane with all
+// of its entries' logits, and the wave forms its own max, weights and
+// weighted V sum without a workgroup barrier.  The NW waves are merged in
+// LDS by log-sum-exp in a fixed order.  Every reduction runs in
 // the order of the entry number j, never of the row it is stored in, so the
 // result does not depend on where rows sit.
 #pragma once
@@ -18,17 +21,18 @@ namespace dd {
 
 constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / 64;
-constexpr int kWaveEntries = 32;
-constexpr int kAttnChunk = kAttnWaves * kWaveEntries;
+constexpr int kAttnChunk = 128;  // entries per chunk
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <typename T, int D>
+// NW: waves sharing a chunk.
+template <typename T, int D, int NW = kAttnWaves>
 struct AttnShape {
+  static constexpr int WE = kAttnChunk / NW;       // entries per wave
   static constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane per load
   static constexpr int LPR = D / EPL;              // lanes per row
   static constexpr int RPI = 64 / LPR;             // rows per wave load instruction
-  static constexpr int U = kWaveEntries / RPI;     // entries (K and V loads) per lane
-  static_assert(U >= 1 && U * RPI == kWaveEntries, "shape");
+  static constexpr int U = WE / RPI;               // entries (K and V loads) per lane
+  static_assert(WE * NW == kAttnChunk && U >= 1 && U * RPI == WE, "shape");
 };
 
 // All-reduce of NV values over aligned groups of G lanes.
@@ -64,45 +68,53 @@ struct AttnRows {
 };
 
 // LDS of one chunk merge, per query: per-wave max, weight sum and weighted V.
-template <int D, int NQ = 1>
+template <int D, int NQ = 1, int NW = kAttnWaves>
 struct AttnLds {
-  float m[NQ][kAttnWaves];
-  float l[NQ][kAttnWaves];
-  float o[NQ][kAttnWaves][D];
+  float m[NQ][NW];
+  float l[NQ][NW];
+  float o[NQ][NW][D];
 };
 
 // The rows of one chunk in registers: entry slot rows (-1: skipped), the
 // host row of each miss (-1 otherwise) and every entry's K and V bytes.
-template <typename T, int D>
+template <typename T, int D, int NW = kAttnWaves>
 struct AttnFetch {
-  using S = AttnShape<T, D>;
+  using S = AttnShape<T, D, NW>;
   int rows[S::U];
   int hrow[S::U];
   u32x4 kr[S::U], vr[S::U];
 };
 
 // First half of a chunk (entries c0 .. c0 + 127 below lim, handled by the
-// 256 threads tid = 0 .. 255): resolves each entry's rows through
+// NW waves of threads tid = 0 .. 64 NW - 1): resolves each entry's rows through
 // entry(j, r, c, o) (slot row r, -1: skipped; host row c; row o of the
 // previous step's slot holding a miss, else -1) and issues its K and V loads, all at once (slot rows and device keys from
 // HBM, missed rows over the host link); a skipped entry reads row 0 of the
 // slab (when there is one) and is masked later.  Nothing waits for the
 // loads here, so a caller can fetch the next chunk before it finishes this
 // one.
-template <typename T, int D, class Entry>
+template <typename T, int D, int NW = kAttnWaves, class Entry>
 __device__ __forceinline__ void attn_fetch(const AttnRows<T>& R, int c0, int lim, Entry entry,
-                                           AttnFetch<T, D>& f, int tid) {
-  using S = AttnShape<T, D>;
+                                           AttnFetch<T, D, NW>& f, int tid) {
+  using S = AttnShape<T, D, NW>;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int col = lane % S::LPR;
   const int rsub = lane / S::LPR;
-  const int e0 = c0 + wave * kWaveEntries;  // this wave's first entry
-  if (wave >= kAttnWaves) {  // a larger workgroup's other waves: no entries, no loads
+  const int e0 = c0 + wave * S::WE;  // this wave's first entry
+  if (wave >= NW) {  // a larger workgroup's other waves: no entries, no loads
+    // The stores in the order of the loads' path below (rows, hrow, then K
+    // and V), so that the compiler can merge both paths' stores without
+    // selecting between addresses (which would keep f in scratch memory).
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
-      f.rows[u] = f.hrow[u] = -1;
-      f.kr[u] = f.vr[u] = u32x4{0u, 0u, 0u, 0u};
+      f.rows[u] = -1;
+      f.hrow[u] = -1;
+    }
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      f.kr[u] = u32x4{0u, 0u, 0u, 0u};
+      f.vr[u] = u32x4{0u, 0u, 0u, 0u};
     }
     return;
   }
@@ -157,20 +169,28 @@ __device__ __forceinline__ void attn_fetch(const AttnRows<T>& R, int c0, int lim
 // attn_fetch for the common case of the layer step: every K row from the
 // device key copy by row index (kdb set), no previous slot (vob null).  The
 // same rows and addresses as attn_fetch with fewer selects on the way.
-template <typename T, int D, class Entry>
+template <typename T, int D, int NW = kAttnWaves, class Entry>
 __device__ __forceinline__ void attn_fetch_kdev(const AttnRows<T>& R, int c0, int lim, Entry entry,
-                                                AttnFetch<T, D>& f, int tid) {
-  using S = AttnShape<T, D>;
+                                                AttnFetch<T, D, NW>& f, int tid) {
+  using S = AttnShape<T, D, NW>;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int col = lane % S::LPR;
   const int rsub = lane / S::LPR;
-  const int e0 = c0 + wave * kWaveEntries;
-  if (wave >= kAttnWaves) {  // a larger workgroup's other waves: no entries, no loads
+  const int e0 = c0 + wave * S::WE;
+  if (wave >= NW) {  // a larger workgroup's other waves: no entries, no loads
+    // The stores in the order of the loads' path below (rows, hrow, then K
+    // and V), so that the compiler can merge both paths' stores without
+    // selecting between addresses (which would keep f in scratch memory).
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
-      f.rows[u] = f.hrow[u] = -1;
-      f.kr[u] = f.vr[u] = u32x4{0u, 0u, 0u, 0u};
+      f.rows[u] = -1;
+      f.hrow[u] = -1;
+    }
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      f.kr[u] = u32x4{0u, 0u, 0u, 0u};
+      f.vr[u] = u32x4{0u, 0u, 0u, 0u};
     }
     return;
   }
@@ -225,20 +245,20 @@ __device__ __forceinline__ void attn_fetch_kdev(const AttnRows<T>& R, int c0, in
 // first nq <= NQ queries: s[qi * U + u] is query qi's scaled logit of the
 // lane's entry u (entries with rows[u] < 0 are skipped), vr[u] its V row
 // bytes.  Each wave forms its own max, weights and weighted V sum over its
-// 32 entries; the four waves are then merged in LDS in wave order (one
+// 128 / NW entries; the NW waves are then merged in LDS in wave order (one
 // workgroup barrier; every thread of the workgroup must call it: in a
-// workgroup of more than four waves the others have no entries).
+// workgroup of more than NW waves the others have no entries).
 // Afterwards cm[j] and cl[j] (all threads) are query j's max logit and
 // weight sum over the chunk, and threads d < D hold od[j] = its weighted V
 // sum of column d.  The caller must not touch lds until a barrier after
 // this returns.
-template <typename T, int D, int NQ>
+template <typename T, int D, int NQ, int NW = kAttnWaves>
 __device__ __forceinline__ void attn_softmax_merge(float* s, const int* rows, const u32x4* vr,
-                                                   AttnLds<D, NQ>& lds, int nq,
+                                                   AttnLds<D, NQ, NW>& lds, int nq,
                                                    float (&cm)[NQ], float (&cl)[NQ],
                                                    float (&od)[NQ], int tid) {
 #pragma clang fp contract(off)
-  using S = AttnShape<T, D>;
+  using S = AttnShape<T, D, NW>;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int col = lane % S::LPR;
@@ -247,7 +267,7 @@ __device__ __forceinline__ void attn_softmax_merge(float* s, const int* rows, co
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
     if (qi >= nq) break;
-    // Wave-local softmax of query qi over its 32 entries (RPI row groups x U).
+    // Wave-local softmax of query qi over its WE entries (RPI row groups x U).
     float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
@@ -278,7 +298,7 @@ __device__ __forceinline__ void attn_softmax_merge(float* s, const int* rows, co
 #pragma unroll
       for (int e = 0; e < S::EPL; ++e) o[e] += __shfl_xor(o[e], off);
     }
-    if (rsub == 0 && wave < kAttnWaves) {  // (a larger workgroup's other waves hold nothing)
+    if (rsub == 0 && wave < NW) {  // (a larger workgroup's other waves hold nothing)
 #pragma unroll
       for (int e = 0; e < S::EPL; ++e) lds.o[qi][wave][col * S::EPL + e] = o[e];
       if (col == 0) {
@@ -289,7 +309,7 @@ __device__ __forceinline__ void attn_softmax_merge(float* s, const int* rows, co
   }
   __syncthreads();
 
-  // Merge the waves (entry order is fixed: wave 0, 1, 2, 3).
+  // Merge the waves (entry order is fixed: wave 0, 1, ..., NW - 1).
   const int d = tid;
 #pragma unroll
   for (int qi = 0; qi < NQ; ++qi) {
@@ -299,18 +319,18 @@ __device__ __forceinline__ void attn_softmax_merge(float* s, const int* rows, co
     if (qi >= nq) continue;
     float m = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) m = fmaxf(m, lds.m[qi][w]);
-    float fw[kAttnWaves];
+    for (int w = 0; w < NW; ++w) m = fmaxf(m, lds.m[qi][w]);
+    float fw[NW];
     float tl = 0.f;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       fw[w] = (lds.l[qi][w] > 0.f) ? exp2f((lds.m[qi][w] - m) * kLog2e) : 0.f;
       tl = fmaf(lds.l[qi][w], fw[w], tl);
     }
     float acc = 0.f;
     if (d < D) {
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) acc = fmaf(lds.o[qi][w][d], fw[w], acc);
+      for (int w = 0; w < NW; ++w) acc = fmaf(lds.o[qi][w][d], fw[w], acc);
     }
     cm[qi] = m;
     cl[qi] = tl;
@@ -319,20 +339,20 @@ __device__ __forceinline__ void attn_softmax_merge(float* s, const int* rows, co
 }
 
 // Second half of a chunk fetched by attn_fetch (tid: the thread's index in
-// the 256 that handle the chunk; every thread of the workgroup must call
+// the 64 NW that handle the chunk; every thread of the workgroup must call
 // it, since it holds a workgroup barrier), for the first nq <= NQ
 // queries at once: query j is q + j * D (D floats; all NQ are read).  Every
 // K and V row is read once and serves every query; a missed row is first
 // copied into its slot row.  Contraction is off: only the explicit fmaf
 // calls fuse, so a query's result is the same bits whatever nq is.
 // Outputs as attn_softmax_merge.
-template <typename T, int D, int NQ>
+template <typename T, int D, int NQ, int NW = kAttnWaves>
 __device__ __forceinline__ void attn_finish(const float* __restrict__ q, const AttnRows<T>& R,
-                                            float scale, const AttnFetch<T, D>& f,
-                                            AttnLds<D, NQ>& lds, int nq, float (&cm)[NQ],
+                                            float scale, const AttnFetch<T, D, NW>& f,
+                                            AttnLds<D, NQ, NW>& lds, int nq, float (&cm)[NQ],
                                             float (&cl)[NQ], float (&od)[NQ], int tid) {
 #pragma clang fp contract(off)
-  using S = AttnShape<T, D>;
+  using S = AttnShape<T, D, NW>;
   const int lane = tid & 63;
   const int col = lane % S::LPR;
   const bool from_host = R.vhb != nullptr;
@@ -374,15 +394,15 @@ __device__ __forceinline__ void attn_finish(const float* __restrict__ q, const A
 #pragma unroll
     for (int u = 0; u < S::U; ++u) s[qi * S::U + u] *= scale;
   }
-  attn_softmax_merge<T, D, NQ>(s, f.rows, f.vr, lds, nq, cm, cl, od, tid);
+  attn_softmax_merge<T, D, NQ, NW>(s, f.rows, f.vr, lds, nq, cm, cl, od, tid);
 }
 
 // A chunk whose logits are already known (the layer step's own scores of
 // the selected keys): the V rows of its entries and their scores, fetched
 // in one round trip.
-template <typename T, int D, int NQ>
+template <typename T, int D, int NQ, int NW = kAttnWaves>
 struct AttnFetchS {
-  using S = AttnShape<T, D>;
+  using S = AttnShape<T, D, NW>;
   int rows[S::U];
   int hrow[S::U];
   u32x4 vr[S::U];
@@ -396,20 +416,21 @@ struct AttnFetchS {
 // or the previous slot) and the entry's scaled logit of each of the first
 // nq queries, srow[qi * sstride + c].  A skipped entry reads row 0 and
 // score 0 and is masked later.
-template <typename T, int D, int NQ, class Entry>
+template <typename T, int D, int NQ, int NW = kAttnWaves, class Entry>
 __device__ __forceinline__ void attn_fetch_s(const AttnRows<T>& R, const float* __restrict__ srow,
                                              int64_t sstride, int nq, int c0, int lim,
-                                             Entry entry, AttnFetchS<T, D, NQ>& f, int tid) {
-  using S = AttnShape<T, D>;
+                                             Entry entry, AttnFetchS<T, D, NQ, NW>& f, int tid) {
+  using S = AttnShape<T, D, NW>;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int col = lane % S::LPR;
   const int rsub = lane / S::LPR;
-  const int e0 = c0 + wave * kWaveEntries;
-  if (wave >= kAttnWaves) {  // a larger workgroup's other waves: no entries, no loads
+  const int e0 = c0 + wave * S::WE;
+  if (wave >= NW) {  // a larger workgroup's other waves: no entries, no loads
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
-      f.rows[u] = f.hrow[u] = -1;
+      f.rows[u] = -1;
+      f.hrow[u] = -1;
       f.vr[u] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int qi = 0; qi < NQ; ++qi) f.s[qi * S::U + u] = 0.f;
@@ -466,11 +487,11 @@ __device__ __forceinline__ void attn_fetch_s(const AttnRows<T>& R, const float* 
 // Second half of a chunk fetched by attn_fetch_s: a missed row is first
 // copied into its slot row, then attn_softmax_merge over the fetched
 // logits.  Every thread of the workgroup must call it.
-template <typename T, int D, int NQ>
-__device__ __forceinline__ void attn_finish_s(const AttnRows<T>& R, AttnFetchS<T, D, NQ>& f,
-                                              AttnLds<D, NQ>& lds, int nq, float (&cm)[NQ],
+template <typename T, int D, int NQ, int NW = kAttnWaves>
+__device__ __forceinline__ void attn_finish_s(const AttnRows<T>& R, AttnFetchS<T, D, NQ, NW>& f,
+                                              AttnLds<D, NQ, NW>& lds, int nq, float (&cm)[NQ],
                                               float (&cl)[NQ], float (&od)[NQ], int tid) {
-  using S = AttnShape<T, D>;
+  using S = AttnShape<T, D, NW>;
   const int col = (tid & 63) % S::LPR;
   if (R.vhb != nullptr && R.m > 0) {  // the slot keeps a copy of every fetched miss
 #pragma unroll
@@ -481,22 +502,22 @@ __device__ __forceinline__ void attn_finish_s(const AttnRows<T>& R, AttnFetchS<T
       }
     }
   }
-  attn_softmax_merge<T, D, NQ>(f.s, f.rows, f.vr, lds, nq, cm, cl, od, tid);
+  attn_softmax_merge<T, D, NQ, NW>(f.s, f.rows, f.vr, lds, nq, cm, cl, od, tid);
 }
 
 // Entries c0 .. c0 + 127 (those < lim): attn_fetch (attn_fetch_kdev when
 // KDEV: K rows from the device copy, no previous slot), then attn_finish.
-template <typename T, int D, int NQ, bool KDEV = false, class Entry>
+template <typename T, int D, int NQ, bool KDEV = false, int NW = kAttnWaves, class Entry>
 __device__ __forceinline__ void attend_chunk_n(const float* __restrict__ q, const AttnRows<T>& R,
                                                int c0, int lim, float scale, Entry entry,
-                                               AttnLds<D, NQ>& lds, int nq, float (&cm)[NQ],
+                                               AttnLds<D, NQ, NW>& lds, int nq, float (&cm)[NQ],
                                                float (&cl)[NQ], float (&od)[NQ]) {
-  AttnFetch<T, D> f;
+  AttnFetch<T, D, NW> f;
   if constexpr (KDEV)
-    attn_fetch_kdev<T, D>(R, c0, lim, entry, f, threadIdx.x);
+    attn_fetch_kdev<T, D, NW>(R, c0, lim, entry, f, threadIdx.x);
   else
-    attn_fetch<T, D>(R, c0, lim, entry, f, threadIdx.x);
-  attn_finish<T, D, NQ>(q, R, scale, f, lds, nq, cm, cl, od, threadIdx.x);
+    attn_fetch<T, D, NW>(R, c0, lim, entry, f, threadIdx.x);
+  attn_finish<T, D, NQ, NW>(q, R, scale, f, lds, nq, cm, cl, od, threadIdx.x);
 }
 
 // Merge of the chunk partials of one (b, h) by log-sum-exp, for column d:

@@ -95,10 +95,12 @@ struct Lay {
 static_assert(Lay<true>::words * 4 <= 160 * 1024, "cached layout exceeds LDS");
 static_assert(Lay<false>::words * 4 <= 160 * 1024, "long-row layout exceeds LDS");
 static_assert(4 * 256 <= kBins, "selection histograms fit the bound histogram");
-// attention scratch, both queries (dual-token): per-wave partials and up to
-// 32 chunk partials of D+2 each; the tail of region C for a cached row, the
-// candidate lists otherwise (both free once the selection is emitted)
-constexpr int kAttnScratchWords = 2 * (8 + 4 * 128) + 8 + 2 * 32 * (128 + 2);
+// attention scratch, both queries (dual-token): per-wave partials of the
+// kNW waves and up to 32 chunk partials of D+2 each; the tail of region C
+// for a cached row, the candidate lists otherwise (both free once the
+// selection is emitted)
+constexpr int kAttnScratchWords =
+    (int)(sizeof(AttnLds<128, 2, kNW>) + 15) / 16 * 4 + 2 * 32 * (128 + 2);
 static_assert(Lay<true>::end + kAttnScratchWords <= Lay<true>::words, "dual scratch fits (cached)");
 static_assert(kLIdx + kAttnScratchWords <= Lay<false>::c, "dual scratch fits (long rows)");
 // Rows kept across steps: each entry's row in the previous step's slot (or
@@ -1295,8 +1297,8 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
                                                   float* scratch, const float* srow) {
   constexpr int NQ = 2;
   const int nq = fa.out_spec != nullptr ? 2 : 1;
-  AttnLds<D, NQ>& lds = *reinterpret_cast<AttnLds<D, NQ>*>(scratch);
-  float* part = scratch + (sizeof(AttnLds<D, NQ>) + 15) / 16 * 4;
+  AttnLds<D, NQ, kNW>& lds = *reinterpret_cast<AttnLds<D, NQ, kNW>*>(scratch);
+  float* part = scratch + (sizeof(AttnLds<D, NQ, kNW>) + 15) / 16 * 4;
   const int cs = fa.chunk_shift;
   const int k = ks << cs;  // rows attended (at most)
   const int64_t n_rows = fa.n_rows;
@@ -1329,31 +1331,36 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
   };
   const int chunks = (k + kAttnChunk - 1) / kAttnChunk;
   const float* qrow = fa.q + (int64_t)bh * 2 * D;  // plane 0, then plane 1
-  float* const outs[2] = {fa.out, fa.out_spec};
-  float* const lses[2] = {fa.lse, fa.lse_spec};
+  // Output pointers of query qi by value selects (an array indexed by qi
+  // would live in scratch memory).
+  auto out_of = [&](int qi) { return qi == 0 ? fa.out : fa.out_spec; };
+  auto lse_of = [&](int qi) { return qi == 0 ? fa.lse : fa.lse_spec; };
   const int d = threadIdx.x;
-  // Four waves attend a chunk of kAttnChunk entries; the workgroup's other
-  // waves find no entry below the chunk's limit and only join its barriers.
+  // All kNW waves attend each chunk of kAttnChunk entries, 128 / kNW each.
   for (int ch = 0; ch < chunks; ++ch) {
     float cm[NQ], cl[NQ], od[NQ];
     if (srow != nullptr) {
-      AttnFetchS<T, D, NQ> f;
-      attn_fetch_s<T, D, NQ>(R, srow, n_rows, nq, ch * kAttnChunk,
-                             min(k, (ch + 1) * kAttnChunk), entry, f, threadIdx.x);
-      attn_finish_s<T, D, NQ>(R, f, lds, nq, cm, cl, od, threadIdx.x);
+      AttnFetchS<T, D, NQ, kNW> f;
+      attn_fetch_s<T, D, NQ, kNW>(R, srow, n_rows, nq, ch * kAttnChunk,
+                                  min(k, (ch + 1) * kAttnChunk), entry, f, threadIdx.x);
+      attn_finish_s<T, D, NQ, kNW>(R, f, lds, nq, cm, cl, od, threadIdx.x);
     } else if (kdev && lold == nullptr) {
-      attend_chunk_n<T, D, NQ, true>(qrow, R, ch * kAttnChunk, min(k, (ch + 1) * kAttnChunk),
-                                     fa.scale, entry, lds, nq, cm, cl, od);
+      attend_chunk_n<T, D, NQ, true, kNW>(qrow, R, ch * kAttnChunk,
+                                          min(k, (ch + 1) * kAttnChunk), fa.scale, entry, lds,
+                                          nq, cm, cl, od);
     } else {
-      attend_chunk_n<T, D, NQ>(qrow, R, ch * kAttnChunk, min(k, (ch + 1) * kAttnChunk),
-                               fa.scale, entry, lds, nq, cm, cl, od);
+      attend_chunk_n<T, D, NQ, false, kNW>(qrow, R, ch * kAttnChunk,
+                                           min(k, (ch + 1) * kAttnChunk), fa.scale, entry, lds,
+                                           nq, cm, cl, od);
     }
     if (d < D) {
-      for (int qi = 0; qi < nq; ++qi) {
+#pragma unroll
+      for (int qi = 0; qi < NQ; ++qi) {
+        if (qi >= nq) break;
         if (chunks == 1) {
-          outs[qi][(int64_t)bh * D + d] = (cl[qi] > 0.f) ? od[qi] / cl[qi] : 0.f;
-          if (d == 0 && lses[qi] != nullptr)
-            lses[qi][bh] = (cl[qi] > 0.f) ? cm[qi] + logf(cl[qi]) : -INFINITY;
+          out_of(qi)[(int64_t)bh * D + d] = (cl[qi] > 0.f) ? od[qi] / cl[qi] : 0.f;
+          if (d == 0 && lse_of(qi) != nullptr)
+            lse_of(qi)[bh] = (cl[qi] > 0.f) ? cm[qi] + logf(cl[qi]) : -INFINITY;
         } else {
           float* pc = part + (qi * chunks + ch) * (D + 2);
           pc[d] = od[qi];
@@ -1367,11 +1374,13 @@ __device__ __forceinline__ void fused_attention_t(const FusedAttn& fa, int bh, i
     __syncthreads();  // lds is reused by the next chunk; partials complete
   }
   if (chunks > 1 && d < D) {
-    for (int qi = 0; qi < nq; ++qi) {
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) {
+      if (qi >= nq) break;
       float o, l;
       combine_chunks<D>(part + qi * chunks * (D + 2), chunks, d, o, l);
-      outs[qi][(int64_t)bh * D + d] = o;
-      if (d == 0 && lses[qi] != nullptr) lses[qi][bh] = l;
+      out_of(qi)[(int64_t)bh * D + d] = o;
+      if (d == 0 && lse_of(qi) != nullptr) lse_of(qi)[bh] = l;
     }
   }
 }
