@@ -30,12 +30,15 @@ namespace dd {
 
 namespace {
 
-// A workgroup scores 4 waves x 2 iterations x (64 / Q) keys: 256 keys of
-// 256 B for the two-query bf16 case (64 KB per workgroup).  Smaller tiles
+// A workgroup scores 4 waves x ITERS iterations x (64 / Q) keys: 256 keys
+// of 256 B for the two-query bf16 case (64 KB per workgroup).  Smaller tiles
 // than that lost to launch overhead and larger ones to the last partial
-// round of workgroups (measured on MI355X for 32 x 32768 keys).
+// round of workgroups (measured on MI355X for 32 x 32768 keys).  Rows of
+// 4-byte elements take one iteration, so that a workgroup still reads 64 KB
+// at D = 128 (two iterations, 128 KB, scanned the 64 MiB of fp32 chunk
+// landmarks 6% slower from HBM: 14.8 against 13.9 us).
 constexpr int kScoreWaves = 4;
-constexpr int kScoreIters = 2;
+constexpr int kScoreIters = 2;  // iterations for 2-byte elements
 
 template <typename T, int D, int Q>
 struct ScoreShape {
@@ -44,7 +47,8 @@ struct ScoreShape {
   static constexpr int RPI = 64 / LPR;             // rows per wave load instruction
   static constexpr int U = LPR / Q;                // loads per lane per iteration
   static constexpr int KPI = U * RPI;              // keys per wave iteration (= 64 / Q)
-  static constexpr int TILE = kScoreWaves * kScoreIters * KPI;
+  static constexpr int ITERS = sizeof(T) == 4 ? 1 : kScoreIters;
+  static constexpr int TILE = kScoreWaves * ITERS * KPI;
   static_assert(U >= 1 && U * Q == LPR, "shape");
   // Group maxima: a group of kMaxGroup keys is VPG consecutive vu values of
   // every rsub; GPI groups per wave iteration.
@@ -111,9 +115,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void k_score(
   // never mixes rows, so those lanes' scores are simply not stored.  The
   // keys are read once: non-temporal loads keep them from evicting the
   // scores (and prefetched rows) that the next kernels read from L2.
-  u32x4 raw_it[kScoreIters][S::U];
+  u32x4 raw_it[S::ITERS][S::U];
 #pragma unroll
-  for (int it = 0; it < kScoreIters; ++it) {
+  for (int it = 0; it < S::ITERS; ++it) {
     const int64_t key0 = tile0 + ((int64_t)it * kScoreWaves + wave) * S::KPI;
     if (key0 < n) {
 #pragma unroll
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void k_score(
   }
 
 #pragma unroll
-  for (int it = 0; it < kScoreIters; ++it) {
+  for (int it = 0; it < S::ITERS; ++it) {
     const int64_t key0 = tile0 + ((int64_t)it * kScoreWaves + wave) * S::KPI;
     if (key0 >= n_max) break;
     const int64_t my_row = key0 + vu * S::RPI + rsub;
