@@ -30,12 +30,17 @@ __global__ __launch_bounds__(256) void k_stream_copy(const u32x4* __restrict__ s
   for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
-// Streaming read in the scoring kernel's shape: a one-shot grid whose
-// workgroups read 64 KB each, every lane with 16 non-temporal 16-byte loads
-// in flight (each load instruction of the workgroup covers 4 KB), folded
-// into a xor; one word per wave goes to the 64-word sink so that the loads
-// cannot be dropped (waves share sink words: the values are meaningless).
-constexpr int kReadUnroll = 16;
+// Streaming read, the ceiling the scans are measured against: a one-shot
+// grid whose workgroups read 16 KB each, every lane with 4 non-temporal
+// 16-byte loads in flight (each load instruction of the workgroup covers
+// 4 KB), folded into a xor; one word per wave goes to the 64-word sink so
+// that the loads cannot be dropped (waves share sink words: the values are
+// meaningless).  The fastest of the shapes swept on MI355X for 256 MiB read
+// from HBM: 39.5 us, against 39.8-41.0 us for 8 or 16 loads per lane in
+// 256- to 1024-thread workgroups or a persistent grid, 41.5 us for the
+// scoring kernel's own shape (16 loads per lane, 64 KB per workgroup), and
+// 43.6-46.1 us with plain loads.
+constexpr int kReadUnroll = 4;
 __global__ __launch_bounds__(256) void k_stream_read(const u32x4* __restrict__ src, int64_t n16,
                                                      uint32_t* __restrict__ sink) {
   const int64_t base = (int64_t)blockIdx.x * (256 * kReadUnroll) + threadIdx.x;
