@@ -8,7 +8,10 @@
 // one fp32 row of D elements is written per chunk.  A chunk is handled by
 // LPR lanes (16 B of each row per lane), so a wave covers 64 / LPR chunks
 // and each of its load instructions reads one row of each of them.  The
-// rows of a chunk are loaded 8 at a time, all in flight together.
+// rows of a chunk are loaded 8 at a time, all in flight together, with
+// non-temporal loads (every key row is read once): 60.6 -> 52.4 us for the
+// 7B layer's 256 MiB of keys at c = 8 on MI355X.  The landmarks are stored
+// plainly (non-temporal stores took 65.4 us).
 #include "dd_device.h"
 #include "dd_internal.h"
 
@@ -51,7 +54,7 @@ __global__ __launch_bounds__(kLmThreads) void k_landmarks(const T* __restrict__ 
 #pragma unroll
     for (int u = 0; u < kLmBatch; ++u) {
       const int64_t i = i0 + u < cnt ? i0 + u : cnt - 1;  // stays inside the chunk's valid rows
-      raw[u] = *reinterpret_cast<const u32x4*>(base + i * D);
+      raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + i * D));
     }
 #pragma unroll
     for (int u = 0; u < kLmBatch; ++u) {
