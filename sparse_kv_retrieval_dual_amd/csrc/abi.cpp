@@ -41,8 +41,11 @@ namespace {
 constexpr int kResidentWgsScale = 4;
 
 // Host-link bytes a layer's selection kernel hides before its attention
-// needs the prediction's rows: about 8 us at about 50 GB/s.
-constexpr int64_t kSelectWindowLinkBytes = int64_t(384) << 10;
+// needs the prediction's rows: about 5 us at about 50 GB/s.  256 KiB (8
+// slabs of 32 KiB) was the fastest of 6 to 20 slabs for the 7B layer at
+// c = 8 (38.1-38.4 us a step, against 39.5-40.4 us with 12) and at c = 16
+// (36.4-36.6 against 37.8-37.9 us) on MI355X.
+constexpr int64_t kSelectWindowLinkBytes = int64_t(256) << 10;
 // Bytes the key scan streams from HBM while the host link moves one byte
 // of prefetch beside it.
 constexpr int64_t kScanBytesPerLinkByte = 100;
