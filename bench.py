@@ -902,7 +902,11 @@ def main():
     # attention reads the gathered K rows), timed the same way as the
     # headline when a graph is available, else eagerly.
     host_kv = None
-    if args.k_rows == "device" and chunk == 1:
+    # Only at the 7B layer's shape: run as the main workload, hiconc_64 ended
+    # in a host segmentation fault somewhere after its reference rates,
+    # before its JSON line (cause not found), so this stage stays off for the
+    # other shapes.
+    if args.k_rows == "device" and chunk == 1 and w.name == "llama7b_32k_layer":
         hctx = dd.Context(ring_slots=args.ring, gather_cus=args.gather_cus,
                           prefetch_wgs=args.prefetch_wgs, prefetch=args.prefetch, k_rows="host")
         step(0, pred, c=hctx)
