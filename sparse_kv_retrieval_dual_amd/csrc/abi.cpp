@@ -607,7 +607,11 @@ DD_API int dd_layer_step(dd_ctx* c, const dd_layer_step_args* a) {
       if (e != hipSuccess) return hip_fail(e, "resident state reset");
     }
   }
-  DD_CHECK_HIP(hipEventRecord(c->ev_start, caller), "record start");
+  // The start event orders the context's own streams after the caller's
+  // work; with neither in use (one stream, the prefetch inside the scoring
+  // kernel) it is not recorded at all.
+  if (ms != caller || use_side)
+    DD_CHECK_HIP(hipEventRecord(c->ev_start, caller), "record start");
   if (ms != caller) DD_CHECK_HIP(hipStreamWaitEvent(ms, c->ev_start, 0), "main waits start");
   if (use_side) DD_CHECK_HIP(hipStreamWaitEvent(side, c->ev_start, 0), "side waits start");
 
