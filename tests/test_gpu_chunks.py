@@ -109,6 +109,8 @@ def _run(ctx, w, data, c, pred=None, ring=None):
     ("hiconc_64", dict(B=3, H=2, n_max=20000, len_lo=300, len_hi=20000, k=512), 16, 3),
     ("llama13b_128k", dict(L=1, B=1, H=2, n_max=16384, k=2048), 32, 2),
     ("llama7b_32k_step", dict(L=2, B=2, H=2, n_max=8192, k=1024), 64, 1),
+    ("llama7b_32k_layer", dict(H=3, n_max=4096), 2, 2),
+    ("hiconc_64", dict(B=3, H=2, n_max=3000, len_lo=100, len_hi=3000, k=128), 4, 2),
 ])
 def test_chunk_layer_step_matches_oracle(name, kw, c, R):
     dd = require_gpu()
@@ -271,11 +273,13 @@ def test_chunk_layer_step_full_size_7b():
     # ragged: some requests shorter than k rows (every chunk selected)
     ("hiconc_64", dict(B=4, H=2, n_max=4096, len_lo=1, len_hi=4096, k=128), 8, 0),
     ("hiconc_64", dict(B=4, H=2, n_max=4096, len_lo=1, len_hi=4096, k=128), 8, 5),
+    ("llama7b_32k_layer", dict(H=8, n_max=4096), 2, 0),
+    ("llama7b_32k_layer", dict(H=8, n_max=4096), 4, 3),
 ])
 def test_selection_side_prefetch_matches_side_stream(name, kw, c, sel):
     """One layer with 256-byte V rows and k <= 128 rows: the prediction's rows
     are fetched by the selection kernel for the last slabs (by the layer's
-    sizes: all slabs at the small shapes, 12 of 32 at the full 7B shape; or
+    sizes: all slabs at the small shapes, 8 of 32 at the full 7B shape; or
     the last `sel`; none for -1) and by the scoring kernel for the rest.  Outputs,
     statistics and every slab's prefetched slot rows must equal those of a
     side-stream prefetch bit for bit, and the slot rows must hold the host
