@@ -66,6 +66,10 @@ def _check_layer(w, d, res, l, pred_np=None):
     ("llama7b_32k_step", dict(L=1, B=2, H=2, n_max=8192, k=1024), 1),
     ("llama13b_128k", dict(L=1, B=1, H=2, n_max=16384, k=2048), 2),
     ("hiconc_64", dict(B=3, H=2, n_max=20000, len_lo=300, len_hi=20000, k=512), 3),
+    # the attention's other two lane shapes: bf16 rows of 64 (two entries per
+    # lane) and fp32 rows of 128 (eight), with k over one 128-entry chunk
+    ("llama7b_32k_layer", dict(B=2, H=3, D=64, n_max=3000, len_lo=2000, len_hi=3000), 2),
+    ("tiny", dict(H=3, D=128, n_max=3000, len_lo=2500, len_hi=3000, k=192), 2),
 ])
 def test_layer_step_matches_oracle(name, kw, R):
     dd = require_gpu()
