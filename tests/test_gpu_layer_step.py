@@ -89,6 +89,41 @@ def test_layer_step_matches_oracle(name, kw, R):
     print(f"worst relative attention error {worst:.2e}")
 
 
+@pytest.mark.parametrize("mode,R", [("side", 2), ("fused", 1), ("fused", 2)])
+def test_layer_step_short_and_empty_requests(mode, R):
+    """Requests of 0, 1, k - 1, k, k + 1 and n_max keys in one batch: a
+    request of length n <= k selects all of its keys (then -1), an empty one
+    selects nothing and attends to nothing (zero output, lse -inf), and a
+    second step on the speculated sets (-1 entries included) agrees again."""
+    dd = require_gpu()
+    w = gen.workload("llama7b_32k_layer").scaled(L=2, B=6, H=2, n_max=3000, k=128)
+    lens = torch.tensor([0, 1, w.k - 1, w.k, w.k + 1, w.n_max], dtype=torch.int32)
+    announce(f"layer_step short and empty requests lens={lens.tolist()} mode={mode} R={R}")
+    data = _stage(dd, w, w.L)
+    for d in data:
+        d["lens"] = lens
+    ctx = dd.Context(ring_slots=R, prefetch=mode)
+    cold = _run(dd, ctx, w, data)
+    refs = []
+    for l in range(w.L):
+        _, ref = _check_layer(w, data[l], cold, l)
+        refs.append(ref)
+    for l in range(w.L):
+        cur = cold["cur"][l].cpu().numpy()
+        assert (cur[0] == -1).all()
+        assert np.array_equal(cur[1, :, 0], [0] * w.H) and (cur[1, :, 1:] == -1).all()
+        assert (cur[2, :, :w.k - 1] == np.arange(w.k - 1)).all() and (cur[2, :, w.k - 1] == -1).all()
+        assert (cur[3] == np.arange(w.k)).all()
+        assert (cold["out"][l][0] == 0).all()
+        assert torch.isneginf(cold["lse"][l][0]).all()
+    pred = [torch.from_numpy(r["spec"]).cuda() for r in refs]
+    hot = _run(dd, ctx, w, data, pred=pred)
+    for l in range(w.L):
+        _check_layer(w, data[l], hot, l, pred_np=refs[l]["spec"])
+        assert torch.equal(hot["out"][l], cold["out"][l])
+    ctx.close()
+
+
 def test_outputs_do_not_depend_on_prediction_or_ring():
     """Misses are fetched on the critical path, so any prediction (none,
     perfect, speculated, random, another request's) and any ring size give
