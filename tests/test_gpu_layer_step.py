@@ -70,6 +70,10 @@ def _check_layer(w, d, res, l, pred_np=None):
     # lane) and fp32 rows of 128 (eight), with k over one 128-entry chunk
     ("llama7b_32k_layer", dict(B=2, H=3, D=64, n_max=3000, len_lo=2000, len_hi=3000), 2),
     ("tiny", dict(H=3, D=128, n_max=3000, len_lo=2500, len_hi=3000, k=192), 2),
+    # selection sizes at the edges: one key, an odd count, one past a chunk
+    ("llama7b_32k_layer", dict(B=2, H=3, n_max=5000, len_lo=1, len_hi=5000, k=1), 2),
+    ("llama7b_32k_layer", dict(B=3, H=2, n_max=4099, len_lo=20, len_hi=4099, k=33), 1),
+    ("hiconc_64", dict(B=2, H=2, n_max=6000, len_lo=100, len_hi=6000, k=129), 2),
 ])
 def test_layer_step_matches_oracle(name, kw, R):
     dd = require_gpu()

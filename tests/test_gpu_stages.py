@@ -106,6 +106,8 @@ TOPK_CASES = [
     ("planted", (1, 2, 2), 65536, [65536], 200),
     ("normal", (1, 1, 2), 65536, [50000], 256),
     ("normal", (1, 2, 1), 9999, [9999], 50),
+    ("normal", (2, 2, 2), 20000, [20000, 777], 1),
+    ("ties", (1, 2, 2), 5000, [5000], 1),
 ]
 
 
