@@ -80,6 +80,9 @@ def _check_step(w, res, ref, lens, chunk, q_cur, kst, vst):
     # prepared steps (and its two output sets) from the third step on
     ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000), 0, True),
     ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000), 8, True),
+    # requests growing from below k (every key, or every chunk, selected) past it
+    ("llama7b_32k_layer", dict(B=3, H=2, n_max=512, len_lo=125, len_hi=128), 0, False),
+    ("llama7b_32k_layer", dict(B=3, H=2, n_max=512, len_lo=123, len_hi=128), 8, False),
 ])
 def test_decode_loop_matches_oracle(name, kw, chunk, qbuf):
     """Four real steps: at each, the GPU's sets, attention and (where the sets
