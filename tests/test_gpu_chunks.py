@@ -80,10 +80,12 @@ def test_gather_chunks_bytes(c, planes):
         assert np.array_equal(stored(out), want), plane
 
 
-def _stage(dd, w, c):
+def _stage(dd, w, c, fixed_lens=None):
     data = []
     for l in range(w.L):
         lay = gen.make_layer(w, l, "cpu")
+        if fixed_lens is not None:
+            lay["lens"] = torch.tensor(fixed_lens, dtype=torch.int32)
         k_dev = lay["k"].cuda()
         lens = lay["lens"].cuda()
         data.append({"q": lay["q"], "k": lay["k"], "v": lay["v"], "lens": lay["lens"],
@@ -111,12 +113,18 @@ def _run(ctx, w, data, c, pred=None, ring=None):
     ("llama7b_32k_step", dict(L=2, B=2, H=2, n_max=8192, k=1024), 64, 1),
     ("llama7b_32k_layer", dict(H=3, n_max=4096), 2, 2),
     ("hiconc_64", dict(B=3, H=2, n_max=3000, len_lo=100, len_hi=3000, k=128), 4, 2),
+    # an empty request and requests of 1, 16 (= k/c chunks) less one key, 16
+    # chunks, 16 chunks and one key, and n_max keys
+    ("llama7b_32k_layer", dict(B=6, H=2, n_max=3000, k=128, lens=[0, 1, 127, 128, 129, 3000]),
+     8, 2),
 ])
 def test_chunk_layer_step_matches_oracle(name, kw, c, R):
     dd = require_gpu()
+    kw = dict(kw)
+    fixed = kw.pop("lens", None)
     w = gen.workload(name).scaled(**kw)
-    announce(f"chunk layer_step {name} {kw} chunk={c} R={R}")
-    data = _stage(dd, w, c)
+    announce(f"chunk layer_step {name} {kw} lens={fixed} chunk={c} R={R}")
+    data = _stage(dd, w, c, fixed)
     B, H, ks = w.B, w.H, w.k // c
     ctx = dd.Context(ring_slots=R)
     ring = torch.zeros(dd.ring_bytes(R, B, H, w.D, w.k, dd.kv_dtype(data[0]["k_dev"])),
