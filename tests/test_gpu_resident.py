@@ -21,6 +21,8 @@ pytestmark = pytest.mark.gpu
     ("tiny", dict(n_max=2048, len_lo=1500, len_hi=1500), None),
     # request 0 shorter than k: its sets and predictions carry -1 padding
     ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000), 60),
+    # request 0 empty before the first append: it grows from 1 key
+    ("llama7b_32k_layer", dict(B=2, H=2, n_max=4096, len_lo=3000, len_hi=4000), 0),
     # the other row sizes of the copy queues: 128 B (bf16, D = 64), 512 B (fp32, D = 128)
     ("llama7b_32k_layer", dict(B=2, H=2, D=64, n_max=4096, len_lo=3000, len_hi=4000), None),
     ("tiny", dict(H=4, D=128, n_max=2048, len_lo=1500, len_hi=1500), None),
