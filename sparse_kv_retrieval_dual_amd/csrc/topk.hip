@@ -167,8 +167,9 @@ __device__ __forceinline__ float key_floor(uint32_t b) {
 // counters (digit order = key order) and the count in larger digits.
 // Thread t scans the 8 digits below kBins - 8t, one block scan orders the
 // threads, and the thread whose digits reach kr broadcasts through out2.
+// With top, also the highest digit that counts anything.
 __device__ __forceinline__ void pick_bin(const uint32_t* hist, int kr, ScanBufs& sb, int* out2,
-                                         int& digit, int& above) {
+                                         int& digit, int& above, int* top_digit = nullptr) {
   constexpr int BPT = kBins / kNT;
   const int top = kBins - BPT * (int)threadIdx.x;  // this thread's digits: [top - BPT, top)
   int c[BPT];
@@ -197,9 +198,22 @@ __device__ __forceinline__ void pick_bin(const uint32_t* hist, int kr, ScanBufs&
     out2[0] = d;
     out2[1] = a;
   }
+  if (top_digit != nullptr && before == 0 && sum > 0) {
+    int d = top - BPT;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      if (!found && c[i] > 0) {
+        found = true;
+        d = top - 1 - i;
+      }
+    }
+    out2[2] = d;
+  }
   __syncthreads();
   digit = out2[0];
   above = out2[1];
+  if (top_digit != nullptr) *top_digit = out2[2];
 }
 
 // The exact k-th largest key T among the cnt candidate keys (k <= cnt <=
@@ -210,10 +224,15 @@ __device__ __forceinline__ void pick_bin(const uint32_t* hist, int kr, ScanBufs&
 // each pass's barrier every wave scans the histogram itself, so T needs no
 // broadcast.  When the chosen digit's keys are exactly the ones still
 // needed, all of them are taken and the passes stop: T is then just below
-// the digit's lowest key and no key equal to T is taken.
+// the digit's lowest key and no key equal to T is taken.  With P > 0 the
+// top P bits of T are known to be those of prefix0 (every key that can be
+// among the k largest has them); keys without them are not counted, and
+// the digits start below them (the last one narrower when 32 - P is not a
+// multiple of 8).
 template <int CAP>
 __device__ __forceinline__ void select_kth(const uint32_t* fkey, int cnt, int k, uint32_t* h4,
-                                           uint32_t& thr, int& take_eq) {
+                                           uint32_t& thr, int& take_eq, uint32_t prefix0 = 0u,
+                                           int P = 0) {
   constexpr int R = CAP / kNT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -227,16 +246,18 @@ __device__ __forceinline__ void select_kth(const uint32_t* fkey, int cnt, int k,
     if (kNT * r >= cnt) break;
     if (tid + kNT * r < cnt) x[r] = fkey[tid + kNT * r];
   }
-  uint32_t prefix = 0u, pmask = 0u;
+  uint32_t pmask = P > 0 ? ~0u << (32 - P) : 0u;
+  uint32_t prefix = prefix0 & pmask;
   int kr = k;
 #pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  for (int pass = 0, hi = 32 - P; hi > 0; ++pass, hi -= 8) {
+    const int shift = hi > 8 ? hi - 8 : 0;
+    const uint32_t dmask = (1u << (hi - shift)) - 1u;
     uint32_t* h = h4 + 256 * pass;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (kNT * r >= cnt) break;
-      if (tid + kNT * r < cnt && (x[r] & pmask) == prefix) atomicAdd(&h[(x[r] >> shift) & 255u], 1u);
+      if (tid + kNT * r < cnt && (x[r] & pmask) == prefix) atomicAdd(&h[(x[r] >> shift) & dmask], 1u);
     }
     __syncthreads();
     // lane l holds digits 255 - 4l .. 252 - 4l, highest first
@@ -266,7 +287,7 @@ __device__ __forceinline__ void select_kth(const uint32_t* fkey, int cnt, int k,
     cd = __builtin_amdgcn_readlane(cd, src);
     kr -= a;
     prefix |= (uint32_t)d << shift;
-    pmask |= 255u << shift;
+    pmask |= dmask << shift;
     if (kr == cd && prefix != 0u) {  // every key of this digit is taken
       thr = prefix - 1u;
       take_eq = 0;
@@ -757,10 +778,14 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
 #pragma unroll
   for (int g = 0; g < G; ++g) atomicAdd(&hist[order_key(gmax[g]) >> 21], 1u);
   __syncthreads();
-  int d0, above;
-  pick_bin(hist, k, sb, bcast, d0, above);
+  int d0, above, dtop;
+  pick_bin(hist, k, sb, bcast, d0, above, &dtop);
   const float fb = key_floor((uint32_t)d0 << 21);
   clear(hist, 4 * 256);  // the selection's histograms (ordered by the next barrier)
+  // The k largest keys have top digits in [d0, dtop] (dtop: the row
+  // maximum's), so they share the leading bits on which d0 and dtop agree.
+  const uint32_t ddiff = (uint32_t)(d0 ^ dtop);
+  const int kp = ddiff == 0u ? 11 : __clz(ddiff) - 21;
 
   // Candidates: every entry >= fb, by index.  Count, scan, then write.
   int cnt;
@@ -867,7 +892,7 @@ __device__ __forceinline__ bool filter_select(const float* __restrict__ row, int
   int pf = 0, pn = 0;
   uint32_t thr;
   int take_eq;
-  select_kth<CAP>(fkey, cnt, k, hist, thr, take_eq);
+  select_kth<CAP>(fkey, cnt, k, hist, thr, take_eq, (uint32_t)d0 << 21, kp);
   if (book) {
     mark_prediction(pv, k, n, n_max, pbits, pf, pn);
     sk.pbits = pbits;
