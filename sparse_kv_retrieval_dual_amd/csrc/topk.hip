@@ -1028,11 +1028,15 @@ __device__ __forceinline__ bool maxima_select(const float* __restrict__ row,
     }
   }
   __syncthreads();  // histogram complete; the prediction list stored
-  int d0, above;
-  pick_bin(hist, k, sb, bcast, d0, above);
+  int d0, above, dtop;
+  pick_bin(hist, k, sb, bcast, d0, above, &dtop);
   const uint32_t bkey = (uint32_t)d0 << 21;
   const float fb = key_floor(bkey);
   clear(hist, 4 * 256);  // the selection's histograms (ordered by the barriers below)
+  // As in the filter path: the k largest keys share the leading bits on
+  // which d0 and the row maximum's digit agree.
+  const uint32_t ddiff = (uint32_t)(d0 ^ dtop);
+  const int kp = ddiff == 0u ? 11 : __clz(ddiff) - 21;
 
   // Candidate groups, and whether the prediction ascends.
   int unsorted = 0;
@@ -1111,7 +1115,7 @@ __device__ __forceinline__ bool maxima_select(const float* __restrict__ row,
 
   uint32_t thr;
   int take_eq;
-  select_kth<kCapM>(fkey, cnt, k, hist, thr, take_eq);
+  select_kth<kCapM>(fkey, cnt, k, hist, thr, take_eq, bkey, kp);
 
   // Emit: thread t owns candidates [t E, t E + E) of the ascending list.
   constexpr int EM = kCapM / kNT;
