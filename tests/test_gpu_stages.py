@@ -74,6 +74,15 @@ def _topk_case(kind, rows_shape, n_max, seed):
         s = gen.random_tensor((B, H, Q, n_max), seed=seed, scale=3.0)
     elif kind == "ties":
         s = gen.tie_scores(B * H * Q, n_max, seed=seed, nvalues=5).reshape(B, H, Q, n_max)
+    elif kind == "signedzero":
+        # 20 positive keys, then 30 entries of +0 and 30 of -0 at random
+        # places over a negative background: the k-th largest is a zero
+        s = -1.0 - gen.random_tensor((B, H, Q, n_max), seed=seed, scale=1.0).abs()
+        flat = s.view(B * H * Q, n_max)
+        idx = gen.random_positions(B * H * Q, min(80, n_max), n_max, seed + 1).long()
+        flat.scatter_(1, idx[:, :20], 1.0 + gen.random_tensor((B * H * Q, 20), seed=seed + 2).abs())
+        flat.scatter_(1, idx[:, 20:50], 0.0)
+        flat.scatter_(1, idx[:, 50:80], -0.0)
     elif kind == "allzero":
         s = torch.zeros(B, H, Q, n_max)
         s[..., ::2] = -0.0
@@ -98,6 +107,11 @@ TOPK_CASES = [
     ("ties", (1, 2, 2), 40961, [40961], 3000),
     ("ties", (2, 1, 1), 37, [37, 36], 5),
     ("allzero", (1, 1, 2), 5000, [5000], 33),
+    # +0 and -0 (equal scores, one key) tied at the k-th largest: the
+    # lower index wins whatever the sign
+    ("signedzero", (2, 2, 2), 8192, [8192, 5000], 40),
+    ("signedzero", (2, 2, 2), 8192, [8192, 5000], 30),
+    ("signedzero", (1, 2, 2), 40961, [40961], 40),
     ("planted", (2, 2, 1), 20000, [20000, 16384], 40),
     ("planted", (1, 1, 2), 70000, [70000], 39),
     ("normal", (3, 1, 1), 50, [0, 1, 2], 1),
